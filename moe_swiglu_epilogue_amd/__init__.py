@@ -1,0 +1,19 @@
+"""MI355X (gfx950) fused SwiGLU + NVFP4 block quantization.
+
+The compute lives in ``libmoe_nvfp4.so`` (hand-written HIP kernels behind a
+C ABI, declared in ``include/moe_nvfp4.h``); this package is a thin binding:
+``nvfp4_quantize``, ``swiglu_nvfp4_quantize`` and ``nvfp4_dequantize`` take
+torch tensors on the GPU, marshal pointers, sizes and the current stream, and
+call the library. Importing the package does not load the library; the first
+call does, and raises if it is missing.
+"""
+
+__all__ = ["nvfp4_quantize", "swiglu_nvfp4_quantize", "nvfp4_dequantize",
+           "Nvfp4Error", "library_path"]
+
+
+def __getattr__(name):
+    if name in __all__:
+        from . import binding
+        return getattr(binding, name)
+    raise AttributeError(name)

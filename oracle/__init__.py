@@ -1,0 +1,249 @@
+"""NumPy front end of the CPU oracle (``liboracle_nvfp4.so``).
+
+TEST INFRASTRUCTURE ONLY. The oracle is the plain definition of NVFP4 block
+quantization and of the fused SwiGLU + NVFP4 quantize step; the GPU library
+is checked against it. Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this package. It shares no
+code with the HIP path and never imports it.
+
+Every function takes and returns host NumPy arrays. BF16 tensors travel as
+``uint16`` bit patterns. ``gs_rows`` is one FP32 global scale per row (None
+means 1.0); :func:`rows_global_scale` expands per-expert scales to rows.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import numpy as np
+
+from . import build as _build
+
+_LIB = None
+
+_u8p = C.POINTER(C.c_uint8)
+_u16p = C.POINTER(C.c_uint16)
+_i32p = C.POINTER(C.c_int32)
+_f32p = C.POINTER(C.c_float)
+_i64 = C.c_int64
+
+
+def lib():
+    """Load the oracle library, building it with gcc if it is missing."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(_build.LIB):
+            _build.build()
+        L = C.CDLL(_build.LIB)
+        L.oracle_bf16_to_f32.argtypes = [C.c_uint16]
+        L.oracle_bf16_to_f32.restype = C.c_float
+        L.oracle_swiglu.argtypes = [C.c_float, C.c_float]
+        L.oracle_swiglu.restype = C.c_float
+        L.oracle_fp8_e4m3_encode.argtypes = [C.c_float]
+        L.oracle_fp8_e4m3_encode.restype = C.c_uint8
+        L.oracle_fp8_e4m3_decode.argtypes = [C.c_uint8]
+        L.oracle_fp8_e4m3_decode.restype = C.c_float
+        L.oracle_e2m1_index.argtypes = [C.c_int]
+        L.oracle_e2m1_index.restype = C.c_int
+        L.oracle_e2m1_decode.argtypes = [C.c_uint8]
+        L.oracle_e2m1_decode.restype = C.c_float
+        L.oracle_quantize_block.argtypes = [_f32p, C.c_float, _u8p, _u8p, _f32p, _f32p]
+        L.oracle_quantize_block.restype = None
+        L.oracle_fp8_encode_array.argtypes = [_f32p, _i64, _u8p]
+        L.oracle_swiglu_rows.argtypes = [_u16p, _i64, _i64, _i64, _f32p]
+        L.oracle_quantize_f32_rows.argtypes = [_f32p, _i64, _i64, _i64, _f32p,
+                                               _u8p, _u8p, _f32p, _f32p]
+        L.oracle_quantize_bf16_rows.argtypes = [_u16p, _i64, _i64, _i64, _f32p,
+                                                _u8p, _u8p]
+        L.oracle_swiglu_quantize_rows.argtypes = [_u16p, _i64, _i64, _i64, _f32p,
+                                                  _u8p, _u8p, _f32p, _f32p, _f32p]
+        L.oracle_dequantize_rows.argtypes = [_u8p, _u8p, _i64, _i64, _f32p, _f32p]
+        L.oracle_group_amax.argtypes = [_f32p, _i64, _i64, _i32p, C.c_int32, _f32p]
+        L.oracle_num_threads.argtypes = []
+        L.oracle_num_threads.restype = C.c_int
+        L.oracle_set_num_threads.argtypes = [C.c_int]
+        L.oracle_set_num_threads.restype = None
+        _LIB = L
+    return _LIB
+
+
+def _p(a, t):
+    return None if a is None else a.ctypes.data_as(t)
+
+
+def _check(rc, what):
+    if rc != 0:
+        raise ValueError("oracle %s rejected its arguments" % what)
+
+
+def _rows_gs(gs_rows, rows):
+    if gs_rows is None:
+        return None
+    g = np.ascontiguousarray(gs_rows, dtype=np.float32)
+    if g.shape != (rows,):
+        raise ValueError("gs_rows must have one value per row")
+    return g
+
+
+def num_threads() -> int:
+    return int(lib().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    lib().oracle_set_num_threads(int(n))
+
+
+# ---- scalar primitives ------------------------------------------------------
+def bf16_to_f32(bits: int) -> float:
+    return float(lib().oracle_bf16_to_f32(int(bits)))
+
+
+def swiglu_scalar(g: float, u: float) -> float:
+    return float(lib().oracle_swiglu(float(g), float(u)))
+
+
+def fp8_encode_scalar(v: float) -> int:
+    return int(lib().oracle_fp8_e4m3_encode(float(v)))
+
+
+def fp8_decode(code: int) -> float:
+    return float(lib().oracle_fp8_e4m3_decode(int(code)))
+
+
+def e2m1_index(half_step: int) -> int:
+    return int(lib().oracle_e2m1_index(int(half_step)))
+
+
+def e2m1_decode(nibble: int) -> float:
+    return float(lib().oracle_e2m1_decode(int(nibble)))
+
+
+def quantize_block(x, gs: float = 1.0):
+    """One 16-value block -> (packed[8] uint8, sf, bsf, v[16])."""
+    xb = np.ascontiguousarray(x, dtype=np.float32)
+    assert xb.shape == (16,)
+    packed = np.zeros(8, np.uint8)
+    sf = np.zeros(1, np.uint8)
+    bsf = np.zeros(1, np.float32)
+    v = np.zeros(16, np.float32)
+    lib().oracle_quantize_block(_p(xb, _f32p), C.c_float(gs), _p(packed, _u8p),
+                                _p(sf, _u8p), _p(bsf, _f32p), _p(v, _f32p))
+    return packed, int(sf[0]), float(bsf[0]), v
+
+
+# ---- array drivers ----------------------------------------------------------
+def fp8_encode(v: np.ndarray) -> np.ndarray:
+    a = np.ascontiguousarray(v, dtype=np.float32).reshape(-1)
+    out = np.empty(a.shape, np.uint8)
+    _check(lib().oracle_fp8_encode_array(_p(a, _f32p), a.size, _p(out, _u8p)),
+           "fp8_encode")
+    return out.reshape(np.shape(v))
+
+
+def swiglu(gate_up: np.ndarray) -> np.ndarray:
+    """Interleaved BF16 [rows][2I] ([gate x8, up x8, ...]) -> FP32 [rows][I]."""
+    x = np.ascontiguousarray(gate_up, dtype=np.uint16)
+    rows, two_i = x.shape
+    inter = two_i // 2
+    y = np.empty((rows, inter), np.float32)
+    _check(lib().oracle_swiglu_rows(_p(x, _u16p), rows, inter, two_i, _p(y, _f32p)),
+           "swiglu")
+    return y
+
+
+def quantize_f32(x: np.ndarray, gs_rows=None, diag: bool = False):
+    """FP32 [rows][cols] -> packed [rows][cols/2], scales [rows][cols/16]
+    (+ bsf [rows][cols/16] and v [rows][cols] when diag)."""
+    a = np.ascontiguousarray(x, dtype=np.float32)
+    rows, cols = a.shape
+    packed = np.empty((rows, cols // 2), np.uint8)
+    scales = np.empty((rows, cols // 16), np.uint8)
+    bsf = np.empty((rows, cols // 16), np.float32) if diag else None
+    v = np.empty((rows, cols), np.float32) if diag else None
+    g = _rows_gs(gs_rows, rows)
+    _check(lib().oracle_quantize_f32_rows(_p(a, _f32p), rows, cols, cols, _p(g, _f32p),
+                                          _p(packed, _u8p), _p(scales, _u8p),
+                                          _p(bsf, _f32p), _p(v, _f32p)),
+           "quantize_f32")
+    return (packed, scales, bsf, v) if diag else (packed, scales)
+
+
+def quantize_bf16(x: np.ndarray, gs_rows=None):
+    """BF16 bits [rows][cols] -> packed [rows][cols/2], scales [rows][cols/16]."""
+    a = np.ascontiguousarray(x, dtype=np.uint16)
+    rows, cols = a.shape
+    packed = np.empty((rows, cols // 2), np.uint8)
+    scales = np.empty((rows, cols // 16), np.uint8)
+    g = _rows_gs(gs_rows, rows)
+    _check(lib().oracle_quantize_bf16_rows(_p(a, _u16p), rows, cols, cols,
+                                           _p(g, _f32p), _p(packed, _u8p),
+                                           _p(scales, _u8p)),
+           "quantize_bf16")
+    return packed, scales
+
+
+def swiglu_quantize(gate_up: np.ndarray, gs_rows=None, diag: bool = False):
+    """Fused path definition: interleaved BF16 [rows][2I] ->
+    (packed [rows][I/2], scales [rows][I/16], swiglu FP32 [rows][I]
+    [, bsf [rows][I/16], v [rows][I]])."""
+    x = np.ascontiguousarray(gate_up, dtype=np.uint16)
+    rows, two_i = x.shape
+    inter = two_i // 2
+    packed = np.empty((rows, inter // 2), np.uint8)
+    scales = np.empty((rows, inter // 16), np.uint8)
+    y = np.empty((rows, inter), np.float32)
+    bsf = np.empty((rows, inter // 16), np.float32) if diag else None
+    v = np.empty((rows, inter), np.float32) if diag else None
+    g = _rows_gs(gs_rows, rows)
+    _check(lib().oracle_swiglu_quantize_rows(_p(x, _u16p), rows, inter, two_i,
+                                             _p(g, _f32p), _p(packed, _u8p),
+                                             _p(scales, _u8p), _p(y, _f32p),
+                                             _p(bsf, _f32p), _p(v, _f32p)),
+           "swiglu_quantize")
+    return (packed, scales, y, bsf, v) if diag else (packed, scales, y)
+
+
+def dequantize(packed: np.ndarray, scales: np.ndarray, gs_rows=None) -> np.ndarray:
+    p = np.ascontiguousarray(packed, dtype=np.uint8)
+    s = np.ascontiguousarray(scales, dtype=np.uint8)
+    rows = p.shape[0]
+    cols = p.shape[1] * 2
+    if s.shape != (rows, cols // 16):
+        raise ValueError("scales shape does not match packed")
+    out = np.empty((rows, cols), np.float32)
+    g = _rows_gs(gs_rows, rows)
+    _check(lib().oracle_dequantize_rows(_p(p, _u8p), _p(s, _u8p), rows, cols,
+                                        _p(g, _f32p), _p(out, _f32p)),
+           "dequantize")
+    return out
+
+
+def group_amax(y: np.ndarray, offsets: np.ndarray) -> np.ndarray:
+    a = np.ascontiguousarray(y, dtype=np.float32)
+    o = np.ascontiguousarray(offsets, dtype=np.int32)
+    groups = o.size - 1
+    out = np.empty(groups, np.float32)
+    _check(lib().oracle_group_amax(_p(a, _f32p), a.shape[0], a.shape[1],
+                                   _p(o, _i32p), groups, _p(out, _f32p)),
+           "group_amax")
+    return out
+
+
+def expert_global_scale(amax: np.ndarray) -> np.ndarray:
+    """Two-level NVFP4 global scale per expert: gs_e = RN32(amax_e / (6*448)),
+    so that the largest block scale of the expert lands on the FP8 maximum.
+    An empty or all-zero expert gets 1.0 (its value is never used)."""
+    a = np.asarray(amax, dtype=np.float32)
+    gs = a / np.float32(6.0 * 448.0)          # binary32 IEEE division
+    return np.where(a > 0, gs, np.float32(1.0)).astype(np.float32)
+
+
+def rows_global_scale(gs: np.ndarray, offsets: np.ndarray, rows: int) -> np.ndarray:
+    """Expand per-expert scales to one value per row (row r belongs to expert
+    e when offsets[e] <= r < offsets[e+1])."""
+    o = np.asarray(offsets, dtype=np.int64)
+    g = np.asarray(gs, dtype=np.float32)
+    out = np.empty(rows, np.float32)
+    for e in range(o.size - 1):
+        out[o[e]:o[e + 1]] = g[e]
+    return out

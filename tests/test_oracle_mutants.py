@@ -1,0 +1,69 @@
+"""The pins must catch plausible mistakes in the oracle.
+
+Each case plants one mistake in a private copy of the oracle's C source (the
+kinds of bug the pages record - round-half-up, m/1024 subnormals, no mantissa
+carry, a 240 clamp, bias 8 - plus a dropped sign, swapped nibbles, swapped
+gate/up, a dropped global scale and a wrong exponent sign), builds it with gcc
+into a temporary directory, swaps it in, and requires that at least one pin
+fails. The committed oracle is never modified.
+"""
+import os
+import subprocess
+
+import pytest
+
+import oracle
+import test_oracle_pins as P
+from oracle import build as B
+
+MUTANTS = {
+    "round_half_up": ("int hs = (int)rint((double)v);",
+                      "int hs = (int)floor((double)v + 0.5);"),
+    "subnormal_1024": ("(double)m / 512.0", "(double)m / 1024.0"),
+    "no_mantissa_carry": ("if (mant == 8.0) {                    /* mantissa overflow: carry */\n        e += 1;\n        mant = 0.0;",
+                          "if (mant == 8.0) {\n        mant = 7.0;"),
+    "clamp_240": ("if (v > 448.0f)\n        v = 448.0f;", "if (v > 240.0f)\n        v = 240.0f;"),
+    "bias_8": ("int biased = e + 7;", "int biased = e + 8;"),
+    "decode_bias_8": ("ldexp(1.0 + (double)m / 8.0, e - 7)", "ldexp(1.0 + (double)m / 8.0, e - 8)"),
+    "dropped_sign": ("(signbit(x[j]) ? 8 : 0)", "0"),
+    "swapped_nibbles": ("code[2 * i] | (code[2 * i + 1] << 4)", "code[2 * i + 1] | (code[2 * i] << 4)"),
+    "swapped_gate_up": ("float g = oracle_bf16_to_f32(row[base + j % 8]);\n            float u = oracle_bf16_to_f32(row[base + 8 + j % 8]);",
+                        "float u = oracle_bf16_to_f32(row[base + j % 8]);\n            float g = oracle_bf16_to_f32(row[base + 8 + j % 8]);"),
+    "no_global_scale_in_k": ("float k = 6.0f * gs;", "float k = 6.0f;"),
+    "exp_sign": ("double y = g * u / (1.0 + exp(-g));", "double y = g * u / (1.0 + exp(g));"),
+    "no_six_clamp": ("v = 2.0f * fminf(fabsf(s), 6.0f);", "v = fminf(2.0f * fabsf(s), 13.0f);"),
+    "t7_toward_zero": ("{0, 1, 2, 3, 4, 4, 5, 6, 6, 6, 6, 7, 7}", "{0, 1, 2, 3, 4, 4, 5, 5, 6, 6, 6, 7, 7}"),
+}
+
+FAST_PINS = [P.pin_page_facts, P.pin_fp8_decode_vs_torch, P.pin_fp8_saturation,
+             P.pin_fp8_roundtrip, P.pin_e2m1_format, P.pin_e2m1_table,
+             P.pin_swiglu_vs_torch, P.pin_swiglu_closed_forms,
+             P.pin_quantize_vs_twin, P.pin_dequant_closed_form,
+             lambda: P.pin_fp8_encode_vs_torch(step=997)]
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_mutant(name, tmp_path, monkeypatch):
+    old, new = MUTANTS[name]
+    src = open(B.SRC).read()
+    assert src.count(old) == 1, "mutation target not found exactly once: " + name
+    csrc = tmp_path / "nvfp4_oracle.c"
+    csrc.write_text(src.replace(old, new))
+    hdr = os.path.join(os.path.dirname(B.SRC), "nvfp4_oracle.h")
+    (tmp_path / "nvfp4_oracle.h").write_text(open(hdr).read())
+    so = tmp_path / "libmutant.so"
+    subprocess.run(["gcc", *B.CFLAGS, str(csrc), "-o", str(so), "-lm"], check=True)
+
+    real = oracle.lib()
+    monkeypatch.setattr(B, "LIB", str(so))
+    monkeypatch.setattr(oracle, "_LIB", None)
+    try:
+        caught = []
+        for pin in FAST_PINS:
+            try:
+                pin()
+            except AssertionError:
+                caught.append(getattr(pin, "__name__", "fp8_encode_strided"))
+        assert caught, "no pin caught mutant " + name
+    finally:
+        monkeypatch.setattr(oracle, "_LIB", real)

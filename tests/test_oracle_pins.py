@@ -1,0 +1,332 @@
+"""Pins of the CPU oracle to things other than itself.
+
+* the worked facts the pages print (tests/golden/page_facts.txt);
+* PyTorch's float8_e4m3fn cast and decode (a library routine), exhaustively
+  over every binary32 in [0, 448] and all 256 codes;
+* the OCP E2M1 format definition (bias-1 exponent, 1 mantissa bit);
+* PyTorch's float64 SiLU for the SwiGLU step, plus closed forms;
+* an exact-rational restatement (tests/exact_twin.py) on small inputs,
+  including every injected edge block of the standalone workload;
+* invariants that follow from the definitions.
+
+The ``pin_*`` functions are also run by test_oracle_mutants.py against
+deliberately broken copies of the oracle, to show they catch such mistakes.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import exact_twin as twin
+import oracle
+from moe_swiglu_epilogue_amd import workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "page_facts.txt")
+
+
+def _num(s):
+    s = s.strip()
+    if s == "nan":
+        return float("nan")
+    return int(s, 16) if s.startswith("0x") else float(s)
+
+
+def _facts():
+    out = []
+    with open(GOLDEN) as f:
+        for line in f:
+            line = line.split("#", 1)[0] if line.startswith("#") else line
+            if not line.strip():
+                continue
+            body, _, cite = line.partition("|")
+            kind, a, b = body.split()
+            out.append((kind, _num(a), _num(b), cite.strip()))
+    return out
+
+
+def _block_with(value, amax=6.0):
+    x = np.zeros(16, np.float32)
+    x[0] = amax
+    x[1] = value
+    return x
+
+
+# ---- pin functions (each raises AssertionError on a mismatch) ---------------
+def pin_page_facts():
+    for kind, a, b, cite in _facts():
+        if kind == "fp8_encode":
+            got = oracle.fp8_encode_scalar(a)
+            assert got == b, (kind, a, hex(got), cite)
+        elif kind == "fp8_decode":
+            got = oracle.fp8_decode(int(a))
+            if math.isnan(b):
+                assert math.isnan(got), (kind, a, got, cite)
+            else:
+                # the pages print 6 significant digits
+                assert abs(got - b) <= 5e-7 * max(1.0, abs(b)), (kind, a, got, cite)
+        elif kind == "e2m1_nibble":
+            packed, sf, _, _ = oracle.quantize_block(_block_with(a))
+            assert sf == 0x38, "amax 6 must give scale 1.0"
+            assert packed[0] >> 4 == b, (kind, a, packed[0] >> 4, cite)
+        elif kind == "e2m1_nibble_half_up":
+            hs = int(math.floor(2 * a + 0.5))
+            assert oracle.e2m1_index(hs) == b, (kind, a, cite)
+            packed, _, _, _ = oracle.quantize_block(_block_with(a))
+            assert packed[0] >> 4 != b, "oracle must not round half up"
+        elif kind == "e2m1_index":
+            assert oracle.e2m1_index(int(a)) == b, (kind, a, cite)
+        else:
+            raise AssertionError("unknown fact kind " + kind)
+
+
+def pin_fp8_decode_vs_torch():
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float32)
+    for c in range(256):
+        got = oracle.fp8_decode(c)
+        r = float(ref[c])
+        if math.isnan(r):
+            assert math.isnan(got), hex(c)
+        else:
+            assert got == r and math.copysign(1, got) == math.copysign(1, r), (hex(c), got, r)
+
+
+def pin_fp8_encode_vs_torch(step: int = 1, chunk: int = 1 << 26):
+    """Every binary32 bit pattern in [0, 448] (step 1), or a strided subset."""
+    top = int(np.array(448.0, np.float32).view(np.uint32))
+    for start in range(0, top + 1, chunk * step):
+        stop = min(top + 1, start + chunk * step)
+        a = np.arange(start, stop, step, dtype=np.uint32).view(np.float32)
+        got = oracle.fp8_encode(a)
+        ref = torch.from_numpy(a).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        bad = np.nonzero(got != ref)[0]
+        assert bad.size == 0, ("fp8 encode differs from torch", a[bad[:5]],
+                               got[bad[:5]], ref[bad[:5]])
+
+
+def pin_fp8_saturation():
+    vals = np.array([448.0, 448.00003, 460.0, 464.0, 470.0, 480.0, 500.0, 1e4,
+                     3.0e38, np.inf], np.float32)
+    assert np.all(oracle.fp8_encode(vals) == 0x7E)
+
+
+def pin_fp8_roundtrip():
+    for c in range(0x7F):
+        assert oracle.fp8_encode_scalar(oracle.fp8_decode(c)) == c, hex(c)
+
+
+def pin_e2m1_format():
+    """The 16 E2M1 codes from the OCP bit-field definition."""
+    for nib in range(16):
+        s, e, m = nib >> 3, (nib >> 1) & 3, nib & 1
+        mag = 0.5 * m if e == 0 else 2.0 ** (e - 1) * (1 + 0.5 * m)
+        want = -mag if s else mag
+        got = oracle.e2m1_decode(nib)
+        assert got == want and math.copysign(1, got) == math.copysign(1, want), nib
+
+
+def pin_e2m1_table():
+    """step_to_idx equals ties-to-even nearest rounding of hs/2 onto the E2M1
+    grid (brute force over the grid)."""
+    from fractions import Fraction as F
+    for hs in range(13):
+        assert oracle.e2m1_index(hs) == twin.e2m1_nearest_index(F(hs, 2)), hs
+    assert oracle.e2m1_index(13) == -1 and oracle.e2m1_index(-1) == -1
+
+
+def _swiglu_inputs(n=200000, seed=11):
+    rng = np.random.default_rng(seed)
+    g = np.concatenate([rng.standard_normal(n) * 3,
+                        rng.uniform(-120, 120, n // 4),
+                        np.array([0.0, -0.0, 1e-3, -1e-3, 20, -20, 88, -88, 100, -100,
+                                  700, -700, 800, -800])])
+    u = np.concatenate([rng.standard_normal(g.size - 14) * 2,
+                        np.array([1.0, -1.0, 2.0, -3.0, 1.0, 1.0, -1.0, 1.0, 1.0,
+                                  2.0, 1.0, 1.0, -1.0, 1.0])])
+    gb = W.bf16_bits_to_f32(W.to_bf16_bits(g))
+    ub = W.bf16_bits_to_f32(W.to_bf16_bits(u))
+    return gb, ub
+
+
+def pin_swiglu_vs_torch():
+    g, u = _swiglu_inputs()
+    gate_up = W.to_bf16_bits(W.interleave(g.reshape(1, -1)[:, :g.size // 8 * 8],
+                                          u.reshape(1, -1)[:, :g.size // 8 * 8]))
+    y = oracle.swiglu(gate_up).reshape(-1)
+    n = y.size
+    gt = torch.from_numpy(g[:n].astype(np.float64))
+    ut = torch.from_numpy(u[:n].astype(np.float64))
+    ref = (torch.nn.functional.silu(gt) * ut).to(torch.float32).numpy()
+    # both are float64 evaluations rounded once to float32; allow 1 ulp
+    yi = y.view(np.int32).astype(np.int64)
+    ri = ref.view(np.int32).astype(np.int64)
+    same_sign = np.signbit(y) == np.signbit(ref)
+    ulps = np.abs(yi - ri)
+    tiny = (np.abs(ref) < 1e-37) & (np.abs(y) < 1e-37)
+    assert np.all(same_sign | tiny)
+    assert np.all((ulps <= 1) | tiny), np.max(ulps)
+    assert np.mean(ulps == 0) > 0.99
+
+
+def pin_swiglu_closed_forms():
+    # silu(0) * u = 0 with the sign of gate * up
+    for g, u in ((0.0, 1.0), (0.0, -1.0), (-0.0, 1.0), (-0.0, -1.0), (2.0, 0.0), (2.0, -0.0)):
+        y = oracle.swiglu_scalar(g, u)
+        assert y == 0.0 and math.copysign(1, y) == math.copysign(1, g) * math.copysign(1, u)
+    # for large gate, silu(g) = g to within 1 ulp of binary32, so y = RN(g*u)
+    for g in (40.0, 64.0, 100.0, 1000.0):
+        for u in (1.0, -2.5, 3.0):
+            assert oracle.swiglu_scalar(g, u) == np.float32(g * u)
+    # silu(g) - silu(-g) = g
+    for g in (0.5, 1.0, 2.0, 3.75, 7.0):
+        d = oracle.swiglu_scalar(g, 1.0) - oracle.swiglu_scalar(-g, 1.0)
+        assert abs(d - g) <= 4 * np.spacing(np.float32(g))
+    # silu(g) at a point checked by hand: g = ln 3 gives sigmoid 3/4
+    g = float(np.float32(math.log(3.0)))
+    assert abs(oracle.swiglu_scalar(g, 1.0) - 0.75 * g) <= 1e-6 * g
+
+
+def _twin_blocks():
+    rng = np.random.default_rng(21)
+    blocks = [(vals, 1.0) for _, vals in W.standalone_blocks(rng)]
+    for _ in range(150):
+        scale = 10.0 ** rng.uniform(-4, 4)
+        blocks.append((rng.standard_normal(16) * scale, 1.0))
+    for _ in range(150):
+        gs = float(np.float32(10.0 ** rng.uniform(-3, 1)))
+        scale = 10.0 ** rng.uniform(-3, 3)
+        blocks.append((rng.standard_normal(16) * scale, gs))
+    # blocks whose s values sit exactly on half-steps at a non-power-of-two scale
+    for d in (1.25, 1.75, 0.875, 3.0 / 512.0, 448.0):
+        blocks.append((np.array(twin_ties()) * d, 1.0))
+    return [(W.bf16_bits_to_f32(W.to_bf16_bits(v)), gs) for v, gs in blocks]
+
+
+def twin_ties():
+    return [6.0, 0.25, 0.75, 1.25, 1.75, 2.25, 2.5, 2.75, 3.25, 3.5, 3.75, 4.75,
+            5.0, 5.25, 5.75, -0.25]
+
+
+def pin_quantize_vs_twin():
+    for x, gs in _twin_blocks():
+        p, sf, bsf, v = oracle.quantize_block(x, gs)
+        tp, tsf, tbsf, tv = twin.quantize_block(list(x), gs)
+        assert sf == tsf, (x, gs, sf, tsf)
+        assert list(p) == tp, (x, gs, list(p), tp)
+        assert bsf == float(tbsf)
+        assert [float(a) for a in v] == [float(b) for b in tv]
+
+
+def pin_dequant_closed_form():
+    """All 127 finite scales x random nibbles x three global scales against
+    RN32(RN32(e2m1 * scale) * gs) computed from the format definitions."""
+    rng = np.random.default_rng(31)
+    scales = np.arange(0, 0x7F, dtype=np.uint8).reshape(-1, 1)
+    rows = scales.shape[0]
+    for gs in (1.0, float(np.float32(rng.uniform(1e-3, 1.0))), float(np.float32(3.3e-3))):
+        p = rng.integers(0, 256, (rows, 8)).astype(np.uint8)
+        p[0] = np.arange(0, 128, 16) | np.arange(1, 129, 16)   # all 16 nibbles once
+        out = oracle.dequantize(p, scales, np.full(rows, gs, np.float32))
+        for r in range(rows):
+            for c in range(16):
+                byte = int(p[r, c // 2])
+                nib = byte & 15 if c % 2 == 0 else byte >> 4
+                want = twin.dequant_value(nib, int(scales[r, 0]), gs)
+                assert out[r, c] == float(want), (r, c, nib, scales[r, 0], gs)
+
+
+ALL_PINS = [pin_page_facts, pin_fp8_decode_vs_torch, pin_fp8_saturation,
+            pin_fp8_roundtrip, pin_e2m1_format, pin_e2m1_table, pin_swiglu_vs_torch,
+            pin_swiglu_closed_forms, pin_quantize_vs_twin, pin_dequant_closed_form]
+
+
+# ---- tests --------------------------------------------------------------------
+@pytest.mark.parametrize("pin", ALL_PINS, ids=lambda f: f.__name__)
+def test_pin(pin):
+    pin()
+
+
+@pytest.mark.slow
+def test_fp8_encode_exhaustive_vs_torch():
+    pin_fp8_encode_vs_torch(step=1)
+
+
+def test_standalone_workload_vs_twin():
+    """Every block of the 128 x 256 standalone workload (random and injected)
+    against the exact-rational twin."""
+    w = W.standalone()
+    packed, scales = oracle.quantize_bf16(w.x)
+    x = W.bf16_bits_to_f32(w.x)
+    rng = np.random.default_rng(5)
+    nb = x.shape[1] // 16
+    injected = list(w.meta["injected"].keys())
+    sample = injected + [(int(r), int(b)) for r, b in
+                         zip(rng.integers(0, x.shape[0], 300), rng.integers(0, nb, 300))]
+    for r, b in sample:
+        tp, tsf, _, _ = twin.quantize_block(list(x[r, 16 * b:16 * b + 16]), 1.0)
+        assert scales[r, b] == tsf, (r, b)
+        assert list(packed[r, 8 * b:8 * b + 8]) == tp, (r, b)
+
+
+def test_standalone_injected_scales():
+    """The injected blocks land where the pages and the format put them."""
+    w = W.standalone()
+    _, scales = oracle.quantize_bf16(w.x)
+    x = W.bf16_bits_to_f32(w.x)
+    for (r, b), kind in w.meta["injected"].items():
+        blk = x[r, 16 * b:16 * b + 16]
+        amax = float(np.max(np.abs(blk)))
+        sf = int(scales[r, b])
+        if kind in ("zero", "negzero", "tiny"):
+            assert sf == 0x00, (kind, amax)
+        elif kind == "large":
+            want = {1440.0: 0x77, 1488.0: 0x78}.get(amax, 0x7E)
+            assert sf == want, (amax, hex(sf))
+        elif kind == "subnormal_scale":
+            assert 0x01 <= sf <= 0x08, (amax, hex(sf))
+        elif kind == "fp8_ties":
+            want = {6.375: 0x38, 7.125: 0x3A, 11.625: 0x40}[amax]
+            assert sf == want, (amax, hex(sf))
+
+
+def test_invariants_random():
+    rng = np.random.default_rng(41)
+    rows, cols = 256, 512
+    x = (rng.standard_normal((rows, cols)) *
+         10.0 ** rng.uniform(-4, 4, (rows, 1))).astype(np.float32)
+    gs = (10.0 ** rng.uniform(-2, 1, rows)).astype(np.float32)
+    packed, scales, bsf, v = oracle.quantize_f32(x, gs, diag=True)
+    assert scales.max() <= 0x7E
+    deq = oracle.dequantize(packed, scales, gs)
+    nb = cols // 16
+    for r in range(rows):
+        for b in range(nb):
+            blk = x[r, 16 * b:16 * b + 16]
+            sf = int(scales[r, b])
+            dec = oracle.fp8_decode(sf)
+            denom = np.float32(dec) * gs[r]
+            if sf == 0 or bsf[r, b] >= 448.0 or bsf[r, b] < 2.0 ** -6:
+                continue
+            # unsaturated normal-scale block: the amax element gets magnitude 7
+            j = int(np.argmax(np.abs(blk)))
+            byte = int(packed[r, 8 * b + j // 2])
+            nib = byte & 15 if j % 2 == 0 else byte >> 4
+            assert nib & 7 == 7, (r, b)
+            # reconstruction error is at most 1.25 denominators (|s| <= 6)
+            err = np.abs(deq[r, 16 * b:16 * b + 16].astype(np.float64) - blk)
+            assert np.all(err <= 1.25 * float(denom) * (1 + 2.0 ** -20)), (r, b)
+    # v is 2 min(|s|, 6): in [0, 12]
+    assert v.min() >= 0 and v.max() <= 12
+
+
+def test_zero_blocks_and_signs():
+    z = np.zeros(16, np.float32)
+    p, sf, _, _ = oracle.quantize_block(z)
+    assert sf == 0 and np.all(p == 0)
+    p, sf, _, _ = oracle.quantize_block(-z)
+    assert sf == 0 and np.all(p == 0x88)
+    # a negative value that rounds to magnitude 0 keeps its sign bit
+    x = _block_with(-0.1)
+    p, _, _, _ = oracle.quantize_block(x)
+    assert p[0] >> 4 == 0x8
