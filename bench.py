@@ -1,0 +1,212 @@
+"""Benchmark: fused SwiGLU + NVFP4 quantize on the prefill-shaped MoE L1 output.
+
+One step = one launch of ``swiglu_nvfp4_quantize`` over the whole prefill
+workload: 65536 rows of interleaved BF16 [gate x8, up x8, ...] with
+intermediate size 3072 (805,306,368 bytes read), writing 65536 x 1536 packed
+E2M1 bytes and 65536 x 192 FP8 scale bytes. Inputs are seeded synthetic data
+(gate/up ~ N(0,1) times a per-row lognormal(0,1) factor), resident in HBM
+before timing starts.
+
+Prints ONE JSON line with the throughput (HBM GB/s over the algorithmic bytes,
+4.5625 B per output element), the roofline of the fused kernel, the CPU
+oracle's throughput on the host cores, and secondary figures (standalone
+quantize, dequantize, a device copy of the same input as a ceiling).
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0               # MI355X HBM3E peak, 8 TB/s
+ROWS, INTER = 65536, 3072
+BYTES_PER_ELEM = 4.5625             # 4 B read (gate+up BF16) + 0.5 B codes + 1/16 B scale
+ALG_BYTES = int(ROWS * INTER * BYTES_PER_ELEM)      # 918,552,576
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "swiglu_nvfp4_kernel_prefill_pmc.json")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in ("moe_swiglu_epilogue_amd/csrc/moe_nvfp4.hip",
+                "moe_swiglu_epilogue_amd/csrc/nvfp4_device.hpp"):
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per launch from the committed rocprofv3 counter summary, when
+    it was taken on the current kernel source; else None."""
+    try:
+        with open(PMC_SUMMARY) as f:
+            s = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if s.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    return s.get("traffic_bytes_per_launch")
+
+
+def time_launches(fn, steps, warmup):
+    """Warm up, then time `steps` launches: wall clock between two device
+    synchronizations, and per-launch HIP events on the launch stream."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record()
+        fn()
+        ends[i].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    return wall, per
+
+
+def cpu_baseline(x):
+    """The CPU oracle on the same prefill input: all host threads over the
+    whole workload (median of 3), plus one thread over 16384 rows."""
+    import oracle
+    n_elem = x.shape[0] * (x.shape[1] // 2)
+    threads = oracle.num_threads()
+    times = []
+    for _ in range(3):
+        t = time.perf_counter()
+        oracle.swiglu_quantize(x)
+        times.append(time.perf_counter() - t)
+    med = statistics.median(times)
+    oracle.set_num_threads(1)
+    sub = x[:16384]
+    t = time.perf_counter()
+    oracle.swiglu_quantize(sub)
+    one = time.perf_counter() - t
+    oracle.set_num_threads(threads)
+    one_elem = sub.shape[0] * (sub.shape[1] // 2)
+    return {
+        "value": round(n_elem * BYTES_PER_ELEM / med / 1e9, 3),
+        "unit": "GB/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": "full prefill workload 65536x6144 BF16, median of 3 passes on %d threads "
+                  "(%.2f s each); 1 thread over 16384 rows: %.3f GB/s"
+                  % (threads, med, one_elem * BYTES_PER_ELEM / one / 1e9),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the fused SwiGLU+NVFP4 path has no cross-GPU "
+              "step (rows shard with no exchange); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import moe_swiglu_epilogue_amd as M
+    from moe_swiglu_epilogue_amd import workloads as W
+
+    print("[bench] generating prefill workload %dx%d" % (ROWS, 2 * INTER), file=sys.stderr, flush=True)
+    w = W.prefill(rows=ROWS, inter=INTER)
+    dev = torch.device("cuda:0")
+    x = torch.from_numpy(w.x.view(np.int16)).to(dev).view(torch.bfloat16)
+    packed = torch.empty((ROWS, INTER // 2), dtype=torch.uint8, device=dev)
+    scales = torch.empty((ROWS, INTER // 16), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    def step():
+        M.swiglu_nvfp4_quantize(x, packed=packed, scales=scales)
+
+    print("[bench] timing %d steps after %d warmup" % (args.steps, args.warmup), file=sys.stderr, flush=True)
+    wall, per = time_launches(step, args.steps, args.warmup)
+    ms_per_step = wall * 1e3 / args.steps
+    value = ALG_BYTES / (wall / args.steps) / 1e9
+    kern_ms = statistics.mean(per)
+    achieved = ALG_BYTES / (kern_ms / 1e3) / 1e9
+
+    secondary = None
+    if not args.no_secondary:
+        print("[bench] secondary: quantize, dequantize, copy ceiling", file=sys.stderr, flush=True)
+        secondary = {}
+        # standalone quantize of a compact BF16 tensor of the same output shape
+        xq = x.view(torch.int16)[:, :INTER].contiguous().view(torch.bfloat16)
+        pq = torch.empty_like(packed)
+        sq = torch.empty_like(scales)
+        _, perq = time_launches(lambda: M.nvfp4_quantize(xq, packed=pq, scales=sq), 20, 3)
+        mq = statistics.mean(perq)
+        secondary["nvfp4_quantize"] = {
+            "shape": [ROWS, INTER], "bytes_per_launch": int(ROWS * INTER * 2.5625),
+            "ms": round(mq, 4), "GB_s": round(ROWS * INTER * 2.5625 / mq / 1e6, 1)}
+        del xq, pq, sq
+        out = torch.empty((ROWS, INTER), dtype=torch.float32, device=dev)
+        _, perd = time_launches(lambda: M.nvfp4_dequantize(packed, scales, out=out), 20, 3)
+        md = statistics.mean(perd)
+        secondary["nvfp4_dequantize"] = {
+            "shape": [ROWS, INTER], "bytes_per_launch": int(ROWS * INTER * 4.5625),
+            "ms": round(md, 4), "GB_s": round(ROWS * INTER * 4.5625 / md / 1e6, 1)}
+        del out
+        dst = torch.empty_like(x)
+        _, perc = time_launches(lambda: dst.copy_(x), 20, 3)
+        mc = statistics.mean(perc)
+        copy_gbs = 2 * x.numel() * 2 / mc / 1e6
+        secondary["device_copy_ceiling"] = {
+            "bytes_per_launch": 2 * x.numel() * 2, "ms": round(mc, 4), "GB_s": round(copy_gbs, 1),
+            "fused_frac_of_copy": round(achieved / copy_gbs, 4)}
+        del dst
+        secondary["fused_kernel_ms_p10_p50_p90"] = [
+            round(float(np.percentile(per, q)), 4) for q in (10, 50, 90)]
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle on host cores)", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(w.x)
+
+    line = {
+        "metric": "fused SwiGLU+NVFP4 quantize HBM GB/s and % of MI355X peak, prefill shape",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded; gate/up N(0,1) x per-row lognormal(0,1))",
+        "config": {"workload": "prefill-shaped MoE L1 epilogue", "rows": ROWS,
+                   "intermediate": INTER, "input": [ROWS, 2 * INTER],
+                   "layout": "interleaved [gate x8, up x8]", "global_scale": 1.0,
+                   "alg_bytes_per_step": ALG_BYTES, "parallelism": "single GPU"},
+        "pct_of_peak": round(100.0 * value / PEAK_HBM_GBS, 2),
+        "elements_per_s": round(ROWS * INTER / (wall / args.steps), 1),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": measured_traffic(),
+                     "kernel": "swiglu_nvfp4_kernel", "kernel_ms": round(kern_ms, 5)},
+        "cpu_baseline": cpu,
+        "secondary": secondary,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,142 @@
+/*
+ * moe_nvfp4.h - C ABI of libmoe_nvfp4.so: NVFP4 block quantization and the
+ * fused SwiGLU + NVFP4 quantize step of an MoE L1 epilogue, on MI355X
+ * (gfx950) with hand-written HIP kernels.
+ *
+ * The method comes from the "nvfp4-megamoe-kernel" project log pages
+ * (2026-05-28): "NVFP4-1.1_APPROACH_PART_2.md" (FP8 E4M3 scale rules, the
+ * half-step E2M1 rounding, the fused-epilogue write path) and
+ * "NVFP4-1.1_APPROACH.md" ("Revised approach: Compact SwiGLU output": the
+ * interleaved [gate x8, up x8, ...] BF16 L1 output; "Implementation plan").
+ *
+ * Formats
+ *   NVFP4 block   16 consecutive values along a row -> 8 bytes of E2M1 codes
+ *                 (element 2i in the low nibble of byte i, 2i+1 in the high
+ *                 nibble; code = sign << 3 | magnitude index, magnitudes
+ *                 {0, .5, 1, 1.5, 2, 3, 4, 6}) plus one FP8 E4M3 scale byte.
+ *   scale byte    OCP E4M3 ("fn"): bias 7, exponent field 0..15, exp 15 with
+ *                 mantissa 7 is NaN and never written, largest value 448,
+ *                 subnormals m/512, round to nearest even with mantissa carry
+ *                 into the exponent, saturating at 448 (0x7e).
+ *   global scale  gs, FP32, decode direction: value ~ e2m1 * scale * gs.
+ *   per block     bsf = RN(amax / RN(6 gs)); sf = E4M3(bsf);
+ *                 d = RN(E4M3value(sf) * gs); s = RN(x / d) (0 when d == 0);
+ *                 code magnitude = step_to_idx[rint(2 min(|s|, 6))] with
+ *                 ties to even; sign = IEEE sign bit of x.
+ *
+ * Layouts (all row-major; ld_* are row pitches in ELEMENTS of that tensor)
+ *   plain input   x[rows][ld_x] BF16 (raw uint16 bit patterns), cols used.
+ *   fused input   gate_up[rows][ld_in] BF16, 2*inter columns used, laid out
+ *                 as repeating 8-wide subtiles [gate x8, up x8]: output
+ *                 column j reads gate at 16*(j/8) + j%8 and up at
+ *                 16*(j/8) + 8 + j%8.
+ *   packed        [rows][cols/2] bytes, contiguous (pitch cols/2).
+ *   scales        [rows][cols/16] bytes, contiguous (pitch cols/16).
+ *   swiglu_out    [rows][inter] FP32, contiguous (optional debug output).
+ *   out           [rows][cols] FP32, contiguous.
+ *
+ * Global scales and experts
+ *   gs == NULL                      every row uses 1.0.
+ *   gs != NULL, expert_offsets NULL gs[0] is used for every row.
+ *   expert_offsets != NULL          num_experts >= 1 groups of rows: row r
+ *                                   belongs to expert e when
+ *                                   expert_offsets[e] <= r < expert_offsets[e+1];
+ *                                   it uses gs[e] (or 1.0 when gs == NULL).
+ *                                   expert_offsets has num_experts + 1
+ *                                   int32 entries, starts at 0, is
+ *                                   non-decreasing and ends at rows. Empty
+ *                                   experts are allowed.
+ *
+ * Memory and ownership
+ *   Every pointer is a DEVICE pointer (HIP/PyTorch allocations), except that
+ *   none is dereferenced on the host. The caller owns every buffer. The
+ *   library allocates nothing, keeps no state between calls, never
+ *   synchronizes, and enqueues exactly one kernel on `stream` (NULL = the
+ *   default stream). Inputs and outputs must not overlap. Every byte of the
+ *   output regions described above is written.
+ *
+ * Preconditions checked on the host, before any HIP call (so they work on a
+ * machine without a GPU) - a failing check returns without launching:
+ *   rows, cols/inter >= 0; cols (inter) % 16 == 0; ld >= used columns;
+ *   required pointers non-NULL; BF16 input base and row pitch 16-byte
+ *   aligned; packed 8-byte aligned; FP32 outputs 16-byte aligned;
+ *   num_experts >= 1 exactly when expert_offsets != NULL; rows < 2^31 and
+ *   rows * ceil(cols / 1024) <= 2^30 (tiles of 64 blocks).
+ *   rows == 0 or cols == 0 is a successful no-op.
+ * Not checked (device data, asynchronous): finite inputs; gs finite, > 0
+ *   and within [2^-100, 2^100]; the offset rules above. Violations give
+ *   unspecified output bytes, never out-of-bounds accesses on the output
+ *   region for rows that the offsets place inside [0, rows).
+ * Errors: a launch failure reported by hipGetLastError() returns
+ *   NVFP4_ERROR_LAUNCH; faults during execution surface at the caller's next
+ *   synchronization, as usual for HIP.
+ */
+#ifndef MOE_NVFP4_H
+#define MOE_NVFP4_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    NVFP4_SUCCESS = 0,
+    NVFP4_ERROR_INVALID_VALUE = 1,     /* negative size, NULL pointer, bad ld, experts */
+    NVFP4_ERROR_UNSUPPORTED_SHAPE = 2, /* cols/inter not a multiple of 16, too large */
+    NVFP4_ERROR_MISALIGNED = 3,        /* base or pitch alignment rule broken */
+    NVFP4_ERROR_LAUNCH = 4             /* hipGetLastError() after the launch */
+} nvfp4_status_t;
+
+/*
+ * Standalone NVFP4 quantize of a BF16 tensor.
+ * Page: "2026-05-28_STATUS.md", "GPU-only NVFP4 quantize" (byte-exact with
+ * the Python reference) and "NVFP4-1.1_APPROACH_PART_2.md" (quantize_nvfp4.cu
+ * half-step rounding). Reads x[rows][cols] (pitch ld_x), writes
+ * packed[rows][cols/2] and scales[rows][cols/16].
+ */
+nvfp4_status_t nvfp4_quantize(const uint16_t *x, int64_t rows, int64_t cols,
+                              int64_t ld_x, const float *gs,
+                              const int32_t *expert_offsets, int32_t num_experts,
+                              uint8_t *packed, uint8_t *scales,
+                              hipStream_t stream);
+
+/*
+ * Fused SwiGLU + NVFP4 quantize (the MoE L1 epilogue as a standalone pass).
+ * Page: "NVFP4-1.1_APPROACH_PART_2.md", fused-epilogue design (SiLU of the
+ * gate subtile, SwiGLU of the up subtile kept in FP32, two up subtiles per
+ * FP4 block, amax + FP8 scale + E2M1 pack) and "NVFP4-1.1_APPROACH.md"
+ * (interleaved [gate x8, up x8] L1 layout). Reads gate_up[rows][2*inter]
+ * (pitch ld_in), computes y = silu(gate) * up in FP32 and writes
+ * packed[rows][inter/2], scales[rows][inter/16] and, when swiglu_out is not
+ * NULL, the FP32 y values [rows][inter] (a debug output: the quantized bytes
+ * are the same with or without it).
+ */
+nvfp4_status_t swiglu_nvfp4_quantize(const uint16_t *gate_up, int64_t rows,
+                                     int64_t inter, int64_t ld_in,
+                                     const float *gs,
+                                     const int32_t *expert_offsets,
+                                     int32_t num_experts, uint8_t *packed,
+                                     uint8_t *scales, float *swiglu_out,
+                                     hipStream_t stream);
+
+/*
+ * NVFP4 dequantize: out[r][c] = RN(RN(e2m1(code) * E4M3value(sf)) * gs_row).
+ * Page: "2026-05-28_STATUS.md" commit list (fp8_e4m3_to_float32) and the
+ * E2M1 code definition. Reads packed[rows][cols/2] and scales[rows][cols/16],
+ * writes out[rows][cols] FP32.
+ */
+nvfp4_status_t nvfp4_dequantize(const uint8_t *packed, const uint8_t *scales,
+                                int64_t rows, int64_t cols, const float *gs,
+                                const int32_t *expert_offsets,
+                                int32_t num_experts, float *out,
+                                hipStream_t stream);
+
+/* Static English text for a status code (never NULL). */
+const char *nvfp4_status_string(nvfp4_status_t status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_NVFP4_H */

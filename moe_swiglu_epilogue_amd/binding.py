@@ -1,0 +1,192 @@
+"""ctypes binding of libmoe_nvfp4.so (include/moe_nvfp4.h).
+
+Argument marshalling only: the functions take torch tensors that live on the
+GPU, check dtypes and shapes, allocate missing outputs with ``torch.empty``,
+and pass raw device pointers, sizes and torch's current HIP stream to the
+C ABI. Every step of the computation runs in the library's kernels. If the
+library is missing, loading it raises: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_nvfp4.so")
+
+STATUS = {0: "NVFP4_SUCCESS", 1: "NVFP4_ERROR_INVALID_VALUE",
+          2: "NVFP4_ERROR_UNSUPPORTED_SHAPE", 3: "NVFP4_ERROR_MISALIGNED",
+          4: "NVFP4_ERROR_LAUNCH"}
+
+EXPORTS = ("nvfp4_quantize", "swiglu_nvfp4_quantize", "nvfp4_dequantize",
+           "nvfp4_status_string")
+
+_LIB = None
+_vp = C.c_void_p
+_i64 = C.c_int64
+_i32 = C.c_int32
+
+
+class Nvfp4Error(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        text = _lib().nvfp4_status_string(status).decode()
+        super().__init__("%s: %s (%s)" % (what, STATUS.get(status, status), text))
+
+
+def library_path() -> str:
+    return LIB_PATH
+
+
+def _lib():
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                "libmoe_nvfp4.so is not built (%s); run "
+                "`python -m moe_swiglu_epilogue_amd.build`" % LIB_PATH)
+        L = C.CDLL(LIB_PATH)
+        L.nvfp4_quantize.argtypes = [_vp, _i64, _i64, _i64, _vp, _vp, _i32, _vp, _vp, _vp]
+        L.nvfp4_quantize.restype = C.c_int
+        L.swiglu_nvfp4_quantize.argtypes = [_vp, _i64, _i64, _i64, _vp, _vp, _i32, _vp,
+                                            _vp, _vp, _vp]
+        L.swiglu_nvfp4_quantize.restype = C.c_int
+        L.nvfp4_dequantize.argtypes = [_vp, _vp, _i64, _i64, _vp, _vp, _i32, _vp, _vp]
+        L.nvfp4_dequantize.restype = C.c_int
+        L.nvfp4_status_string.argtypes = [C.c_int]
+        L.nvfp4_status_string.restype = C.c_char_p
+        _LIB = L
+    return _LIB
+
+
+def raw():
+    """The loaded ctypes library (for callers that pass raw pointers)."""
+    return _lib()
+
+
+# ---- marshalling helpers -----------------------------------------------------
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _bf16_matrix(t: torch.Tensor, name: str) -> torch.Tensor:
+    if t.dtype == torch.bfloat16:
+        t = t.view(torch.int16)
+    if t.dtype not in (torch.int16, torch.uint16):
+        raise TypeError("%s must be bfloat16 (or its 16-bit bit pattern)" % name)
+    if not t.is_cuda:
+        raise TypeError("%s must be a GPU tensor" % name)
+    if t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1):
+        raise ValueError("%s must be a 2-D tensor with unit column stride" % name)
+    return t
+
+
+def _pitch(t: torch.Tensor) -> int:
+    return t.stride(0) if t.shape[0] > 1 else t.shape[1]
+
+
+def _experts(gs, expert_offsets, device):
+    if gs is not None:
+        if gs.dtype != torch.float32 or gs.device != device or not gs.is_contiguous():
+            raise TypeError("gs must be a contiguous float32 tensor on the input's device")
+    if expert_offsets is None:
+        if gs is not None and gs.numel() < 1:
+            raise ValueError("gs must hold at least one value")
+        return 0
+    if (expert_offsets.dtype != torch.int32 or expert_offsets.device != device
+            or not expert_offsets.is_contiguous()):
+        raise TypeError("expert_offsets must be a contiguous int32 tensor on the input's device")
+    e = expert_offsets.numel() - 1
+    if e < 1:
+        raise ValueError("expert_offsets must hold num_experts + 1 >= 2 entries")
+    if gs is not None and gs.numel() != e:
+        raise ValueError("gs must hold one value per expert")
+    return e
+
+
+def _out(t, shape, dtype, device, name):
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    if t.shape != torch.Size(shape) or t.dtype != dtype or t.device != device or not t.is_contiguous():
+        raise ValueError("%s must be a contiguous %s tensor of shape %s" % (name, dtype, tuple(shape)))
+    return t
+
+
+def _call(fn, what, *args):
+    st = fn(*args)
+    if st != 0:
+        raise Nvfp4Error(st, what)
+
+
+# ---- the three entry points -----------------------------------------------------
+def nvfp4_quantize(x: torch.Tensor, gs: torch.Tensor | None = None,
+                   expert_offsets: torch.Tensor | None = None, *,
+                   packed: torch.Tensor | None = None, scales: torch.Tensor | None = None,
+                   stream=None):
+    """BF16 [rows, cols] -> (packed uint8 [rows, cols/2], scales uint8 [rows, cols/16])."""
+    x = _bf16_matrix(x, "x")
+    rows, cols = x.shape
+    e = _experts(gs, expert_offsets, x.device)
+    packed = _out(packed, (rows, cols // 2), torch.uint8, x.device, "packed")
+    scales = _out(scales, (rows, cols // 16), torch.uint8, x.device, "scales")
+    _call(_lib().nvfp4_quantize, "nvfp4_quantize", _ptr(x), rows, cols, _pitch(x), _ptr(gs),
+          _ptr(expert_offsets), e, _ptr(packed), _ptr(scales), _stream(stream))
+    return packed, scales
+
+
+def swiglu_nvfp4_quantize(gate_up: torch.Tensor, gs: torch.Tensor | None = None,
+                          expert_offsets: torch.Tensor | None = None, *,
+                          packed: torch.Tensor | None = None,
+                          scales: torch.Tensor | None = None,
+                          swiglu_out: torch.Tensor | bool | None = None, stream=None):
+    """Interleaved BF16 [rows, 2I] ([gate x8, up x8, ...]) -> (packed [rows, I/2],
+    scales [rows, I/16]) and, when ``swiglu_out`` is True or a tensor, the FP32
+    SwiGLU values [rows, I] as a third result."""
+    x = _bf16_matrix(gate_up, "gate_up")
+    rows, two_i = x.shape
+    if two_i % 2:
+        raise ValueError("gate_up must have an even number of columns")
+    inter = two_i // 2
+    e = _experts(gs, expert_offsets, x.device)
+    packed = _out(packed, (rows, inter // 2), torch.uint8, x.device, "packed")
+    scales = _out(scales, (rows, inter // 16), torch.uint8, x.device, "scales")
+    y = None
+    if swiglu_out is True:
+        y = torch.empty((rows, inter), dtype=torch.float32, device=x.device)
+    elif isinstance(swiglu_out, torch.Tensor):
+        y = _out(swiglu_out, (rows, inter), torch.float32, x.device, "swiglu_out")
+    _call(_lib().swiglu_nvfp4_quantize, "swiglu_nvfp4_quantize", _ptr(x), rows, inter,
+          _pitch(x), _ptr(gs), _ptr(expert_offsets), e, _ptr(packed), _ptr(scales),
+          _ptr(y), _stream(stream))
+    return (packed, scales) if y is None else (packed, scales, y)
+
+
+def nvfp4_dequantize(packed: torch.Tensor, scales: torch.Tensor,
+                     gs: torch.Tensor | None = None,
+                     expert_offsets: torch.Tensor | None = None, *,
+                     out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """(packed uint8 [rows, cols/2], scales uint8 [rows, cols/16]) -> FP32 [rows, cols]."""
+    if packed.dtype != torch.uint8 or scales.dtype != torch.uint8:
+        raise TypeError("packed and scales must be uint8")
+    if not packed.is_cuda or scales.device != packed.device:
+        raise TypeError("packed and scales must be GPU tensors on one device")
+    if not packed.is_contiguous() or not scales.is_contiguous():
+        raise ValueError("packed and scales must be contiguous")
+    rows, half = packed.shape
+    cols = 2 * half
+    if tuple(scales.shape) != (rows, cols // 16):
+        raise ValueError("scales must have shape (rows, cols/16)")
+    e = _experts(gs, expert_offsets, packed.device)
+    out = _out(out, (rows, cols), torch.float32, packed.device, "out")
+    _call(_lib().nvfp4_dequantize, "nvfp4_dequantize", _ptr(packed), _ptr(scales), rows, cols,
+          _ptr(gs), _ptr(expert_offsets), e, _ptr(out), _stream(stream))
+    return out

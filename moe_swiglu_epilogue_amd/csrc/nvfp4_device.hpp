@@ -1,0 +1,195 @@
+// Device-side arithmetic of NVFP4 block quantization for gfx950.
+//
+// Method: "nvfp4-megamoe-kernel" project log (2026-05-28),
+// "NVFP4-1.1_APPROACH_PART_2.md" (FP8 E4M3 scale rules, half-step E2M1
+// rounding, fused-epilogue design) and "2026-05-28_STATUS.md" (the commit
+// listing the quantization primitives and their five fixes).
+//
+// Every function here reproduces the binary32 definition of the method
+// exactly (bit for bit), except swiglu(), which is a fast FP32 evaluation
+// within a few ulps of the correctly rounded value.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+// ---- BF16 -> FP32 (exact: a BF16 is the top half of a binary32) ------------
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// ---- SwiGLU: silu(g) * u = g * u / (1 + e^-g) in FP32 ----------------------
+// e^-g = 2^(-g log2 e). The product -g * log2(e) is carried as hi + lo (lo is
+// the exact rounding error of hi plus the tail of log2 e), so that the
+// exponential keeps ~1 ulp relative accuracy for |g| up to 88; v_exp_f32 of
+// hi is then corrected by the factor (1 + lo ln 2). Error budget: v_exp_f32
+// 1 ulp, v_rcp_f32 1 ulp, four roundings: < 5 ulp, about 6e-7 relative.
+// g < -88.7 overflows e to +inf and gives y = +-0 (true |y| < 1e-36).
+__device__ __forceinline__ float swiglu(float g, float u)
+{
+    const float kLog2e = 0x1.715476p+0f;     // RN(log2 e)
+    const float kLog2eLo = 0x1.4ae0c0p-26f;  // log2 e - kLog2e
+    const float kLn2 = 0x1.62e430p-1f;       // RN(ln 2)
+    const float t = -g;
+    const float hi = t * kLog2e;
+    float lo = __builtin_fmaf(t, kLog2e, -hi);
+    lo = __builtin_fmaf(t, kLog2eLo, lo);
+    float e = __builtin_amdgcn_exp2f(hi);
+    e = e * __builtin_fmaf(lo, kLn2, 1.0f);
+    const float sig = __builtin_amdgcn_rcpf(1.0f + e);
+    return (g * u) * sig;
+}
+
+// ---- FP8 E4M3 ("fn") encode of a non-negative block scale -------------------
+// Saturates at 448 (exp 15 / mant 6; exp 15 / mant 7 is NaN and never made).
+// v < 2^-6 is subnormal, value m / 512: m = rint(v * 512) (exact product,
+// ties to even; m == 8 is the smallest normal, code 0x08 as well).
+// Otherwise round the binary32 mantissa to 3 bits, ties to even, by adding
+// 0x7ffff plus the kept LSB; a carry out of the mantissa moves into the
+// exponent by itself (250 -> 256 = 0x78); rebias 127 -> 7.
+__device__ __forceinline__ uint32_t fp8_e4m3_encode(float v)
+{
+    v = fminf(v, 448.0f);
+    const uint32_t sub = (uint32_t)__builtin_rintf(v * 512.0f);
+    const uint32_t b = __float_as_uint(v);
+    const uint32_t nrm = ((b + 0x7ffffu + ((b >> 20) & 1u)) >> 20) - (120u << 3);
+    return v < 0x1p-6f ? sub : nrm;
+}
+
+// ---- FP8 E4M3 decode (finite codes 0x00..0x7e) -----------------------------
+// e == 0: m / 512; else 2^(e-7) (1 + m/8), built directly as binary32 bits.
+__device__ __forceinline__ float fp8_e4m3_decode(uint32_t code)
+{
+    const uint32_t e = code >> 3;
+    const uint32_t m = code & 7u;
+    const float nrm = __uint_as_float(((e + 120u) << 23) | (m << 20));
+    const float sub = (float)m * 0x1p-9f;
+    return e ? nrm : sub;
+}
+
+// Per-block constants of the element quantizer.
+struct BlockScale {
+    uint32_t sf;   // E4M3 scale byte
+    float half_d;  // d / 2, d = RN(decode(sf) * gs)
+    float rcp;     // RN(1 / half_d) = RN(2 / d); 0 when d == 0
+};
+
+// amax -> scale byte and element-quantizer constants.
+//   bsf = RN(amax / k) with k = RN(6 gs) (IEEE division), sf = E4M3(bsf),
+//   d = RN(decode(sf) * gs).
+__device__ __forceinline__ BlockScale block_scale(float amax, float gs, float k)
+{
+    BlockScale s;
+    const float bsf = amax / k;
+    s.sf = fp8_e4m3_encode(bsf);
+    const float d = fp8_e4m3_decode(s.sf) * gs;
+    s.half_d = 0.5f * d;
+    const float r = 1.0f / s.half_d;          // IEEE division, correctly rounded
+    s.rcp = d != 0.0f ? r : 0.0f;
+    return s;
+}
+
+// One element -> signed half-step value h = +-rint(2 min(|s|,6)) / 2, ready
+// for the E2M1 convert. s2 = RN(2x / d) = 2 RN(x / d) is formed without a
+// division: q0 = RN(x * RN(2/d)), then one Newton/Markstein correction with
+// the exact remainder x - q0 (d/2) gives the correctly rounded quotient
+// (checked exhaustively on the CPU for every FP8 scale mantissa and every
+// binary32 numerator mantissa; beyond that it is Markstein's theorem).
+// When d == 0 the magnitude is 0 (rcp == 0 makes q0, q1 zero).
+__device__ __forceinline__ float half_step(float x, const BlockScale& s)
+{
+    const float q0 = x * s.rcp;
+    const float rem = __builtin_fmaf(-q0, s.half_d, x);
+    const float q1 = __builtin_fmaf(rem, s.rcp, q0);
+    const float v = fminf(__builtin_fabsf(q1), 12.0f);   // 2 min(|s|, 6)
+    const float h = __builtin_rintf(v) * 0.5f;            // ties to even
+    // sign = IEEE sign bit of x (also for -0 and values rounding to 0)
+    return __uint_as_float(__float_as_uint(h) | (__float_as_uint(x) & 0x80000000u));
+}
+
+// Two signed half-step values -> one byte of E2M1 codes (first value in the
+// low nibble) placed at byte `sel` of `word`. The half-step grid {0, .5, 1,
+// ..., 6} maps onto E2M1 by round-to-nearest-even, which is exactly the
+// step_to_idx table (2.5 -> 2, 3.5 -> 4, 4.5 -> 4, 5 -> 4, 5.5 -> 6); scale 1.
+template <int sel>
+__device__ __forceinline__ uint32_t pack_e2m1(uint32_t word, float h0, float h1)
+{
+    return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, h0, h1, 1.0f, sel);
+}
+
+// 16 FP32 values -> 8 bytes of packed E2M1 codes (returned as uint2) and the
+// scale byte.
+__device__ __forceinline__ uint2 quantize16(const float (&y)[16], float gs, float k,
+                                            uint32_t& sf_out)
+{
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+        amax = fmaxf(amax, __builtin_fabsf(y[j]));
+    const BlockScale s = block_scale(amax, gs, k);
+    float h[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+        h[j] = half_step(y[j], s);
+    uint32_t w0 = 0, w1 = 0;
+    w0 = pack_e2m1<0>(w0, h[0], h[1]);
+    w0 = pack_e2m1<1>(w0, h[2], h[3]);
+    w0 = pack_e2m1<2>(w0, h[4], h[5]);
+    w0 = pack_e2m1<3>(w0, h[6], h[7]);
+    w1 = pack_e2m1<0>(w1, h[8], h[9]);
+    w1 = pack_e2m1<1>(w1, h[10], h[11]);
+    w1 = pack_e2m1<2>(w1, h[12], h[13]);
+    w1 = pack_e2m1<3>(w1, h[14], h[15]);
+    sf_out = s.sf;
+    return make_uint2(w0, w1);
+}
+
+// Byte `sel` of `word` (two E2M1 codes, low nibble first) -> two FP32
+// values RN(RN(e2m1 * dec) * gs). The convert with scale 1 is exact.
+template <int sel>
+__device__ __forceinline__ void dequant_byte(uint32_t word, float dec, float gs, float* out)
+{
+    const auto v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, sel);
+    out[0] = (v[0] * dec) * gs;
+    out[1] = (v[1] * dec) * gs;
+}
+
+// 8 packed bytes + scale -> 16 dequantized FP32 values:
+// RN(RN(e2m1 * decode(sf)) * gs); the inner product is exact.
+__device__ __forceinline__ void dequantize16(uint2 packed, uint32_t sf, float gs,
+                                             float* out)
+{
+    const float dec = fp8_e4m3_decode(sf);
+    dequant_byte<0>(packed.x, dec, gs, out + 0);
+    dequant_byte<1>(packed.x, dec, gs, out + 2);
+    dequant_byte<2>(packed.x, dec, gs, out + 4);
+    dequant_byte<3>(packed.x, dec, gs, out + 6);
+    dequant_byte<0>(packed.y, dec, gs, out + 8);
+    dequant_byte<1>(packed.y, dec, gs, out + 10);
+    dequant_byte<2>(packed.y, dec, gs, out + 12);
+    dequant_byte<3>(packed.y, dec, gs, out + 14);
+}
+
+// Global scale of a row: gs[0], or gs[e] of the expert holding the row
+// (largest e with offsets[e] <= row), or 1.0 without gs. `row` is
+// wave-uniform, so the search runs on scalar registers and loads.
+__device__ __forceinline__ float row_global_scale(const float* gs, const int32_t* offsets,
+                                                  int num_experts, int row)
+{
+    int e = 0;
+    if (offsets != nullptr) {
+        int lo = 0, hi = num_experts;
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (offsets[mid] <= row)
+                lo = mid;
+            else
+                hi = mid;
+        }
+        e = lo;
+    }
+    return gs != nullptr ? gs[e] : 1.0f;
+}
+
+}  // namespace nvfp4

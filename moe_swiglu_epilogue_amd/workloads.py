@@ -25,11 +25,28 @@ Workloads (rows x interleaved BF16 columns):
 from __future__ import annotations
 
 import hashlib
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field
 
 import numpy as np
 
 CHUNK_ROWS = 4096
+
+
+def _workers() -> int:
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def _run_chunks(fn, n: int) -> None:
+    """Run fn(k) for k in range(n) on a thread pool (NumPy's generators and
+    array arithmetic release the GIL); results must not depend on order."""
+    if n <= 1:
+        for k in range(n):
+            fn(k)
+        return
+    with ThreadPoolExecutor(max_workers=_workers()) as ex:
+        list(ex.map(fn, range(n)))
 
 
 # ---- layout helpers (no method arithmetic) -----------------------------------
@@ -175,8 +192,11 @@ def prefill_chunk(k: int, seed: int = 4, inter: int = 3072,
 def prefill(seed: int = 4, rows: int = 65536, inter: int = 3072) -> Workload:
     n_chunks = (rows + CHUNK_ROWS - 1) // CHUNK_ROWS
     x = np.empty((rows, 2 * inter), np.uint16)
-    for k in range(n_chunks):
+
+    def fill(k):
         x[k * CHUNK_ROWS:(k + 1) * CHUNK_ROWS] = prefill_chunk(k, seed, inter, rows)
+
+    _run_chunks(fill, n_chunks)
     return Workload("prefill", x, fused=True, meta={"seed": seed})
 
 
@@ -203,13 +223,16 @@ def ragged(seed: int = 5, rows: int = 131072, inter: int = 2048,
     factors = np.random.default_rng(children[0]).lognormal(0.0, 1.0, experts)
     row_expert = np.repeat(np.arange(experts), np.diff(off.astype(np.int64)))
     x = np.empty((rows, 2 * inter), np.uint16)
-    for k in range(n_chunks):
+
+    def fill(k):
         r0, r1 = k * CHUNK_ROWS, min(rows, (k + 1) * CHUNK_ROWS)
         rng = np.random.default_rng(children[k + 1])
         f = factors[row_expert[r0:r1]][:, None]
         g = rng.standard_normal((r1 - r0, inter)) * f
         u = rng.standard_normal((r1 - r0, inter)) * f
         x[r0:r1] = to_bf16_bits(interleave(g, u))
+
+    _run_chunks(fill, n_chunks)
     return Workload("ragged", x, fused=True, offsets=off,
                     meta={"seed": seed, "experts": experts})
 

@@ -1,0 +1,129 @@
+"""C ABI on the host, no GPU needed: the library loads, exports every symbol
+that include/moe_nvfp4.h declares, and rejects bad arguments with the
+documented status before touching HIP."""
+import ctypes as C
+import os
+import re
+import subprocess
+
+import pytest
+import torch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_nvfp4.h")
+
+OK, INVALID, SHAPE, MISALIGNED = 0, 1, 2, 3
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from moe_swiglu_epilogue_amd import binding, build
+    if not os.path.exists(binding.LIB_PATH):
+        build.build()
+    return binding.raw()
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+char\s*\*|nvfp4_status_t)\s*(\w+)\s*\(",
+                                 text, re.M)))
+
+
+def test_header_declares_the_entry_points():
+    assert _declared() == sorted(["nvfp4_quantize", "swiglu_nvfp4_quantize",
+                                  "nvfp4_dequantize", "nvfp4_status_string"])
+
+
+def test_library_exports_every_declared_symbol(lib):
+    from moe_swiglu_epilogue_amd import binding
+    out = subprocess.run(["nm", "-D", "--defined-only", binding.LIB_PATH],
+                         capture_output=True, text=True, check=True).stdout
+    exported = set(l.split()[-1] for l in out.splitlines() if " T " in l)
+    for name in _declared():
+        assert name in exported, name
+        assert getattr(lib, name) is not None
+    assert set(_declared()) == set(binding.EXPORTS)
+
+
+def test_header_compiles_as_c(tmp_path):
+    src = tmp_path / "t.c"
+    src.write_text('#include "moe_nvfp4.h"\nint main(void){return (int)NVFP4_SUCCESS;}\n')
+    subprocess.run(["gcc", "-std=c11", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"),
+                    "-I", "/opt/rocm/include", "-c", str(src), "-o", str(tmp_path / "t.o")],
+                   check=True)
+
+
+def test_status_strings(lib):
+    for s in range(5):
+        assert lib.nvfp4_status_string(s)
+    assert lib.nvfp4_status_string(99) == b"unknown status"
+
+
+A16 = 0x10000      # a fake 16-byte-aligned "device" address, never dereferenced
+
+
+def q(lib, x=A16, rows=4, cols=32, ld=32, gs=None, offs=None, ne=0, packed=A16, scales=A16):
+    return lib.nvfp4_quantize(x, rows, cols, ld, gs, offs, ne, packed, scales, None)
+
+
+def f(lib, x=A16, rows=4, inter=32, ld=64, gs=None, offs=None, ne=0, packed=A16,
+      scales=A16, y=None):
+    return lib.swiglu_nvfp4_quantize(x, rows, inter, ld, gs, offs, ne, packed, scales, y, None)
+
+
+def d(lib, packed=A16, scales=A16, rows=4, cols=32, gs=None, offs=None, ne=0, out=A16):
+    return lib.nvfp4_dequantize(packed, scales, rows, cols, gs, offs, ne, out, None)
+
+
+def test_quantize_validation(lib):
+    assert q(lib, rows=-1) == INVALID
+    assert q(lib, cols=-16) == INVALID
+    assert q(lib, cols=24, ld=24) == SHAPE
+    assert q(lib, ld=16) == INVALID
+    assert q(lib, x=None) == INVALID
+    assert q(lib, packed=None) == INVALID
+    assert q(lib, scales=None) == INVALID
+    assert q(lib, x=A16 + 2) == MISALIGNED
+    assert q(lib, ld=36) == MISALIGNED            # 72-byte pitch
+    assert q(lib, packed=A16 + 4) == MISALIGNED
+    assert q(lib, ne=3) == INVALID                # experts without offsets
+    assert q(lib, offs=A16, ne=0) == INVALID      # offsets without experts
+    assert q(lib, offs=A16, ne=-1) == INVALID
+    assert q(lib, rows=2**31, cols=16, ld=16) == SHAPE
+    # empty problems succeed without launching (NULL pointers are fine)
+    assert q(lib, x=None, rows=0, packed=None, scales=None) == OK
+    assert q(lib, x=None, cols=0, ld=0, packed=None, scales=None) == OK
+
+
+def test_fused_validation(lib):
+    assert f(lib, rows=-1) == INVALID
+    assert f(lib, inter=8, ld=16) == SHAPE
+    assert f(lib, ld=63) == INVALID
+    assert f(lib, ld=68) == MISALIGNED
+    assert f(lib, x=A16 + 8) == MISALIGNED
+    assert f(lib, y=A16 + 8) == MISALIGNED
+    assert f(lib, x=None) == INVALID
+    assert f(lib, ne=2) == INVALID
+    assert f(lib, inter=2**62, ld=2**62) == INVALID
+    assert f(lib, rows=0, x=None, packed=None, scales=None) == OK
+
+
+def test_dequant_validation(lib):
+    assert d(lib, rows=-1) == INVALID
+    assert d(lib, cols=8) == SHAPE
+    assert d(lib, out=A16 + 4) == MISALIGNED
+    assert d(lib, packed=A16 + 1) == MISALIGNED
+    assert d(lib, out=None) == INVALID
+    assert d(lib, offs=A16, ne=0) == INVALID
+    assert d(lib, rows=0, packed=None, scales=None, out=None) == OK
+
+
+def test_binding_rejects_host_tensors():
+    import moe_swiglu_epilogue_amd as M
+    x = torch.zeros(4, 32, dtype=torch.bfloat16)
+    with pytest.raises(TypeError):
+        M.nvfp4_quantize(x)
+    with pytest.raises(TypeError):
+        M.swiglu_nvfp4_quantize(torch.zeros(4, 64, dtype=torch.bfloat16))
+    with pytest.raises(TypeError):
+        M.nvfp4_dequantize(torch.zeros(4, 16, dtype=torch.uint8), torch.zeros(4, 2, dtype=torch.uint8))

@@ -1,0 +1,296 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle, on the GPU.
+
+Standalone quantize and dequantize are bit-exact; the fused SwiGLU + NVFP4
+path follows the acceptance rules in tests/parity.py. Workloads: the 128x256
+standalone tensor with its injected edge blocks, the 512x4096 and 8192x4096
+fused tensors (every element checked), the 65536x6144 prefill tensor and the
+131072x4096 ragged 256-expert tensor at full size (sampled rows checked
+element by element, the rest by properties), plus edge cases.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import parity as P
+from moe_swiglu_epilogue_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print("[gpu]", *a, flush=True)
+
+
+@pytest.fixture(scope="module")
+def M():
+    import moe_swiglu_epilogue_amd as M
+    assert torch.cuda.is_available(), "these tests need the GPU"
+    M.binding.raw()     # loads libmoe_nvfp4.so or raises
+    return M
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def dev_bf16(bits):
+    return dev(bits.view(np.int16)).view(torch.bfloat16)
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def gs_tensor(gs):
+    return None if gs is None else dev(np.asarray(gs, np.float32).reshape(-1))
+
+
+# ---- standalone quantize: bit-exact -----------------------------------------------
+def test_standalone_workload_bit_exact(M):
+    w = W.standalone()
+    say("nvfp4_quantize standalone 128x256 seed 1")
+    p, s = M.nvfp4_quantize(dev_bf16(w.x))
+    rp, rs = oracle.quantize_bf16(w.x)
+    P.assert_bytes_equal("scales", host(s), rs)
+    P.assert_bytes_equal("packed", host(p), rp)
+
+
+def test_standalone_e2m1_convert_all_half_steps(M):
+    """Every half-step value and sign through the hardware E2M1 convert,
+    including -0 and the ties 2.5, 3.5, 5 (d = 1, scale byte 0x38)."""
+    vals = np.array([k / 2 for k in range(13)] + [0.0, 6.0, 6.0], np.float64)
+    rows = np.stack([vals, -vals, np.where(np.arange(16) % 2 == 0, vals, -vals)])
+    x = W.to_bf16_bits(rows)
+    say("nvfp4_quantize half-step blocks")
+    p, s = M.nvfp4_quantize(dev_bf16(x))
+    rp, rs = oracle.quantize_bf16(x)
+    assert np.all(host(s) == 0x38)
+    P.assert_bytes_equal("packed", host(p), rp)
+
+
+@pytest.mark.parametrize("rows,cols,ld,seed", [
+    (1, 16, 16, 1), (3, 48, 48, 2), (7, 1600, 1600, 3), (64, 4096, 4104, 4),
+    (257, 1040, 1048, 5), (1000, 256, 256, 6)])
+def test_standalone_shapes_bit_exact(M, rows, cols, ld, seed):
+    rng = np.random.default_rng(seed)
+    full = W.random_plain(rows, ld, seed, scale=10.0 ** rng.uniform(-3, 3))
+    gs = np.float32(rng.uniform(0.01, 2.0))
+    say("nvfp4_quantize", rows, cols, "ld", ld, "gs", gs)
+    xt = dev_bf16(full)[:, :cols]
+    p, s = M.nvfp4_quantize(xt, gs_tensor(gs))
+    rp, rs = oracle.quantize_bf16(full[:, :cols], np.full(rows, gs, np.float32))
+    P.assert_bytes_equal("scales", host(s), rs)
+    P.assert_bytes_equal("packed", host(p), rp)
+
+
+def test_standalone_experts_bit_exact(M):
+    rows, cols, E = 3000, 512, 37
+    x = W.random_plain(rows, cols, 8, scale=3.0)
+    off = W.random_offsets(rows, E, seed=9, empty=6)
+    gs = (10.0 ** np.random.default_rng(10).uniform(-3, 0, E)).astype(np.float32)
+    say("nvfp4_quantize experts", rows, cols, E)
+    p, s = M.nvfp4_quantize(dev_bf16(x), gs_tensor(gs), dev(off))
+    rp, rs = oracle.quantize_bf16(x, oracle.rows_global_scale(gs, off, rows))
+    P.assert_bytes_equal("scales", host(s), rs)
+    P.assert_bytes_equal("packed", host(p), rp)
+
+
+# ---- fused path ----------------------------------------------------------------------
+def run_fused(M, x, gs=None, off=None, rows_gs=None, debug=True):
+    xt = dev_bf16(x)
+    out = M.swiglu_nvfp4_quantize(xt, gs_tensor(gs), None if off is None else dev(off),
+                                  swiglu_out=debug)
+    return [host(t) for t in out]
+
+
+def fused_check(M, x, what, gs=None, off=None):
+    rows = x.shape[0]
+    gs_rows = None
+    if gs is not None:
+        gs_rows = (oracle.rows_global_scale(gs, off, rows) if off is not None
+                   else np.full(rows, gs, np.float32))
+    say("swiglu_nvfp4_quantize", what, x.shape)
+    p, s, y = run_fused(M, x, gs, off)
+    rp, rs, ry, rbsf, rv = oracle.swiglu_quantize(x, gs_rows, diag=True)
+    rep = P.fused_report(p, s, y, rp, rs, ry, rbsf, rv, gs_rows)
+    say(what, rep)
+    P.assert_fused_ok(rep, what)
+    # the production launch (no FP32 debug output) writes the same bytes
+    p2, s2 = run_fused(M, x, gs, off, debug=False)
+    P.assert_bytes_equal(what + " production packed", p2, p)
+    P.assert_bytes_equal(what + " production scales", s2, s)
+    return rep
+
+
+def test_fused_small_workload(M):
+    fused_check(M, W.fused_small().x, "fused_small 512x4096")
+
+
+def test_fused_decode_workload(M):
+    fused_check(M, W.decode().x, "decode 8192x4096")
+
+
+@pytest.mark.parametrize("rows,inter,seed,scale", [
+    (1, 16, 1, 1.0), (5, 48, 2, 4.0), (33, 1040, 3, 0.01), (130, 3072, 4, 30.0),
+    (64, 8192, 5, 1.0)])
+def test_fused_shapes(M, rows, inter, seed, scale):
+    fused_check(M, W.random_fused(rows, inter, seed, scale), "random %dx%d" % (rows, inter))
+
+
+def test_fused_global_scale_and_experts(M):
+    rows, inter, E = 2000, 512, 19
+    x = W.random_fused(rows, inter, 12, 2.0)
+    fused_check(M, x, "scalar gs", gs=np.float32(0.0371))
+    off = W.random_offsets(rows, E, seed=13, empty=4)
+    gs = (10.0 ** np.random.default_rng(14).uniform(-3, 0.5, E)).astype(np.float32)
+    fused_check(M, x, "experts", gs=gs, off=off)
+
+
+def test_fused_swiglu_extremes(M):
+    """Gate across [-100, 100] (exp over/underflow, large |g|) and zeros of
+    both signs."""
+    rows, inter = 64, 1024
+    rng = np.random.default_rng(15)
+    g = rng.uniform(-100, 100, (rows, inter))
+    u = rng.standard_normal((rows, inter)) * 10.0 ** rng.uniform(-2, 2, (rows, 1))
+    g[0, :16] = 0.0
+    g[1, :16] = -0.0
+    u[2, :16] = -0.0
+    x = W.to_bf16_bits(W.interleave(g, u))
+    fused_check(M, x, "swiglu extremes")
+
+
+def test_fused_pitched_input(M):
+    rows, inter, ld = 300, 1024, 2 * 1024 + 64
+    full = W.random_fused(rows, ld // 2, 16, 1.0)
+    say("swiglu_nvfp4_quantize pitched", rows, inter, ld)
+    xt = dev_bf16(full)[:, :2 * inter]
+    p, s = [host(t) for t in M.swiglu_nvfp4_quantize(xt)]
+    rp, rs, ry, rbsf, rv = oracle.swiglu_quantize(full[:, :2 * inter], diag=True)
+    rep = P.fused_report(p, s, None, rp, rs, ry, rbsf, rv)
+    say("pitched", rep)
+    P.assert_fused_ok(rep, "pitched")
+
+
+# ---- full-size workloads: sampled rows ------------------------------------------------
+def _sample_rows(rows, n, seed, extra=()):
+    rng = np.random.default_rng(seed)
+    pick = set(rng.choice(rows, size=min(n, rows), replace=False).tolist())
+    pick |= {0, rows - 1} | set(int(r) for r in extra if 0 <= r < rows)
+    return np.array(sorted(pick))
+
+
+def test_fused_prefill_full_size_sampled(M):
+    w = W.prefill()
+    rows, inter = w.rows, w.out_cols
+    say("swiglu_nvfp4_quantize prefill", w.x.shape)
+    xt = dev_bf16(w.x)
+    p, s = M.swiglu_nvfp4_quantize(xt)
+    p, s = host(p), host(s)
+    del xt
+    sel = _sample_rows(rows, 1024, 44)
+    rp, rs, ry, rbsf, rv = oracle.swiglu_quantize(w.x[sel], diag=True)
+    # same rows through the debug launch for the FP32 values and the re-quantize rule
+    yp, ys, yy = run_fused(M, w.x[sel])
+    P.assert_bytes_equal("debug vs production packed", yp, p[sel])
+    P.assert_bytes_equal("debug vs production scales", ys, s[sel])
+    rep = P.fused_report(p[sel], s[sel], yy, rp, rs, ry, rbsf, rv)
+    say("prefill sampled", rep)
+    P.assert_fused_ok(rep, "prefill sampled rows")
+    # properties over every row: scale bytes never NaN, zero scale <=> zero codes
+    assert s.max() <= 0x7E
+    z = s == 0
+    codes = P.nibbles(p).reshape(rows, inter // 16, 16) & 7
+    assert np.all(codes[z] == 0)
+
+
+def test_fused_ragged_experts_and_dequant(M):
+    w = W.ragged()
+    rows, inter = w.rows, w.out_cols
+    off = w.offsets
+    say("oracle swiglu for per-expert global scales", w.x.shape)
+    y_ref = oracle.swiglu(w.x)
+    gs = oracle.expert_global_scale(oracle.group_amax(y_ref, off))
+    gs_rows = oracle.rows_global_scale(gs, off, rows)
+    say("swiglu_nvfp4_quantize ragged", w.x.shape, "experts", off.size - 1)
+    xt = dev_bf16(w.x)
+    gst, offt = gs_tensor(gs), dev(off)
+    pt, st = M.swiglu_nvfp4_quantize(xt, gst, offt)
+    del xt
+    say("nvfp4_dequantize ragged")
+    dq = M.nvfp4_dequantize(pt, st, gst, offt)
+    p, s, dq = host(pt), host(st), host(dq)
+    counts = np.diff(off)
+    bounds = np.concatenate([off[:-1], off[1:] - 1])
+    sel = _sample_rows(rows, 2048, 55, extra=bounds)
+    rp, rs, ry, rbsf, rv = oracle.swiglu_quantize(w.x[sel], gs_rows[sel], diag=True)
+    rep = P.fused_report(p[sel], s[sel], None, rp, rs, ry, rbsf, rv)
+    say("ragged sampled", rep, "empty experts", int((counts == 0).sum()))
+    P.assert_fused_ok(rep, "ragged sampled rows")
+    # dequant round trip: bit-exact against the oracle's dequant of the GPU bytes
+    rdq = oracle.dequantize(p[sel], s[sel], gs_rows[sel])
+    P.assert_bytes_equal("dequant", dq[sel].view(np.uint32), rdq.view(np.uint32))
+
+
+# ---- dequantize -----------------------------------------------------------------------
+@pytest.mark.parametrize("rows,cols,seed", [(1, 16, 1), (9, 1040, 2), (513, 4096, 3)])
+def test_dequant_bit_exact(M, rows, cols, seed):
+    rng = np.random.default_rng(seed)
+    p = rng.integers(0, 256, (rows, cols // 2)).astype(np.uint8)
+    s = rng.integers(0, 0x7F, (rows, cols // 16)).astype(np.uint8)
+    gs = np.float32(rng.uniform(1e-3, 4.0))
+    say("nvfp4_dequantize", rows, cols, "gs", gs)
+    out = host(M.nvfp4_dequantize(dev(p), dev(s), gs_tensor(gs)))
+    ref = oracle.dequantize(p, s, np.full(rows, gs, np.float32))
+    P.assert_bytes_equal("dequant", out.view(np.uint32), ref.view(np.uint32))
+
+
+# ---- every byte written, deterministic ----------------------------------------------
+def test_poisoned_outputs_fully_written(M):
+    x = W.random_fused(77, 1040, 21, 1.0)
+    xt = dev_bf16(x)
+    results = []
+    for poison in (0xA5, 0x5A):
+        p = torch.full((77, 520), poison, dtype=torch.uint8, device="cuda")
+        s = torch.full((77, 65), poison, dtype=torch.uint8, device="cuda")
+        y = torch.full((77, 1040), float("nan"), dtype=torch.float32, device="cuda")
+        say("swiglu_nvfp4_quantize poison", hex(poison))
+        M.swiglu_nvfp4_quantize(xt, packed=p, scales=s, swiglu_out=y)
+        results.append((host(p), host(s), host(y)))
+    for a, b in zip(results[0], results[1]):
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
+    assert not np.isnan(results[0][2]).any()
+    xq = W.random_plain(77, 1040, 22)
+    outs = []
+    for poison in (0xA5, 0x5A):
+        p = torch.full((77, 520), poison, dtype=torch.uint8, device="cuda")
+        s = torch.full((77, 65), poison, dtype=torch.uint8, device="cuda")
+        M.nvfp4_quantize(dev_bf16(xq), packed=p, scales=s)
+        outs.append((host(p), host(s)))
+    assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])
+    o = [host(M.nvfp4_dequantize(dev(outs[0][0]), dev(outs[0][1]),
+                                 out=torch.full((77, 1040), v, device="cuda")))
+         for v in (float("nan"), 7.0)]
+    assert np.array_equal(o[0].view(np.uint32), o[1].view(np.uint32))
+
+
+def test_empty_inputs_are_noops(M):
+    x = torch.zeros((0, 64), dtype=torch.bfloat16, device="cuda")
+    p, s = M.swiglu_nvfp4_quantize(x)
+    assert p.shape == (0, 16) and s.shape == (0, 2)
+    p, s = M.nvfp4_quantize(torch.zeros((0, 32), dtype=torch.bfloat16, device="cuda"))
+    assert p.shape == (0, 16)
+    out = M.nvfp4_dequantize(torch.zeros((0, 8), dtype=torch.uint8, device="cuda"),
+                             torch.zeros((0, 1), dtype=torch.uint8, device="cuda"))
+    assert out.shape == (0, 16)
+    torch.cuda.synchronize()
+
+
+def test_bad_arguments_raise(M):
+    x = torch.zeros((4, 40), dtype=torch.bfloat16, device="cuda")   # I = 20, not /16
+    with pytest.raises(M.Nvfp4Error):
+        M.swiglu_nvfp4_quantize(x)
+    with pytest.raises(M.Nvfp4Error):
+        M.nvfp4_quantize(torch.zeros((4, 24), dtype=torch.bfloat16, device="cuda"))
