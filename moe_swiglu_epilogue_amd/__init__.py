@@ -7,13 +7,14 @@ torch tensors on the GPU, marshal pointers, sizes and the current stream, and
 call the library. Importing the package does not load the library; the first
 call does, and raises if it is missing.
 """
+import importlib
 
 __all__ = ["nvfp4_quantize", "swiglu_nvfp4_quantize", "nvfp4_dequantize",
            "Nvfp4Error", "library_path"]
 
 
 def __getattr__(name):
-    if name in __all__:
-        from . import binding
-        return getattr(binding, name)
+    if name == "binding" or name in __all__:
+        binding = importlib.import_module(__name__ + ".binding")
+        return binding if name == "binding" else getattr(binding, name)
     raise AttributeError(name)
