@@ -10,7 +10,8 @@ before timing starts.
 Prints ONE JSON line with the throughput (HBM GB/s over the algorithmic bytes,
 4.5625 B per output element), the roofline of the fused kernel, the CPU
 oracle's throughput on the host cores, and secondary figures (standalone
-quantize, dequantize, a device copy of the same input as a ceiling).
+quantize, dequantize, and in-repo read / copy kernels over the same input as
+HBM ceilings).
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -30,6 +31,19 @@ ROWS, INTER = 65536, 3072
 BYTES_PER_ELEM = 4.5625             # 4 B read (gate+up BF16) + 0.5 B codes + 1/16 B scale
 ALG_BYTES = int(ROWS * INTER * BYTES_PER_ELEM)      # 918,552,576
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "swiglu_nvfp4_kernel_prefill_pmc.json")
+CALIB_BLOCKS = 4096
+
+
+def load_calib():
+    import ctypes as C
+    from moe_swiglu_epilogue_amd import build
+    if not os.path.exists(build.CALIB_LIB):
+        raise RuntimeError("libnvfp4_calib.so is not built; run python -m moe_swiglu_epilogue_amd.build")
+    lib = C.CDLL(build.CALIB_LIB)
+    for fn in (lib.nvfp4_calib_copy, lib.nvfp4_calib_read):
+        fn.argtypes = [C.c_void_p, C.c_void_p, C.c_int64, C.c_int32, C.c_void_p]
+        fn.restype = C.c_int
+    return lib
 
 
 def kernel_source_hash() -> str:
@@ -52,6 +66,11 @@ def measured_traffic():
     if s.get("kernel_source_sha256") != kernel_source_hash():
         return None
     return s.get("traffic_bytes_per_launch")
+
+
+def checked(rc):
+    if rc != 0:
+        raise RuntimeError("calibration kernel returned %d" % rc)
 
 
 def time_launches(fn, steps, warmup):
@@ -111,6 +130,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--secondary-steps", type=int, default=20)
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -146,31 +166,45 @@ def main():
     if not args.no_secondary:
         print("[bench] secondary: quantize, dequantize, copy ceiling", file=sys.stderr, flush=True)
         secondary = {}
+        sec_steps = args.secondary_steps
         # standalone quantize of a compact BF16 tensor of the same output shape
         xq = x.view(torch.int16)[:, :INTER].contiguous().view(torch.bfloat16)
         pq = torch.empty_like(packed)
         sq = torch.empty_like(scales)
-        _, perq = time_launches(lambda: M.nvfp4_quantize(xq, packed=pq, scales=sq), 20, 3)
+        _, perq = time_launches(lambda: M.nvfp4_quantize(xq, packed=pq, scales=sq), sec_steps, 3)
         mq = statistics.mean(perq)
         secondary["nvfp4_quantize"] = {
             "shape": [ROWS, INTER], "bytes_per_launch": int(ROWS * INTER * 2.5625),
             "ms": round(mq, 4), "GB_s": round(ROWS * INTER * 2.5625 / mq / 1e6, 1)}
         del xq, pq, sq
         out = torch.empty((ROWS, INTER), dtype=torch.float32, device=dev)
-        _, perd = time_launches(lambda: M.nvfp4_dequantize(packed, scales, out=out), 20, 3)
+        _, perd = time_launches(lambda: M.nvfp4_dequantize(packed, scales, out=out), sec_steps, 3)
         md = statistics.mean(perd)
         secondary["nvfp4_dequantize"] = {
             "shape": [ROWS, INTER], "bytes_per_launch": int(ROWS * INTER * 4.5625),
             "ms": round(md, 4), "GB_s": round(ROWS * INTER * 4.5625 / md / 1e6, 1)}
         del out
+        # in-repo calibration kernels over the same 805 MB input: HBM ceilings
+        calib = load_calib()
+        nbytes = x.numel() * 2
+        scratch = torch.empty(CALIB_BLOCKS * 16, dtype=torch.uint8, device=dev)
+        stream = torch.cuda.current_stream().cuda_stream
+        _, perr = time_launches(lambda: checked(calib.nvfp4_calib_read(
+            x.data_ptr(), scratch.data_ptr(), nbytes, CALIB_BLOCKS, stream)), sec_steps, 3)
+        mr = statistics.mean(perr)
         dst = torch.empty_like(x)
-        _, perc = time_launches(lambda: dst.copy_(x), 20, 3)
+        _, perc = time_launches(lambda: checked(calib.nvfp4_calib_copy(
+            x.data_ptr(), dst.data_ptr(), nbytes, CALIB_BLOCKS, stream)), sec_steps, 3)
         mc = statistics.mean(perc)
-        copy_gbs = 2 * x.numel() * 2 / mc / 1e6
-        secondary["device_copy_ceiling"] = {
-            "bytes_per_launch": 2 * x.numel() * 2, "ms": round(mc, 4), "GB_s": round(copy_gbs, 1),
-            "fused_frac_of_copy": round(achieved / copy_gbs, 4)}
-        del dst
+        del dst, scratch
+        read_gbs = nbytes / mr / 1e6
+        copy_gbs = 2 * nbytes / mc / 1e6
+        secondary["calib_read_ceiling"] = {"bytes_per_launch": nbytes, "ms": round(mr, 4),
+                                           "GB_s": round(read_gbs, 1)}
+        secondary["calib_copy_ceiling"] = {"bytes_per_launch": 2 * nbytes, "ms": round(mc, 4),
+                                           "GB_s": round(copy_gbs, 1)}
+        secondary["fused_frac_of_read_ceiling"] = round(achieved / read_gbs, 4)
+        secondary["fused_frac_of_copy_ceiling"] = round(achieved / copy_gbs, 4)
         secondary["fused_kernel_ms_p10_p50_p90"] = [
             round(float(np.percentile(per, q)), 4) for q in (10, 50, 90)]
 

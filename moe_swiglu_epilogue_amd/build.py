@@ -1,4 +1,5 @@
-"""Build libmoe_nvfp4.so (HIP kernels for gfx950 + the C ABI) with hipcc.
+"""Build libmoe_nvfp4.so (HIP kernels for gfx950 + the C ABI) and the
+bandwidth-calibration library libnvfp4_calib.so with hipcc.
 
 The library is built in-tree, next to this file, so that it travels with the
 source tree. Run ``python -m moe_swiglu_epilogue_amd.build``.
@@ -10,9 +11,9 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SRC = os.path.join(HERE, "csrc", "moe_nvfp4.hip")
-DEPS = [SRC, os.path.join(HERE, "csrc", "nvfp4_device.hpp"),
-        os.path.join(ROOT, "include", "moe_nvfp4.h")]
 LIB = os.path.join(HERE, "libmoe_nvfp4.so")
+CALIB_SRC = os.path.join(HERE, "csrc", "calib.hip")
+CALIB_LIB = os.path.join(HERE, "libnvfp4_calib.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
@@ -26,8 +27,14 @@ FLAGS = [
 
 
 def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), SRC, "-o", tmp]
+    """Build both libraries; return the path of libmoe_nvfp4.so."""
+    _build_one(CALIB_SRC, CALIB_LIB, verbose)
+    return _build_one(SRC, LIB, verbose)
+
+
+def _build_one(src: str, lib: str, verbose: bool) -> str:
+    tmp = lib + ".tmp%d" % os.getpid()
+    cmd = [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), src, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -37,8 +44,8 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed:\n" + err)
     if verbose and err.strip():
         print(err)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 def asm(out_path: str) -> None:

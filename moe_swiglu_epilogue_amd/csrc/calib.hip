@@ -1,0 +1,84 @@
+// libnvfp4_calib.so: bandwidth calibration kernels for gfx950 (declared in
+// include/nvfp4_calib.h). They move a known number of bytes with the same
+// access style as the NVFP4 kernels (16-byte non-temporal lane accesses,
+// wave64, 256-thread workgroups), so that their timings give the achievable
+// HBM ceiling and their rocprofv3 FETCH_SIZE / WRITE_SIZE readings give the
+// counter-to-bytes scale used to turn counters into HBM traffic.
+#include "../../include/nvfp4_calib.h"
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+constexpr int kThreads = 256;
+constexpr int kUnroll = 4;
+
+// dst[i] = src[i] for n16 16-byte words.
+__global__ __launch_bounds__(kThreads) void calib_copy_kernel(const u32x4* __restrict__ src,
+                                                              u32x4* __restrict__ dst, int64_t n16)
+{
+    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n16; i += stride)
+        __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
+}
+
+// out[block] = xor of every 16-byte word the workgroup read (keeps the loads
+// alive); reads n16 words, writes one word per workgroup.
+__global__ __launch_bounds__(kThreads) void calib_read_kernel(const u32x4* __restrict__ src,
+                                                              u32x4* __restrict__ out, int64_t n16)
+{
+    __shared__ u32x4 part[kThreads];
+    u32x4 acc = {0u, 0u, 0u, 0u};
+    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    for (; i + (kUnroll - 1) * stride < n16; i += kUnroll * stride) {
+        u32x4 v[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u)
+            v[u] = __builtin_nontemporal_load(src + i + u * stride);
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u)
+            acc ^= v[u];
+    }
+    for (; i < n16; i += stride)
+        acc ^= __builtin_nontemporal_load(src + i);
+    part[threadIdx.x] = acc;
+    __syncthreads();
+    for (int s = kThreads / 2; s > 0; s >>= 1) {
+        if (threadIdx.x < s)
+            part[threadIdx.x] ^= part[threadIdx.x + s];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0)
+        out[blockIdx.x] = part[0];
+}
+
+}  // namespace
+
+extern "C" {
+
+int nvfp4_calib_copy(const void* src, void* dst, int64_t bytes, int32_t blocks, hipStream_t stream)
+{
+    if (bytes < 0 || bytes % 16 != 0 || blocks < 1 || ((uintptr_t)src | (uintptr_t)dst) % 16)
+        return 1;
+    if (bytes == 0)
+        return 0;
+    hipLaunchKernelGGL(calib_copy_kernel, dim3(blocks), dim3(kThreads), 0, stream,
+                       (const u32x4*)src, (u32x4*)dst, bytes / 16);
+    return hipGetLastError() == hipSuccess ? 0 : 4;
+}
+
+int nvfp4_calib_read(const void* src, void* out, int64_t bytes, int32_t blocks, hipStream_t stream)
+{
+    if (bytes < 0 || bytes % 16 != 0 || blocks < 1 || ((uintptr_t)src | (uintptr_t)out) % 16)
+        return 1;
+    if (bytes == 0)
+        return 0;
+    hipLaunchKernelGGL(calib_read_kernel, dim3(blocks), dim3(kThreads), 0, stream,
+                       (const u32x4*)src, (u32x4*)out, bytes / 16);
+    return hipGetLastError() == hipSuccess ? 0 : 4;
+}
+
+}  // extern "C"

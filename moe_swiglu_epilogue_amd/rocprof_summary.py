@@ -1,0 +1,132 @@
+"""Turn rocprofv3 CSV output into the short text/JSON summaries kept under
+profiles/.
+
+  stats: kernel-trace statistics (calls, average/min/max duration per kernel)
+         from a `rocprofv3 --kernel-trace --stats -f csv` run.
+  pmc:   HBM traffic of one kernel from two counter runs
+         (`--pmc FETCH_SIZE`, then `--pmc WRITE_SIZE`, both in KiB per
+         dispatch), each scaled by what the same counter reads for the
+         calibration copy kernel, which moves a known number of bytes.
+
+Usage:
+  python -m moe_swiglu_epilogue_amd.rocprof_summary stats DIR OUT.txt --cmd "..."
+  python -m moe_swiglu_epilogue_amd.rocprof_summary pmc FETCH_DIR WRITE_DIR OUT \\
+      --kernel swiglu_nvfp4_kernel --calib calib_copy_kernel --calib-bytes N \\
+      --alg-bytes N --source-sha256 H --cmd "..."
+"""
+import argparse
+import csv
+import glob
+import json
+import os
+import statistics
+import sys
+
+
+def _one(dir_, suffix):
+    hits = sorted(glob.glob(os.path.join(dir_, "**", "*" + suffix), recursive=True))
+    if not hits:
+        raise SystemExit("no *%s under %s" % (suffix, dir_))
+    return hits
+
+
+def _short(name):
+    base = name.split("(")[0]
+    return base.split("::")[-1].strip() or name
+
+
+def stats(args):
+    rows = []
+    for path in _one(args.dir, "kernel_stats.csv"):
+        with open(path) as f:
+            rows += list(csv.DictReader(f))
+    lines = ["# rocprofv3 kernel-trace statistics", "", "command:", "  " + args.cmd, "",
+             "%-40s %6s %12s %12s %12s %7s" % ("kernel", "calls", "avg_us", "min_us", "max_us", "pct")]
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        lines.append("%-40s %6s %12.3f %12.3f %12.3f %7.2f" % (
+            _short(r["Name"])[:40], r["Calls"], float(r["AverageNs"]) / 1e3,
+            float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
+    text = "\n".join(lines) + "\n"
+    with open(args.out, "w") as f:
+        f.write(text)
+    print(text)
+
+
+def _counter(dir_, counter):
+    per = {}
+    for path in _one(dir_, "counter_collection.csv"):
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r.get("Counter_Name") != counter:
+                    continue
+                per.setdefault(_short(r["Kernel_Name"]), []).append(float(r["Counter_Value"]))
+    return per
+
+
+def pmc(args):
+    fetch = _counter(args.fetch_dir, "FETCH_SIZE")
+    write = _counter(args.write_dir, "WRITE_SIZE")
+
+    def avg(d, k):
+        hit = [v for name, vs in d.items() if name.startswith(k) for v in vs]
+        if not hit:
+            raise SystemExit("kernel %s not found (have %s)" % (k, sorted(d)))
+        return statistics.mean(hit), len(hit)
+
+    kf, nkf = avg(fetch, args.kernel)
+    kw, nkw = avg(write, args.kernel)
+    cf, _ = avg(fetch, args.calib)
+    cw, _ = avg(write, args.calib)
+    f_scale = args.calib_bytes / (cf * 1024.0)
+    w_scale = args.calib_bytes / (cw * 1024.0)
+    fetch_b = kf * 1024.0 * f_scale
+    write_b = kw * 1024.0 * w_scale
+    out = {
+        "kernel": args.kernel,
+        "kernel_source_sha256": args.source_sha256,
+        "dispatches": {"fetch": nkf, "write": nkw},
+        "fetch_kib_per_dispatch": round(kf, 1),
+        "write_kib_per_dispatch": round(kw, 1),
+        "calib_kernel": args.calib,
+        "calib_bytes_read_and_written": args.calib_bytes,
+        "calib_fetch_kib": round(cf, 1), "calib_write_kib": round(cw, 1),
+        "fetch_scale": round(f_scale, 5), "write_scale": round(w_scale, 5),
+        "traffic_bytes_per_launch": int(round(fetch_b + write_b)),
+        "traffic_read_bytes": int(round(fetch_b)), "traffic_write_bytes": int(round(write_b)),
+        "alg_bytes_per_launch": args.alg_bytes,
+        "traffic_over_alg": round((fetch_b + write_b) / args.alg_bytes, 4),
+        "command": args.cmd,
+    }
+    with open(args.out + ".json", "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    text = ["# rocprofv3 HBM counters: %s" % args.kernel, "", "commands:", "  " + args.cmd, ""]
+    text += ["%-28s %s" % (k, v) for k, v in out.items() if k != "command"]
+    with open(args.out + ".txt", "w") as f:
+        f.write("\n".join(text) + "\n")
+    print("\n".join(text))
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="what", required=True)
+    a = sub.add_parser("stats")
+    a.add_argument("dir")
+    a.add_argument("out")
+    a.add_argument("--cmd", required=True)
+    b = sub.add_parser("pmc")
+    b.add_argument("fetch_dir")
+    b.add_argument("write_dir")
+    b.add_argument("out", help="output path without extension (.json and .txt are written)")
+    b.add_argument("--kernel", required=True)
+    b.add_argument("--calib", required=True)
+    b.add_argument("--calib-bytes", type=int, required=True)
+    b.add_argument("--alg-bytes", type=int, required=True)
+    b.add_argument("--source-sha256", required=True)
+    b.add_argument("--cmd", required=True)
+    args = ap.parse_args(argv)
+    (stats if args.what == "stats" else pmc)(args)
+
+
+if __name__ == "__main__":
+    main(sys.argv[1:])

@@ -11,6 +11,7 @@ import torch
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "moe_nvfp4.h")
+CALIB_HEADER = os.path.join(ROOT, "include", "nvfp4_calib.h")
 
 OK, INVALID, SHAPE, MISALIGNED = 0, 1, 2, 3
 
@@ -23,10 +24,16 @@ def lib():
     return binding.raw()
 
 
-def _declared():
-    text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:const\s+char\s*\*|nvfp4_status_t)\s*(\w+)\s*\(",
+def _declared(path=HEADER):
+    text = open(path).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+char\s*\*|nvfp4_status_t|int)\s*(\w+)\s*\(",
                                  text, re.M)))
+
+
+def _exported(lib_path):
+    out = subprocess.run(["nm", "-D", "--defined-only", lib_path],
+                         capture_output=True, text=True, check=True).stdout
+    return set(l.split()[-1] for l in out.splitlines() if " T " in l)
 
 
 def test_header_declares_the_entry_points():
@@ -36,18 +43,32 @@ def test_header_declares_the_entry_points():
 
 def test_library_exports_every_declared_symbol(lib):
     from moe_swiglu_epilogue_amd import binding
-    out = subprocess.run(["nm", "-D", "--defined-only", binding.LIB_PATH],
-                         capture_output=True, text=True, check=True).stdout
-    exported = set(l.split()[-1] for l in out.splitlines() if " T " in l)
+    exported = _exported(binding.LIB_PATH)
     for name in _declared():
         assert name in exported, name
         assert getattr(lib, name) is not None
     assert set(_declared()) == set(binding.EXPORTS)
 
 
+def test_calib_library_exports_its_header(lib):
+    import ctypes as C
+    from moe_swiglu_epilogue_amd import build
+    names = _declared(CALIB_HEADER)
+    assert names == ["nvfp4_calib_copy", "nvfp4_calib_read"]
+    assert set(names) <= _exported(build.CALIB_LIB)
+    cl = C.CDLL(build.CALIB_LIB)
+    for fn in (cl.nvfp4_calib_copy, cl.nvfp4_calib_read):
+        fn.argtypes = [C.c_void_p, C.c_void_p, C.c_int64, C.c_int32, C.c_void_p]
+        assert fn(A16, A16, 24, 8, None) == 1        # not a multiple of 16
+        assert fn(A16, A16 + 4, 32, 8, None) == 1    # misaligned
+        assert fn(A16, A16, 32, 0, None) == 1        # no workgroups
+        assert fn(A16, A16, 0, 8, None) == 0         # empty: no launch
+
+
 def test_header_compiles_as_c(tmp_path):
     src = tmp_path / "t.c"
-    src.write_text('#include "moe_nvfp4.h"\nint main(void){return (int)NVFP4_SUCCESS;}\n')
+    src.write_text('#include "moe_nvfp4.h"\n#include "nvfp4_calib.h"\n'
+                   'int main(void){return (int)NVFP4_SUCCESS;}\n')
     subprocess.run(["gcc", "-std=c11", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"),
                     "-I", "/opt/rocm/include", "-c", str(src), "-o", str(tmp_path / "t.o")],
                    check=True)
