@@ -13,37 +13,49 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kThreads = 256;
-constexpr int kUnroll = 4;
+constexpr int kWavesPerBlock = kThreads / 64;
+constexpr int kTileWords = 256;     // 4 KB per wave tile, 4 coalesced 1 KB loads
 
-// dst[i] = src[i] for n16 16-byte words.
+// dst[i] = src[i] for n16 16-byte words; wave tiles of 256 words, word
+// j*64 + lane of the tile in instruction j.
 __global__ __launch_bounds__(kThreads) void calib_copy_kernel(const u32x4* __restrict__ src,
                                                               u32x4* __restrict__ dst, int64_t n16)
 {
-    const int64_t stride = (int64_t)gridDim.x * kThreads;
-    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n16; i += stride)
-        __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
+    const int lane = threadIdx.x & 63;
+    const int64_t wave = blockIdx.x * (int64_t)kWavesPerBlock + (threadIdx.x >> 6);
+    const int64_t stride = (int64_t)gridDim.x * kWavesPerBlock;
+    for (int64_t base = wave * kTileWords; base < n16; base += stride * kTileWords) {
+        u32x4 v[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (base + j * 64 + lane < n16)
+                v[j] = __builtin_nontemporal_load(src + base + j * 64 + lane);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (base + j * 64 + lane < n16)
+                __builtin_nontemporal_store(v[j], dst + base + j * 64 + lane);
+    }
 }
 
 // out[block] = xor of every 16-byte word the workgroup read (keeps the loads
-// alive); reads n16 words, writes one word per workgroup.
+// alive); reads n16 words with the same tile pattern, writes one word per
+// workgroup.
 __global__ __launch_bounds__(kThreads) void calib_read_kernel(const u32x4* __restrict__ src,
                                                               u32x4* __restrict__ out, int64_t n16)
 {
     __shared__ u32x4 part[kThreads];
     u32x4 acc = {0u, 0u, 0u, 0u};
-    const int64_t stride = (int64_t)gridDim.x * kThreads;
-    int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-    for (; i + (kUnroll - 1) * stride < n16; i += kUnroll * stride) {
-        u32x4 v[kUnroll];
+    const int lane = threadIdx.x & 63;
+    const int64_t wave = blockIdx.x * (int64_t)kWavesPerBlock + (threadIdx.x >> 6);
+    const int64_t stride = (int64_t)gridDim.x * kWavesPerBlock;
+    for (int64_t base = wave * kTileWords; base < n16; base += stride * kTileWords) {
+        u32x4 v[4] = {};
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u)
-            v[u] = __builtin_nontemporal_load(src + i + u * stride);
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u)
-            acc ^= v[u];
+        for (int j = 0; j < 4; ++j)
+            if (base + j * 64 + lane < n16)
+                v[j] = __builtin_nontemporal_load(src + base + j * 64 + lane);
+        acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
     }
-    for (; i < n16; i += stride)
-        acc ^= __builtin_nontemporal_load(src + i);
     part[threadIdx.x] = acc;
     __syncthreads();
     for (int s = kThreads / 2; s > 0; s >>= 1) {

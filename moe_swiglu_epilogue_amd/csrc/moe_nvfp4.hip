@@ -43,122 +43,256 @@ __device__ __forceinline__ u32x4 ld_stream(const u32x4* p) { return __builtin_no
 __device__ __forceinline__ u32x2 ld_stream(const u32x2* p) { return __builtin_nontemporal_load(p); }
 __device__ __forceinline__ void st_stream(f32x4 v, f32x4* p) { __builtin_nontemporal_store(v, p); }
 
+// Orders this wave's LDS accesses (stores before the loads that follow and
+// vice versa). LDS operations of one wave execute in order, so a compiler
+// barrier plus a wavefront-scope fence is enough; no s_barrier is needed
+// because each wave owns its staging area.
+__device__ __forceinline__ void wave_lds_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+}
+
+// LDS slot of 16-byte word w of a staged tile: one pad slot after every 16
+// words. Global memory is read (or written) one word per lane with
+// consecutive lanes on consecutive words; each lane works on the P (2 or 4)
+// consecutive words of its own block. With the padding both patterns hit 8
+// (or 16) distinct 16-byte bank groups per LDS cycle, and a lane's own block
+// is contiguous, so its P accesses share one address plus immediate offsets.
+constexpr int kStageSlots(int P) { return kTileBlocks * P + kTileBlocks * P / 16; }
+
+__device__ __forceinline__ int lds_slot(int w) { return w + (w >> 4); }
+
+struct Tile {
+    int row;
+    int blk0;   // first block of the tile within the row
+    int nblk;   // blocks in this tile (64, fewer in a row's last tile)
+};
+
+__device__ __forceinline__ Tile tile_at(int tile, const Geometry& geo)
+{
+    Tile t;
+    t.row = uniform(tile / geo.cpr);
+    t.blk0 = uniform((tile - t.row * geo.cpr) * kTileBlocks);
+    t.nblk = uniform(min(kTileBlocks, geo.bpr - t.blk0));
+    return t;
+}
+
 // ---------------------------------------------------------------------------
-// Fused SwiGLU + NVFP4 quantize.
-// Lane input: 64 contiguous bytes = [g0..7][u0..7][g8..15][u8..15] (BF16).
+// Quantize kernels (fused SwiGLU + NVFP4, and plain BF16 -> NVFP4).
+// A block's input is P words: 4 for the fused input [g0..7][u0..7][g8..15]
+// [u8..15] (64 bytes), 2 for plain BF16 (32 bytes). Each wave walks its tiles
+// with a stride of the whole grid and keeps one tile in flight: it issues the
+// coalesced loads of the next tile, computes the staged tile from LDS (each
+// lane its own block), stores it, and then stages the next tile.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kThreads) void swiglu_nvfp4_kernel(
+// Coalesced loads of a tile: instruction j reads word j*64 + lane. In a
+// row's last, partial tile the lanes past the end re-read the last word
+// (clamped, no branch), so every load and LDS store is unconditional and the
+// compiler can wait for exactly the loads it needs.
+template <int P>
+__device__ __forceinline__ void load_tile(u32x4 (&v)[P], const uint16_t* in, int64_t ld,
+                                          const Tile& t, int lane)
+{
+    const u32x4* src = reinterpret_cast<const u32x4*>(in + (int64_t)t.row * ld) + t.blk0 * P;
+    const int last = t.nblk * P - 1;
+#pragma unroll
+    for (int j = 0; j < P; ++j)
+        v[j] = ld_stream(src + min(j * kWave + lane, last));
+}
+
+template <int P>
+__device__ __forceinline__ void stage_tile(u32x4* lds, const u32x4 (&v)[P], int lane)
+{
+#pragma unroll
+    for (int j = 0; j < P; ++j)
+        lds[lds_slot(j * kWave + lane)] = v[j];
+}
+
+// Buffer resource over `bytes` bytes at `base` (raw, stride 0). Stores at an
+// offset past `bytes` are discarded by the hardware's range check, which is
+// how lanes without data of a kind skip a store without a branch.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_over(void* base, int bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, bytes, 0x00020000);
+}
+
+constexpr int kOffRange = 0x7ffffff0;   // a store offset past any tile's output
+constexpr int kOutStorePolicy = 17;     // output stores: sc0 sc1 (system scope; measured fastest)
+
+// Writes one tile's quantized output: block b's 8 packed bytes and its scale
+// byte (lanes past a partial tile's end carry block b = nblk - 1 again).
+// Wide path - every row's block count a multiple of 16, packed and scales
+// 16-byte aligned: the 8*nblk + nblk bytes go through the wave's LDS area
+// (packed at 0, scales at 512) and leave as 16-byte lane stores, lane L
+// writing LDS bytes [16L, 16L + 16): lanes 0..31 the packed bytes, lanes
+// 32..63 the scale bytes, each through a buffer resource that spans exactly
+// that tile's bytes of its kind, so the other lanes' stores (and, in a
+// partial tile, the lanes past the data) fall out of range and are dropped.
+// Narrow path: 8-byte and 1-byte lane stores straight from registers.
+template <bool kWide>
+__device__ __forceinline__ void store_tile_outputs(uint8_t* lds_bytes, uint2 q, uint32_t sf,
+                                                   const Tile& t, int b, int lane,
+                                                   const Geometry& geo, uint8_t* packed,
+                                                   uint8_t* scales)
+{
+    const int64_t tb = (int64_t)t.row * geo.bpr + t.blk0;   // first block of the tile
+    if constexpr (!kWide) {
+        *reinterpret_cast<uint2*>(packed + (tb + b) * 8) = q;
+        scales[tb + b] = (uint8_t)sf;
+    } else {
+        wave_lds_sync();
+        reinterpret_cast<u32x2*>(lds_bytes)[b] = u32x2{q.x, q.y};
+        lds_bytes[kTileBlocks * 8 + b] = (uint8_t)sf;
+        wave_lds_sync();
+        const u32x4 d = reinterpret_cast<const u32x4*>(lds_bytes)[lane];
+        const bool scale_lane = lane >= kWave / 2;
+        const int off = (lane & (kWave / 2 - 1)) * 16;
+        __builtin_amdgcn_raw_buffer_store_b128(d, buffer_over(packed + tb * 8, t.nblk * 8),
+                                               scale_lane ? kOffRange : off, 0, kOutStorePolicy);
+        __builtin_amdgcn_raw_buffer_store_b128(d, buffer_over(scales + tb, t.nblk),
+                                               scale_lane ? off : kOffRange, 0, kOutStorePolicy);
+    }
+}
+
+// Block values from its staged words.
+struct FusedBlock {
+    static constexpr int P = 4;
+    // y = silu(gate) * up for the 16 outputs of the block.
+    __device__ static __forceinline__ void values(const u32x4 (&c)[4], float (&y)[16])
+    {
+        const uint32_t gw[8] = {c[0].x, c[0].y, c[0].z, c[0].w, c[2].x, c[2].y, c[2].z, c[2].w};
+        const uint32_t uw[8] = {c[1].x, c[1].y, c[1].z, c[1].w, c[3].x, c[3].y, c[3].z, c[3].w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            y[2 * i] = nvfp4::swiglu_bf16(nvfp4::bf16_lo(gw[i]), nvfp4::bf16_lo(uw[i]));
+            y[2 * i + 1] = nvfp4::swiglu_bf16(nvfp4::bf16_hi(gw[i]), nvfp4::bf16_hi(uw[i]));
+        }
+    }
+};
+
+struct PlainBlock {
+    static constexpr int P = 2;
+    __device__ static __forceinline__ void values(const u32x4 (&c)[2], float (&y)[16])
+    {
+        const uint32_t w[8] = {c[0].x, c[0].y, c[0].z, c[0].w, c[1].x, c[1].y, c[1].z, c[1].w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            y[2 * i] = nvfp4::bf16_lo(w[i]);
+            y[2 * i + 1] = nvfp4::bf16_hi(w[i]);
+        }
+    }
+};
+
+template <class Block, bool kWide>
+__global__ __launch_bounds__(kThreads) void quantize_tiles_kernel(
     const uint16_t* __restrict__ in, int64_t ld_in, Geometry geo,
     const float* __restrict__ gs, const int32_t* __restrict__ offsets, int num_experts,
     uint8_t* __restrict__ packed, uint8_t* __restrict__ scales,
-    float* __restrict__ swiglu_out)
+    float* __restrict__ values_out)
 {
+    constexpr int P = Block::P;
+    __shared__ u32x4 stage[kWavesPerBlock][kStageSlots(P)];
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = uniform(threadIdx.x / kWave);
-    const int inter = geo.bpr * 16;
-    for (int tile = blockIdx.x * kWavesPerBlock + wave; tile < geo.tiles;
-         tile += gridDim.x * kWavesPerBlock) {
-        const int row = uniform(tile / geo.cpr);
-        const int chunk = tile - row * geo.cpr;
-        const int blk = chunk * kTileBlocks + lane;
-        if (blk >= geo.bpr)
-            continue;
-        const u32x4* src = reinterpret_cast<const u32x4*>(in + (int64_t)row * ld_in + (int64_t)blk * 32);
-        const u32x4 c0 = ld_stream(src + 0);
-        const u32x4 c1 = ld_stream(src + 1);
-        const u32x4 c2 = ld_stream(src + 2);
-        const u32x4 c3 = ld_stream(src + 3);
-        const float g_s = nvfp4::row_global_scale(gs, offsets, num_experts, row);
-        const float k = 6.0f * g_s;
-
-        const uint32_t gw[8] = {c0.x, c0.y, c0.z, c0.w, c2.x, c2.y, c2.z, c2.w};
-        const uint32_t uw[8] = {c1.x, c1.y, c1.z, c1.w, c3.x, c3.y, c3.z, c3.w};
-        float y[16];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            y[2 * i] = nvfp4::swiglu(nvfp4::bf16_lo(gw[i]), nvfp4::bf16_lo(uw[i]));
-            y[2 * i + 1] = nvfp4::swiglu(nvfp4::bf16_hi(gw[i]), nvfp4::bf16_hi(uw[i]));
+    u32x4* lds = stage[wave];
+    const int cols = geo.bpr * 16;
+    const int stride = gridDim.x * kWavesPerBlock;
+    int tile = blockIdx.x * kWavesPerBlock + wave;
+    if (tile >= geo.tiles)
+        return;
+    Tile t = tile_at(tile, geo);
+    u32x4 v[P];
+    load_tile<P>(v, in, ld_in, t, lane);
+    // Without experts the global scale (and its reciprocal) is the same for
+    // every row: computed once here instead of per tile.
+    nvfp4::RowScale rs = nvfp4::row_scale(gs != nullptr ? gs[0] : 1.0f);
+    stage_tile<P>(lds, v, lane);
+    // Loop invariant: tile t is staged in LDS and no loads are in flight.
+    // Each pass issues the loads of the next tile first, computes and stores
+    // tile t, then stages the next tile; the only memory operations younger
+    // than those loads are this tile's stores, so the wait before staging
+    // does not wait for the stores.
+    for (;;) {
+        const int next = tile + stride;
+        const bool has_next = next < geo.tiles;
+        Tile tn = t;
+        if (has_next) {
+            tn = tile_at(next, geo);
+            load_tile<P>(v, in, ld_in, tn, lane);
         }
+        if (offsets != nullptr)
+            rs = nvfp4::row_scale(nvfp4::row_global_scale(gs, offsets, num_experts, t.row));
+        wave_lds_sync();
+        // In a partial tile the lanes past its end redo the tile's last block
+        // and store the same bytes to the same place: no lane is masked, so
+        // there is no branch around the stores (a branch would make the wait
+        // before the next staging also wait for these stores).
+        const int b = min(lane, t.nblk - 1);
+        u32x4 c[P];
+#pragma unroll
+        for (int k = 0; k < P; ++k)
+            c[k] = lds[lds_slot(b * P + k)];
+        float y[16];
+        Block::values(c, y);
         uint32_t sf;
-        const uint2 q = nvfp4::quantize16(y, g_s, k, sf);
-        const int64_t ob = (int64_t)row * geo.bpr + blk;
-        *reinterpret_cast<uint2*>(packed + ob * 8) = q;
-        scales[ob] = (uint8_t)sf;
-        if (swiglu_out != nullptr) {
-            float4* dst = reinterpret_cast<float4*>(swiglu_out + (int64_t)row * inter + (int64_t)blk * 16);
+        const uint2 q = nvfp4::quantize16(y, rs, sf);
+        store_tile_outputs<kWide>(reinterpret_cast<uint8_t*>(lds), q, sf, t, b, lane, geo,
+                                  packed, scales);
+        if (values_out != nullptr) {
+            f32x4* dst = reinterpret_cast<f32x4*>(values_out + (int64_t)t.row * cols) +
+                         (t.blk0 + b) * 4;
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                dst[i] = make_float4(y[4 * i], y[4 * i + 1], y[4 * i + 2], y[4 * i + 3]);
+                dst[i] = f32x4{y[4 * i], y[4 * i + 1], y[4 * i + 2], y[4 * i + 3]};
         }
+        if (!has_next)
+            break;
+        wave_lds_sync();
+        stage_tile<P>(lds, v, lane);
+        tile = next;
+        t = tn;
     }
 }
 
 // ---------------------------------------------------------------------------
-// Standalone NVFP4 quantize of BF16. Lane input: 32 contiguous bytes.
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kThreads) void nvfp4_quantize_kernel(
-    const uint16_t* __restrict__ x, int64_t ld_x, Geometry geo,
-    const float* __restrict__ gs, const int32_t* __restrict__ offsets, int num_experts,
-    uint8_t* __restrict__ packed, uint8_t* __restrict__ scales)
-{
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wave = uniform(threadIdx.x / kWave);
-    for (int tile = blockIdx.x * kWavesPerBlock + wave; tile < geo.tiles;
-         tile += gridDim.x * kWavesPerBlock) {
-        const int row = uniform(tile / geo.cpr);
-        const int chunk = tile - row * geo.cpr;
-        const int blk = chunk * kTileBlocks + lane;
-        if (blk >= geo.bpr)
-            continue;
-        const u32x4* src = reinterpret_cast<const u32x4*>(x + (int64_t)row * ld_x + (int64_t)blk * 16);
-        const u32x4 a = ld_stream(src + 0);
-        const u32x4 b = ld_stream(src + 1);
-        const float g_s = nvfp4::row_global_scale(gs, offsets, num_experts, row);
-        const float k = 6.0f * g_s;
-        const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-        float v[16];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            v[2 * i] = nvfp4::bf16_lo(w[i]);
-            v[2 * i + 1] = nvfp4::bf16_hi(w[i]);
-        }
-        uint32_t sf;
-        const uint2 q = nvfp4::quantize16(v, g_s, k, sf);
-        const int64_t ob = (int64_t)row * geo.bpr + blk;
-        *reinterpret_cast<uint2*>(packed + ob * 8) = q;
-        scales[ob] = (uint8_t)sf;
-    }
-}
-
-// ---------------------------------------------------------------------------
-// NVFP4 dequantize to FP32. Lane output: 64 contiguous bytes.
+// NVFP4 dequantize to FP32. A block's output is 4 words (64 bytes); each lane
+// computes its block, the wave transposes the tile through LDS and writes it
+// with coalesced stores.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads) void nvfp4_dequantize_kernel(
     const uint8_t* __restrict__ packed, const uint8_t* __restrict__ scales, Geometry geo,
     const float* __restrict__ gs, const int32_t* __restrict__ offsets, int num_experts,
     float* __restrict__ out)
 {
+    constexpr int P = 4;
+    __shared__ f32x4 stage[kWavesPerBlock][kStageSlots(P)];
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = uniform(threadIdx.x / kWave);
+    f32x4* lds = stage[wave];
     const int cols = geo.bpr * 16;
     for (int tile = blockIdx.x * kWavesPerBlock + wave; tile < geo.tiles;
          tile += gridDim.x * kWavesPerBlock) {
-        const int row = uniform(tile / geo.cpr);
-        const int chunk = tile - row * geo.cpr;
-        const int blk = chunk * kTileBlocks + lane;
-        if (blk >= geo.bpr)
-            continue;
-        const int64_t ib = (int64_t)row * geo.bpr + blk;
-        const u32x2 pv = ld_stream(reinterpret_cast<const u32x2*>(packed) + ib);
-        const uint2 p = make_uint2(pv.x, pv.y);
-        const uint32_t sf = __builtin_nontemporal_load(scales + ib);
-        const float g_s = nvfp4::row_global_scale(gs, offsets, num_experts, row);
-        float v[16];
-        nvfp4::dequantize16(p, sf, g_s, v);
-        f32x4* dst = reinterpret_cast<f32x4*>(out + (int64_t)row * cols + (int64_t)blk * 16);
+        const Tile t = tile_at(tile, geo);
+        const int nwords = t.nblk * P;
+        const float g_s = nvfp4::row_global_scale(gs, offsets, num_experts, t.row);
+        const int64_t ib = (int64_t)t.row * geo.bpr + t.blk0 + lane;
+        wave_lds_sync();
+        if (lane < t.nblk) {
+            const u32x2 pv = ld_stream(reinterpret_cast<const u32x2*>(packed) + ib);
+            const uint32_t sf = __builtin_nontemporal_load(scales + ib);
+            float v[16];
+            nvfp4::dequantize16(make_uint2(pv.x, pv.y), sf, g_s, v);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            st_stream(f32x4{v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]}, dst + i);
+            for (int k = 0; k < P; ++k)
+                lds[lds_slot(lane * P + k)] = f32x4{v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]};
+        }
+        wave_lds_sync();
+        f32x4* dst = reinterpret_cast<f32x4*>(out + (int64_t)t.row * cols) + t.blk0 * P;
+#pragma unroll
+        for (int j = 0; j < P; ++j)
+            if (j * kWave + lane < nwords)
+                st_stream(lds[lds_slot(j * kWave + lane)], dst + j * kWave + lane);
     }
 }
 
@@ -201,6 +335,39 @@ dim3 grid_for(const Geometry& g)
     return dim3((unsigned)(want < cap ? want : cap));
 }
 
+// Persistent grid for the pipelined quantize kernels: enough workgroups to
+// fill MI355X (256 CUs) at the occupancy the kernels' registers allow, never
+// more than the tiles need.
+constexpr int kMi355xCUs = 256;
+constexpr int kQuantBlocksPerCU = 6;
+dim3 persistent_grid_for(const Geometry& g)
+{
+    const int64_t want = ((int64_t)g.tiles + kWavesPerBlock - 1) / kWavesPerBlock;
+    const int64_t cap = (int64_t)kMi355xCUs * kQuantBlocksPerCU;
+    return dim3((unsigned)(want < cap ? want : cap));
+}
+
+// The 16-byte store path needs every tile's output to start 16-byte aligned.
+bool wide_stores(const Geometry& g, const uint8_t* packed, const uint8_t* scales)
+{
+    return g.bpr % 16 == 0 && aligned(packed, 16) && aligned(scales, 16);
+}
+
+template <class Block>
+void launch_quantize(const Geometry& g, const uint16_t* in, int64_t ld, const float* gs,
+                     const int32_t* offsets, int32_t num_experts, uint8_t* packed,
+                     uint8_t* scales, float* values_out, hipStream_t stream)
+{
+    if (wide_stores(g, packed, scales))
+        hipLaunchKernelGGL((quantize_tiles_kernel<Block, true>), persistent_grid_for(g),
+                           dim3(kThreads), 0, stream, in, ld, g, gs, offsets, (int)num_experts,
+                           packed, scales, values_out);
+    else
+        hipLaunchKernelGGL((quantize_tiles_kernel<Block, false>), persistent_grid_for(g),
+                           dim3(kThreads), 0, stream, in, ld, g, gs, offsets, (int)num_experts,
+                           packed, scales, values_out);
+}
+
 nvfp4_status_t launched()
 {
     return hipGetLastError() == hipSuccess ? NVFP4_SUCCESS : NVFP4_ERROR_LAUNCH;
@@ -231,8 +398,8 @@ nvfp4_status_t nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, int
     Geometry g;
     if ((st = make_geometry(rows, cols, g)) != NVFP4_SUCCESS)
         return st;
-    hipLaunchKernelGGL(nvfp4_quantize_kernel, grid_for(g), dim3(kThreads), 0, stream,
-                       x, ld_x, g, gs, expert_offsets, (int)num_experts, packed, scales);
+    launch_quantize<PlainBlock>(g, x, ld_x, gs, expert_offsets, num_experts, packed, scales,
+                                nullptr, stream);
     return launched();
 }
 
@@ -259,9 +426,8 @@ nvfp4_status_t swiglu_nvfp4_quantize(const uint16_t* gate_up, int64_t rows, int6
     Geometry g;
     if ((st = make_geometry(rows, inter, g)) != NVFP4_SUCCESS)
         return st;
-    hipLaunchKernelGGL(swiglu_nvfp4_kernel, grid_for(g), dim3(kThreads), 0, stream,
-                       gate_up, ld_in, g, gs, expert_offsets, (int)num_experts, packed, scales,
-                       swiglu_out);
+    launch_quantize<FusedBlock>(g, gate_up, ld_in, gs, expert_offsets, num_experts, packed,
+                                scales, swiglu_out, stream);
     return launched();
 }
 

@@ -20,25 +20,23 @@ __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w 
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
 // ---- SwiGLU: silu(g) * u = g * u / (1 + e^-g) in FP32 ----------------------
-// e^-g = 2^(-g log2 e). The product -g * log2(e) is carried as hi + lo (lo is
-// the exact rounding error of hi plus the tail of log2 e), so that the
-// exponential keeps ~1 ulp relative accuracy for |g| up to 88; v_exp_f32 of
-// hi is then corrected by the factor (1 + lo ln 2). Error budget: v_exp_f32
-// 1 ulp, v_rcp_f32 1 ulp, four roundings: < 5 ulp, about 6e-7 relative.
-// g < -88.7 overflows e to +inf and gives y = +-0 (true |y| < 1e-36).
-__device__ __forceinline__ float swiglu(float g, float u)
+// e^-g = 2^(-g log2 e). log2 e is split as kLog2eHi + kLog2eLo with kLog2eHi
+// holding 16 significant bits, so for a BF16 gate (8 significant bits) the
+// product p = -g * kLog2eHi is EXACT in FP32; 2^p comes from v_exp_f32 and
+// the tail 2^(-g kLog2eLo) = 1 + (-g kLog2eLo ln 2) is folded into the
+// denominator with one fma: den = 2^p * (1 + c) + 1. |c| < 4.3e-4 for
+// |g| < 89, so the neglected c^2/2 is < 1e-7. Error budget: v_exp_f32 and
+// v_rcp_f32 about 1 ulp each plus four roundings: ~5 ulp (6e-7 relative).
+// g < -88.7 overflows 2^p to +inf and gives y = +-0 (true |y| < 1e-36).
+// The gate must be a BF16 value (exactness of p).
+__device__ __forceinline__ float swiglu_bf16(float g, float u)
 {
-    const float kLog2e = 0x1.715476p+0f;     // RN(log2 e)
-    const float kLog2eLo = 0x1.4ae0c0p-26f;  // log2 e - kLog2e
-    const float kLn2 = 0x1.62e430p-1f;       // RN(ln 2)
-    const float t = -g;
-    const float hi = t * kLog2e;
-    float lo = __builtin_fmaf(t, kLog2e, -hi);
-    lo = __builtin_fmaf(t, kLog2eLo, lo);
-    float e = __builtin_amdgcn_exp2f(hi);
-    e = e * __builtin_fmaf(lo, kLn2, 1.0f);
-    const float sig = __builtin_amdgcn_rcpf(1.0f + e);
-    return (g * u) * sig;
+    const float kLog2eHi = 0x1.7154p+0f;          // log2 e to 16 bits
+    const float kLog2eLoLn2 = 0x1.480fb6p-18f;    // (log2 e - kLog2eHi) ln 2
+    const float e = __builtin_amdgcn_exp2f(-g * kLog2eHi);
+    const float c = __builtin_fmaf(-g, kLog2eLoLn2, 1.0f);
+    const float den = __builtin_fmaf(e, c, 1.0f);
+    return (g * u) * __builtin_amdgcn_rcpf(den);
 }
 
 // ---- FP8 E4M3 ("fn") encode of a non-negative block scale -------------------
@@ -75,63 +73,86 @@ struct BlockScale {
     float rcp;     // RN(1 / half_d) = RN(2 / d); 0 when d == 0
 };
 
+// Per-row constants: k = RN(6 gs) and rk = RN(1 / k) (IEEE division).
+struct RowScale {
+    float gs, k, rk;
+};
+
+__device__ __forceinline__ RowScale row_scale(float gs)
+{
+    RowScale r;
+    r.gs = gs;
+    r.k = 6.0f * gs;
+    r.rk = 1.0f / r.k;
+    return r;
+}
+
+// Correctly rounded quotient a / b from rb = RN(1 / b): q0 = RN(a rb), then
+// one Newton/Markstein correction with the exact remainder. The remainder is
+// formed as q0 b - a and applied with -rb, which keeps the IEEE sign of a in
+// the result also when a is -0 or the quotient underflows. Checked
+// exhaustively on the CPU for every binary32 numerator mantissa against the
+// 8 E4M3 mantissas as divisors (the power-of-two global-scale case); in
+// general it is Markstein's theorem (rb within half an ulp of 1/b, q0
+// faithful, exact remainder).
+__device__ __forceinline__ float div_rn(float a, float b, float rb)
+{
+    const float q0 = a * rb;
+    const float rem = __builtin_fmaf(q0, b, -a);
+    return __builtin_fmaf(rem, -rb, q0);
+}
+
 // amax -> scale byte and element-quantizer constants.
-//   bsf = RN(amax / k) with k = RN(6 gs) (IEEE division), sf = E4M3(bsf),
-//   d = RN(decode(sf) * gs).
-__device__ __forceinline__ BlockScale block_scale(float amax, float gs, float k)
+//   bsf = RN(amax / k), sf = E4M3(bsf), d = RN(decode(sf) * gs).
+__device__ __forceinline__ BlockScale block_scale(float amax, const RowScale& rs)
 {
     BlockScale s;
-    const float bsf = amax / k;
+    const float bsf = div_rn(amax, rs.k, rs.rk);
     s.sf = fp8_e4m3_encode(bsf);
-    const float d = fp8_e4m3_decode(s.sf) * gs;
+    const float d = fp8_e4m3_decode(s.sf) * rs.gs;
     s.half_d = 0.5f * d;
     const float r = 1.0f / s.half_d;          // IEEE division, correctly rounded
     s.rcp = d != 0.0f ? r : 0.0f;
     return s;
 }
 
-// One element -> signed half-step value h = +-rint(2 min(|s|,6)) / 2, ready
-// for the E2M1 convert. s2 = RN(2x / d) = 2 RN(x / d) is formed without a
-// division: q0 = RN(x * RN(2/d)), then one Newton/Markstein correction with
-// the exact remainder x - q0 (d/2) gives the correctly rounded quotient
-// (checked exhaustively on the CPU for every FP8 scale mantissa and every
-// binary32 numerator mantissa; beyond that it is Markstein's theorem).
-// When d == 0 the magnitude is 0 (rcp == 0 makes q0, q1 zero).
-__device__ __forceinline__ float half_step(float x, const BlockScale& s)
+// One element -> signed half-step count +-rint(2|s|), s = RN(x / d), ties to
+// even. 2s = RN(2x / d) = RN(x / (d/2)) exactly (power-of-two scaling); rint
+// keeps the IEEE sign of x, including -0 and values that round to 0. When
+// d == 0, rcp == 0 gives +-0. The clamp 2 min(|s|, 6) of the method is left
+// to the E2M1 convert, which saturates: any count >= 12 (|s| >= 6) gives the
+// largest magnitude, exactly as the clamped count 12 does.
+__device__ __forceinline__ float half_steps(float x, const BlockScale& s)
 {
-    const float q0 = x * s.rcp;
-    const float rem = __builtin_fmaf(-q0, s.half_d, x);
-    const float q1 = __builtin_fmaf(rem, s.rcp, q0);
-    const float v = fminf(__builtin_fabsf(q1), 12.0f);   // 2 min(|s|, 6)
-    const float h = __builtin_rintf(v) * 0.5f;            // ties to even
-    // sign = IEEE sign bit of x (also for -0 and values rounding to 0)
-    return __uint_as_float(__float_as_uint(h) | (__float_as_uint(x) & 0x80000000u));
+    return __builtin_rintf(div_rn(x, s.half_d, s.rcp));
 }
 
-// Two signed half-step values -> one byte of E2M1 codes (first value in the
-// low nibble) placed at byte `sel` of `word`. The half-step grid {0, .5, 1,
-// ..., 6} maps onto E2M1 by round-to-nearest-even, which is exactly the
-// step_to_idx table (2.5 -> 2, 3.5 -> 4, 4.5 -> 4, 5 -> 4, 5.5 -> 6); scale 1.
+// Two signed half-step counts -> one byte of E2M1 codes (first value in the
+// low nibble) placed at byte `sel` of `word`. The convert divides by its
+// power-of-two scale (2 here, exact) and rounds to nearest even onto E2M1,
+// saturating at 6: on the half-step grid {0, .5, ..., 6} that is exactly the
+// step_to_idx table (2.5 -> 2, 3.5 -> 4, 4.5 -> 4, 5 -> 4, 5.5 -> 6), and
+// every value above 6 gives 6; the sign (also of -0) becomes bit 3.
 template <int sel>
 __device__ __forceinline__ uint32_t pack_e2m1(uint32_t word, float h0, float h1)
 {
-    return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, h0, h1, 1.0f, sel);
+    return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, h0, h1, 2.0f, sel);
 }
 
 // 16 FP32 values -> 8 bytes of packed E2M1 codes (returned as uint2) and the
 // scale byte.
-__device__ __forceinline__ uint2 quantize16(const float (&y)[16], float gs, float k,
+__device__ __forceinline__ uint2 quantize16(const float (&y)[16], const RowScale& rs,
                                             uint32_t& sf_out)
 {
     float amax = 0.0f;
 #pragma unroll
     for (int j = 0; j < 16; ++j)
         amax = fmaxf(amax, __builtin_fabsf(y[j]));
-    const BlockScale s = block_scale(amax, gs, k);
+    const BlockScale s = block_scale(amax, rs);
     float h[16];
 #pragma unroll
     for (int j = 0; j < 16; ++j)
-        h[j] = half_step(y[j], s);
+        h[j] = half_steps(y[j], s);
     uint32_t w0 = 0, w1 = 0;
     w0 = pack_e2m1<0>(w0, h[0], h[1]);
     w0 = pack_e2m1<1>(w0, h[2], h[3]);

@@ -31,8 +31,20 @@ def _one(dir_, suffix):
 
 
 def _short(name):
-    base = name.split("(")[0]
-    return base.split("::")[-1].strip() or name
+    """'void (anonymous namespace)::k<(anonymous namespace)::A, true>(args)' ->
+    'k<A, true>'."""
+    n = name.replace("(anonymous namespace)::", "")
+    depth, cut = 0, len(n)
+    for i, ch in enumerate(n):
+        if ch == "<":
+            depth += 1
+        elif ch == ">":
+            depth -= 1
+        elif ch == "(" and depth == 0:
+            cut = i
+            break
+    n = n[:cut].strip()
+    return n[5:] if n.startswith("void ") else n
 
 
 def stats(args):
