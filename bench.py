@@ -30,7 +30,7 @@ PEAK_HBM_GBS = 8000.0               # MI355X HBM3E peak, 8 TB/s
 ROWS, INTER = 65536, 3072
 BYTES_PER_ELEM = 4.5625             # 4 B read (gate+up BF16) + 0.5 B codes + 1/16 B scale
 ALG_BYTES = int(ROWS * INTER * BYTES_PER_ELEM)      # 918,552,576
-PMC_SUMMARY = os.path.join(ROOT, "profiles", "swiglu_nvfp4_kernel_prefill_pmc.json")
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "fused_quantize_kernel_prefill_pmc.json")
 CALIB_BLOCKS = 49152      # one 4 KB tile per wave over the 805 MB input
 
 
@@ -74,23 +74,24 @@ def checked(rc):
 
 
 def time_launches(fn, steps, warmup):
-    """Warm up, then time `steps` launches: wall clock between two device
-    synchronizations, and per-launch HIP events on the launch stream."""
+    """Warm up, then time `steps` back-to-back launches. Returns (wall seconds
+    between two device synchronizations, device milliseconds per launch from
+    one pair of HIP events recorded on the launch stream around the whole
+    timed region)."""
     import torch
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
-    for i in range(steps):
-        starts[i].record()
+    start.record()
+    for _ in range(steps):
         fn()
-        ends[i].record()
+    end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    per = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    return wall, per
+    return wall, start.elapsed_time(end) / steps
 
 
 def cpu_baseline(x):
@@ -156,10 +157,9 @@ def main():
         M.swiglu_nvfp4_quantize(x, packed=packed, scales=scales)
 
     print("[bench] timing %d steps after %d warmup" % (args.steps, args.warmup), file=sys.stderr, flush=True)
-    wall, per = time_launches(step, args.steps, args.warmup)
+    wall, kern_ms = time_launches(step, args.steps, args.warmup)
     ms_per_step = wall * 1e3 / args.steps
     value = ALG_BYTES / (wall / args.steps) / 1e9
-    kern_ms = statistics.mean(per)
     achieved = ALG_BYTES / (kern_ms / 1e3) / 1e9
 
     secondary = None
@@ -171,15 +171,13 @@ def main():
         xq = x.view(torch.int16)[:, :INTER].contiguous().view(torch.bfloat16)
         pq = torch.empty_like(packed)
         sq = torch.empty_like(scales)
-        _, perq = time_launches(lambda: M.nvfp4_quantize(xq, packed=pq, scales=sq), sec_steps, 3)
-        mq = statistics.mean(perq)
+        _, mq = time_launches(lambda: M.nvfp4_quantize(xq, packed=pq, scales=sq), sec_steps, 3)
         secondary["nvfp4_quantize"] = {
             "shape": [ROWS, INTER], "bytes_per_launch": int(ROWS * INTER * 2.5625),
             "ms": round(mq, 4), "GB_s": round(ROWS * INTER * 2.5625 / mq / 1e6, 1)}
         del xq, pq, sq
         out = torch.empty((ROWS, INTER), dtype=torch.float32, device=dev)
-        _, perd = time_launches(lambda: M.nvfp4_dequantize(packed, scales, out=out), sec_steps, 3)
-        md = statistics.mean(perd)
+        _, md = time_launches(lambda: M.nvfp4_dequantize(packed, scales, out=out), sec_steps, 3)
         secondary["nvfp4_dequantize"] = {
             "shape": [ROWS, INTER], "bytes_per_launch": int(ROWS * INTER * 4.5625),
             "ms": round(md, 4), "GB_s": round(ROWS * INTER * 4.5625 / md / 1e6, 1)}
@@ -189,13 +187,11 @@ def main():
         nbytes = x.numel() * 2
         scratch = torch.empty(CALIB_BLOCKS * 16, dtype=torch.uint8, device=dev)
         stream = torch.cuda.current_stream().cuda_stream
-        _, perr = time_launches(lambda: checked(calib.nvfp4_calib_read(
+        _, mr = time_launches(lambda: checked(calib.nvfp4_calib_read(
             x.data_ptr(), scratch.data_ptr(), nbytes, CALIB_BLOCKS, stream)), sec_steps, 3)
-        mr = statistics.mean(perr)
         dst = torch.empty_like(x)
-        _, perc = time_launches(lambda: checked(calib.nvfp4_calib_copy(
+        _, mc = time_launches(lambda: checked(calib.nvfp4_calib_copy(
             x.data_ptr(), dst.data_ptr(), nbytes, CALIB_BLOCKS, stream)), sec_steps, 3)
-        mc = statistics.mean(perc)
         del dst, scratch
         read_gbs = nbytes / mr / 1e6
         copy_gbs = 2 * nbytes / mc / 1e6
@@ -205,8 +201,6 @@ def main():
                                            "GB_s": round(copy_gbs, 1)}
         secondary["fused_frac_of_read_ceiling"] = round(achieved / read_gbs, 4)
         secondary["fused_frac_of_copy_ceiling"] = round(achieved / copy_gbs, 4)
-        secondary["fused_kernel_ms_p10_p50_p90"] = [
-            round(float(np.percentile(per, q)), 4) for q in (10, 50, 90)]
 
     cpu = None
     if not args.no_cpu_baseline:
