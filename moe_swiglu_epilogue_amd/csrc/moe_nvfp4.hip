@@ -155,25 +155,36 @@ __device__ __forceinline__ void store_tile_outputs(uint8_t* lds_bytes, uint2 q, 
     }
 }
 
-// Block values from its staged words.
+// Block values from its staged words. kWaves is the workgroup size in waves
+// and kBlocksPerCU the persistent grid's workgroups per CU (what LDS allows).
 struct FusedBlock {
     static constexpr int P = 4;
-    // y = silu(gate) * up for the 16 outputs of the block.
-    __device__ static __forceinline__ void values(const u32x4 (&c)[4], float (&y)[16])
+    static constexpr int kWaves = 8;
+    static constexpr int kBlocksPerCU = 2;   // 32 KB sigma table + 8 x 4.25 KB staging
+    static constexpr bool kSigmaTable = true;
+    // y = silu(gate) * up = (gate * up) * sigma(gate) for the 16 outputs.
+    __device__ static __forceinline__ void values(const u32x4 (&c)[4], float (&y)[16],
+                                                  const uint8_t* sig)
     {
         const uint32_t gw[8] = {c[0].x, c[0].y, c[0].z, c[0].w, c[2].x, c[2].y, c[2].z, c[2].w};
         const uint32_t uw[8] = {c[1].x, c[1].y, c[1].z, c[1].w, c[3].x, c[3].y, c[3].z, c[3].w};
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            y[2 * i] = nvfp4::swiglu_bf16(nvfp4::bf16_lo(gw[i]), nvfp4::bf16_lo(uw[i]));
-            y[2 * i + 1] = nvfp4::swiglu_bf16(nvfp4::bf16_hi(gw[i]), nvfp4::bf16_hi(uw[i]));
+            const float s0 = *reinterpret_cast<const float*>(sig + nvfp4::sigma_offset<0>(gw[i]));
+            const float s1 = *reinterpret_cast<const float*>(sig + nvfp4::sigma_offset<16>(gw[i]));
+            y[2 * i] = (nvfp4::bf16_lo(gw[i]) * nvfp4::bf16_lo(uw[i])) * s0;
+            y[2 * i + 1] = (nvfp4::bf16_hi(gw[i]) * nvfp4::bf16_hi(uw[i])) * s1;
         }
     }
 };
 
 struct PlainBlock {
     static constexpr int P = 2;
-    __device__ static __forceinline__ void values(const u32x4 (&c)[2], float (&y)[16])
+    static constexpr int kWaves = 4;
+    static constexpr int kBlocksPerCU = 6;
+    static constexpr bool kSigmaTable = false;
+    __device__ static __forceinline__ void values(const u32x4 (&c)[2], float (&y)[16],
+                                                  const uint8_t*)
     {
         const uint32_t w[8] = {c[0].x, c[0].y, c[0].z, c[0].w, c[1].x, c[1].y, c[1].z, c[1].w};
 #pragma unroll
@@ -185,20 +196,29 @@ struct PlainBlock {
 };
 
 template <class Block, bool kWide>
-__global__ __launch_bounds__(kThreads) void quantize_tiles_kernel(
+__global__ __launch_bounds__(Block::kWaves * kWave) void quantize_tiles_kernel(
     const uint16_t* __restrict__ in, int64_t ld_in, Geometry geo,
     const float* __restrict__ gs, const int32_t* __restrict__ offsets, int num_experts,
     uint8_t* __restrict__ packed, uint8_t* __restrict__ scales,
     float* __restrict__ values_out)
 {
     constexpr int P = Block::P;
-    __shared__ u32x4 stage[kWavesPerBlock][kStageSlots(P)];
+    constexpr int kWaves = Block::kWaves;
+    __shared__ u32x4 stage[kWaves][kStageSlots(P)];
+    __shared__ float sig[Block::kSigmaTable ? nvfp4::kSigEntries : 1];
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = uniform(threadIdx.x / kWave);
     u32x4* lds = stage[wave];
     const int cols = geo.bpr * 16;
-    const int stride = gridDim.x * kWavesPerBlock;
-    int tile = blockIdx.x * kWavesPerBlock + wave;
+    const int stride = gridDim.x * kWaves;
+    int tile = blockIdx.x * kWaves + wave;
+    if constexpr (Block::kSigmaTable) {
+        // Every wave of the workgroup helps fill the table, so the barrier
+        // below is reached by all of them (including waves without a tile).
+        for (int i = threadIdx.x; i < nvfp4::kSigEntries; i += kWaves * kWave)
+            sig[i] = nvfp4::sigma_entry(i);
+        __syncthreads();
+    }
     if (tile >= geo.tiles)
         return;
     Tile t = tile_at(tile, geo);
@@ -234,7 +254,7 @@ __global__ __launch_bounds__(kThreads) void quantize_tiles_kernel(
         for (int k = 0; k < P; ++k)
             c[k] = lds[lds_slot(b * P + k)];
         float y[16];
-        Block::values(c, y);
+        Block::values(c, y, reinterpret_cast<const uint8_t*>(sig));
         uint32_t sf;
         const uint2 q = nvfp4::quantize16(y, rs, sf);
         store_tile_outputs<kWide>(reinterpret_cast<uint8_t*>(lds), q, sf, t, b, lane, geo,
@@ -336,14 +356,14 @@ dim3 grid_for(const Geometry& g)
 }
 
 // Persistent grid for the pipelined quantize kernels: enough workgroups to
-// fill MI355X (256 CUs) at the occupancy the kernels' registers allow, never
-// more than the tiles need.
+// fill MI355X (256 CUs) at the occupancy the kernel's LDS and registers
+// allow, never more than the tiles need.
 constexpr int kMi355xCUs = 256;
-constexpr int kQuantBlocksPerCU = 6;
+template <class Block>
 dim3 persistent_grid_for(const Geometry& g)
 {
-    const int64_t want = ((int64_t)g.tiles + kWavesPerBlock - 1) / kWavesPerBlock;
-    const int64_t cap = (int64_t)kMi355xCUs * kQuantBlocksPerCU;
+    const int64_t want = ((int64_t)g.tiles + Block::kWaves - 1) / Block::kWaves;
+    const int64_t cap = (int64_t)kMi355xCUs * Block::kBlocksPerCU;
     return dim3((unsigned)(want < cap ? want : cap));
 }
 
@@ -358,14 +378,14 @@ void launch_quantize(const Geometry& g, const uint16_t* in, int64_t ld, const fl
                      const int32_t* offsets, int32_t num_experts, uint8_t* packed,
                      uint8_t* scales, float* values_out, hipStream_t stream)
 {
+    const dim3 grid = persistent_grid_for<Block>(g);
+    const dim3 block(Block::kWaves * kWave);
     if (wide_stores(g, packed, scales))
-        hipLaunchKernelGGL((quantize_tiles_kernel<Block, true>), persistent_grid_for(g),
-                           dim3(kThreads), 0, stream, in, ld, g, gs, offsets, (int)num_experts,
-                           packed, scales, values_out);
+        hipLaunchKernelGGL((quantize_tiles_kernel<Block, true>), grid, block, 0, stream, in, ld,
+                           g, gs, offsets, (int)num_experts, packed, scales, values_out);
     else
-        hipLaunchKernelGGL((quantize_tiles_kernel<Block, false>), persistent_grid_for(g),
-                           dim3(kThreads), 0, stream, in, ld, g, gs, offsets, (int)num_experts,
-                           packed, scales, values_out);
+        hipLaunchKernelGGL((quantize_tiles_kernel<Block, false>), grid, block, 0, stream, in, ld,
+                           g, gs, offsets, (int)num_experts, packed, scales, values_out);
 }
 
 nvfp4_status_t launched()

@@ -39,6 +39,44 @@ __device__ __forceinline__ float swiglu_bf16(float g, float u)
     return (g * u) * __builtin_amdgcn_rcpf(den);
 }
 
+// ---- SwiGLU through a table of sigmoid values ------------------------------
+// A BF16 gate has 65536 values; sigma(g) = 1 / (1 + e^-g) only varies in FP32
+// for 2^-24 <= |g| < 256. The table holds sigma for every BF16 magnitude in
+// that range (exponent field 103..134, all 128 mantissas) and both signs:
+// entry 2 (x - kSigLo) + sign, x = the 15 magnitude bits. Magnitudes below
+// the range read the first row (sigma rounds to 1/2 there: |sigma - 1/2| <
+// 2^-26), magnitudes above it the last (sigma is 1, or below the FP32 range
+// for negative g). Entries are computed once per workgroup with
+// sigma_entry(); a lookup then replaces exp and rcp per element.
+constexpr uint32_t kSigLo = 103u << 7;
+constexpr uint32_t kSigHi = (134u << 7) | 127u;
+constexpr int kSigEntries = 2 * (int)(kSigHi - kSigLo + 1);   // 8192 (32 KB)
+
+// sigma(g) for table entry i: the exp2 argument -g * kLog2eHi is exact for a
+// BF16 gate, its tail is folded in by one fma, and the final reciprocal is a
+// correctly rounded division (about 2 ulp overall).
+__device__ __forceinline__ float sigma_entry(int i)
+{
+    const float kLog2eHi = 0x1.7154p+0f;          // log2 e to 16 bits
+    const float kLog2eLoLn2 = 0x1.480fb6p-18f;    // (log2 e - kLog2eHi) ln 2
+    const float a = __uint_as_float((kSigLo + (uint32_t)(i >> 1)) << 16);
+    const float g = (i & 1) ? -a : a;
+    const float e = __builtin_amdgcn_exp2f(-g * kLog2eHi);
+    const float c = __builtin_fmaf(-g, kLog2eLoLn2, 1.0f);
+    return 1.0f / __builtin_fmaf(e, c, 1.0f);
+}
+
+// Byte offset of the table entry for the BF16 gate held in bits [lo, lo+16)
+// of w (lo = 0 or 16).
+template <int lo>
+__device__ __forceinline__ uint32_t sigma_offset(uint32_t w)
+{
+    const uint32_t x = lo == 0 ? (w & 0x7fffu) : ((w >> 16) & 0x7fffu);
+    const uint32_t xc = min(max(x, kSigLo), kSigHi);   // v_med3_u32
+    const uint32_t sign4 = lo == 0 ? ((w >> 13) & 4u) : ((w >> 29) & 4u);
+    return (xc - kSigLo) * 8u + sign4;
+}
+
 // ---- FP8 E4M3 ("fn") encode of a non-negative block scale -------------------
 // Saturates at 448 (exp 15 / mant 6; exp 15 / mant 7 is NaN and never made).
 // v < 2^-6 is subnormal, value m / 512: m = rint(v * 512) (exact product,
@@ -73,9 +111,12 @@ struct BlockScale {
     float rcp;     // RN(1 / half_d) = RN(2 / d); 0 when d == 0
 };
 
-// Per-row constants: k = RN(6 gs) and rk = RN(1 / k) (IEEE division).
+// Per-row constants: k = RN(6 gs), rk = RN(1 / k) (IEEE division), and
+// whether gs is a power of two (then every block divisor d = decode(sf) * gs
+// carries an E4M3 mantissa).
 struct RowScale {
     float gs, k, rk;
+    bool pow2;
 };
 
 __device__ __forceinline__ RowScale row_scale(float gs)
@@ -84,6 +125,7 @@ __device__ __forceinline__ RowScale row_scale(float gs)
     r.gs = gs;
     r.k = 6.0f * gs;
     r.rk = 1.0f / r.k;
+    r.pow2 = (__float_as_uint(gs) & 0x007fffffu) == 0;
     return r;
 }
 
@@ -104,6 +146,12 @@ __device__ __forceinline__ float div_rn(float a, float b, float rb)
 
 // amax -> scale byte and element-quantizer constants.
 //   bsf = RN(amax / k), sf = E4M3(bsf), d = RN(decode(sf) * gs).
+// The element quotients need a reciprocal of d/2 for div_rn. When gs is a
+// power of two, d/2 has one of the 8 E4M3 mantissas, and for those divisors
+// the div_rn correction is exact for every numerator even when the
+// reciprocal is off by one ulp (checked exhaustively on the CPU), so the
+// faithful v_rcp_f32 is enough. Otherwise the reciprocal is the correctly
+// rounded IEEE division. The branch is uniform (gs is per row).
 __device__ __forceinline__ BlockScale block_scale(float amax, const RowScale& rs)
 {
     BlockScale s;
@@ -111,7 +159,11 @@ __device__ __forceinline__ BlockScale block_scale(float amax, const RowScale& rs
     s.sf = fp8_e4m3_encode(bsf);
     const float d = fp8_e4m3_decode(s.sf) * rs.gs;
     s.half_d = 0.5f * d;
-    const float r = 1.0f / s.half_d;          // IEEE division, correctly rounded
+    float r;
+    if (rs.pow2)
+        r = __builtin_amdgcn_rcpf(s.half_d);
+    else
+        r = 1.0f / s.half_d;                  // IEEE division, correctly rounded
     s.rcp = d != 0.0f ? r : 0.0f;
     return s;
 }

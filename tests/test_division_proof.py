@@ -10,6 +10,9 @@ the correctly rounded division a / b:
   quotient depends only on the mantissas and the exponent difference, so this
   covers every element quotient (and every amax / 6 block-scale quotient)
   when the global scale is a power of two;
+* the same exhaustive set with the reciprocal rb moved one ulp down or up
+  (a faithful reciprocal such as v_rcp_f32, used when the global scale is a
+  power of two): the correction still gives the correctly rounded quotient;
 * the sign of zero for +-0 numerators;
 * a large random sample of arbitrary divisor mantissas (general global
   scales), where correctness rests on Markstein's theorem.
@@ -34,20 +37,26 @@ static float div_rn(float a, float b, float rb) {
 }
 int main(int argc, char** argv) {
     long bad = 0, n = 0;
-    /* exhaustive: 8 E4M3 mantissas, all numerator mantissas, 3 exponents */
+    /* exhaustive: 8 E4M3 mantissas, all numerator mantissas, 3 exponents,
+       3 reciprocals */
     for (int m = 0; m < 8; ++m) {
         for (int eb = -1; eb <= 1; ++eb) {
             float b = ldexpf(1.0f + m / 8.0f, eb);
-            float rb = 1.0f / b;
-            #pragma omp parallel for reduction(+:bad,n)
-            for (uint32_t mx = 0; mx < (1u << 23); ++mx)
-                for (uint32_t ex = 126; ex <= 128; ++ex) {
-                    float a = u2f((ex << 23) | mx);
-                    float q = div_rn(a, b, rb), r = a / b;
-                    float qn = div_rn(-a, b, rb), rn = -a / b;
-                    n += 2;
-                    bad += (f2u(q) != f2u(r)) + (f2u(qn) != f2u(rn));
-                }
+            float r0 = 1.0f / b;
+            /* rb = RN(1/b), and its two neighbours (faithful reciprocals) */
+            const float rbs[3] = {r0, nextafterf(r0, 0.0f), nextafterf(r0, INFINITY)};
+            for (int k = 0; k < 3; ++k) {
+                const float rb = rbs[k];
+                #pragma omp parallel for reduction(+:bad,n)
+                for (uint32_t mx = 0; mx < (1u << 23); ++mx)
+                    for (uint32_t ex = 126; ex <= 128; ++ex) {
+                        float a = u2f((ex << 23) | mx);
+                        float q = div_rn(a, b, rb), r = a / b;
+                        float qn = div_rn(-a, b, rb), rn = -a / b;
+                        n += 2;
+                        bad += (f2u(q) != f2u(r)) + (f2u(qn) != f2u(rn));
+                    }
+            }
         }
     }
     /* signed zeros */
@@ -87,6 +96,6 @@ def test_markstein_quotient_matches_ieee_division(tmp_path):
     out = subprocess.run([str(exe), "256"], capture_output=True, text=True, check=True,
                          env={**os.environ, "OMP_NUM_THREADS": str(min(8, os.cpu_count() or 1))})
     n, bad, rn, rbad = map(int, out.stdout.split())
-    assert n == 8 * 3 * (1 << 23) * 3 * 2
+    assert n == 8 * 3 * 3 * (1 << 23) * 3 * 2
     assert bad == 0, "exhaustive E4M3-mantissa check failed in %d cases" % bad
     assert rn > 0 and rbad == 0, "random-divisor check failed in %d of %d cases" % (rbad, rn)
