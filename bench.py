@@ -9,11 +9,17 @@ before timing starts.
 
 Prints ONE JSON line with the throughput (HBM GB/s over the algorithmic bytes,
 4.5625 B per output element), the roofline of the fused kernel, the CPU
-oracle's throughput on the host cores, and secondary figures (standalone
-quantize, dequantize, and in-repo read / copy kernels over the same input as
-HBM ceilings).
+oracle's throughput on the host cores, and secondary figures: the standalone
+quantize, the dequantize and the global-scale pre-pass on the same tensor;
+in-repo read / copy kernels over the same input as HBM ceilings; the ragged
+256-expert workload (pre-pass, quantize with per-expert scales, dequantize);
+the decode-shaped workload over 8 rotating buffer sets.
 
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+Every timed region is preceded by --settle-ms of untimed back-to-back
+launches (the clocks need ~30 ms of load to settle) and the warmup steps.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--settle-ms MS]
+                  [--no-cpu-baseline] [--no-secondary]
 """
 import argparse
 import hashlib
@@ -73,25 +79,60 @@ def checked(rc):
         raise RuntimeError("calibration kernel returned %d" % rc)
 
 
-def time_launches(fn, steps, warmup):
-    """Warm up, then time `steps` back-to-back launches. Returns (wall seconds
-    between two device synchronizations, device milliseconds per launch from
-    one pair of HIP events recorded on the launch stream around the whole
-    timed region)."""
+def settle(fn, settle_ms):
+    """Run fn back to back for settle_ms of wall time (untimed). Under
+    sustained load the GPU's clocks need about 30 ms to reach their steady
+    state, and they drop back after a fraction of a second idle; without
+    this the first few milliseconds of any measurement run slower."""
     import torch
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < settle_ms:
+        for _ in range(8):
+            fn()
+        torch.cuda.synchronize()
+
+
+def time_launches(fn, steps, warmup, settle_ms=0.0, chunks=10):
+    """Settle, warm up, then time `steps` back-to-back launches. Returns
+    (wall seconds between two device synchronizations, device ms per launch
+    from HIP events recorded on the launch stream around the whole region,
+    per-launch ms of each of `chunks` equal runs of launches (events at the
+    chunk boundaries))."""
+    import torch
+    settle(fn, settle_ms)
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
+    n_chunks = max(1, min(chunks, steps))
+    bounds = [round(i * steps / n_chunks) for i in range(n_chunks + 1)]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in bounds]
     t0 = time.perf_counter()
-    start.record()
-    for _ in range(steps):
-        fn()
-    end.record()
+    ev[0].record()
+    for c in range(n_chunks):
+        for _ in range(bounds[c + 1] - bounds[c]):
+            fn()
+        ev[c + 1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    return wall, start.elapsed_time(end) / steps
+    per = [ev[c].elapsed_time(ev[c + 1]) / (bounds[c + 1] - bounds[c]) for c in range(n_chunks)]
+    return wall, ev[0].elapsed_time(ev[-1]) / steps, per
+
+
+def pct(v, q):
+    v = sorted(v)
+    return v[min(len(v) - 1, max(0, int(round(q * (len(v) - 1)))))]
+
+
+def measure(name, fn, nbytes, elems, steps, settle_ms, extra=None):
+    """One secondary figure: kernel ms per launch and GB/s over `nbytes`."""
+    _, ms, per = time_launches(fn, steps, 3, settle_ms)
+    out = {"ms": round(ms, 4), "GB_s": round(nbytes / ms / 1e6, 1),
+           "elements_per_s": round(elems / ms * 1e3, 1), "bytes_per_launch": int(nbytes),
+           "ms_p10_p50_p90": [round(pct(per, q), 4) for q in (0.1, 0.5, 0.9)]}
+    if extra:
+        out.update(extra)
+    print("[bench] %-34s %8.4f ms  %7.1f GB/s" % (name, ms, out["GB_s"]), file=sys.stderr, flush=True)
+    return out
 
 
 def cpu_baseline(x):
@@ -124,14 +165,106 @@ def cpu_baseline(x):
     }
 
 
+def secondary_figures(M, W, x, packed, scales, args, dev):
+    """Other kernels and the other workload shapes (not the headline)."""
+    import numpy as np
+    import torch
+    sec = {}
+    st, ms = args.secondary_steps, args.settle_ms
+    # the other entry points on the prefill tensor
+    xq = x.view(torch.int16)[:, :INTER].contiguous().view(torch.bfloat16)
+    pq, sq = torch.empty_like(packed), torch.empty_like(scales)
+    sec["nvfp4_quantize"] = measure(
+        "nvfp4_quantize prefill-shaped", lambda: M.nvfp4_quantize(xq, packed=pq, scales=sq),
+        ROWS * INTER * 2.5625, ROWS * INTER, st, ms, {"shape": [ROWS, INTER]})
+    del xq, pq, sq
+    out = torch.empty((ROWS, INTER), dtype=torch.float32, device=dev)
+    sec["nvfp4_dequantize"] = measure(
+        "nvfp4_dequantize prefill-shaped",
+        lambda: M.nvfp4_dequantize(packed, scales, out=out),
+        ROWS * INTER * 4.5625, ROWS * INTER, st, ms, {"shape": [ROWS, INTER]})
+    del out
+    gsb = torch.empty(1, dtype=torch.float32, device=dev)
+    sec["swiglu_nvfp4_global_scale"] = measure(
+        "swiglu_nvfp4_global_scale prefill", lambda: M.swiglu_nvfp4_global_scale(x, gs=gsb),
+        ROWS * INTER * 4.0, ROWS * INTER, st, ms,
+        {"shape": [ROWS, 2 * INTER], "note": "per-tensor amax pre-pass; 3 launches"})
+    # in-repo calibration kernels over the same 805 MB input: HBM ceilings
+    calib = load_calib()
+    nbytes = x.numel() * 2
+    scratch = torch.empty(CALIB_BLOCKS * 16, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream().cuda_stream
+    sec["calib_read_ceiling"] = measure(
+        "calib read ceiling", lambda: checked(calib.nvfp4_calib_read(
+            x.data_ptr(), scratch.data_ptr(), nbytes, CALIB_BLOCKS, stream)),
+        nbytes, nbytes // 2, st, ms)
+    dst = torch.empty_like(x)
+    sec["calib_copy_ceiling"] = measure(
+        "calib copy ceiling", lambda: checked(calib.nvfp4_calib_copy(
+            x.data_ptr(), dst.data_ptr(), nbytes, CALIB_BLOCKS, stream)),
+        2 * nbytes, nbytes // 2, st, ms)
+    del dst, scratch
+
+    # ragged grouped MoE: 256 experts (Zipf 1.1), 131072 x 4096, per-expert
+    # global scales from the on-device pre-pass, then quantize and dequantize
+    print("[bench] generating ragged 256-expert workload", file=sys.stderr, flush=True)
+    w = W.ragged()
+    rr, ri = w.rows, w.out_cols
+    xr = torch.from_numpy(w.x.view(np.int16)).to(dev).view(torch.bfloat16)
+    offr = torch.from_numpy(w.offsets).to(dev)
+    del w
+    gsr = torch.empty(256, dtype=torch.float32, device=dev)
+    pr = torch.empty((rr, ri // 2), dtype=torch.uint8, device=dev)
+    sr = torch.empty((rr, ri // 16), dtype=torch.uint8, device=dev)
+    ragged = {"shape": [rr, 2 * ri], "experts": 256}
+    ragged["global_scale"] = measure(
+        "ragged swiglu_nvfp4_global_scale", lambda: M.swiglu_nvfp4_global_scale(xr, offr, gs=gsr),
+        rr * ri * 4.0, rr * ri, st, ms)
+    ragged["quantize"] = measure(
+        "ragged swiglu_nvfp4_quantize",
+        lambda: M.swiglu_nvfp4_quantize(xr, gsr, offr, packed=pr, scales=sr),
+        rr * ri * BYTES_PER_ELEM, rr * ri, st, ms)
+    del xr
+    outr = torch.empty((rr, ri), dtype=torch.float32, device=dev)
+    ragged["dequantize"] = measure(
+        "ragged nvfp4_dequantize", lambda: M.nvfp4_dequantize(pr, sr, gsr, offr, out=outr),
+        rr * ri * 4.5625, rr * ri, st, ms)
+    sec["ragged_256_experts"] = ragged
+    del outr, pr, sr, gsr, offr
+
+    # decode-shaped 8192 x 4096: the 67 MB input fits the 256 MB Infinity
+    # Cache, so launches rotate over 8 distinct input/output sets (537 MB)
+    print("[bench] generating decode-shaped workload", file=sys.stderr, flush=True)
+    w = W.decode()
+    dr, di = w.rows, w.out_cols
+    base = torch.from_numpy(w.x.view(np.int16)).to(dev).view(torch.bfloat16)
+    del w
+    sets = [(base.clone(), torch.empty((dr, di // 2), dtype=torch.uint8, device=dev),
+             torch.empty((dr, di // 16), dtype=torch.uint8, device=dev)) for _ in range(8)]
+    del base
+    k = [0]
+
+    def rotating():
+        xi, pi, si = sets[k[0] % 8]
+        k[0] += 1
+        M.swiglu_nvfp4_quantize(xi, packed=pi, scales=si)
+    sec["decode_shaped"] = measure(
+        "decode-shaped swiglu_nvfp4_quantize", rotating, dr * di * BYTES_PER_ELEM, dr * di,
+        max(st, 80), ms, {"shape": [dr, 2 * di], "note": "8 rotating input/output sets"})
+    del sets
+    return sec
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--settle-ms", type=float, default=300.0,
+                    help="untimed back-to-back launches before each warmup (clock settling)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
-    ap.add_argument("--secondary-steps", type=int, default=20)
+    ap.add_argument("--secondary-steps", type=int, default=40)
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -156,51 +289,22 @@ def main():
     def step():
         M.swiglu_nvfp4_quantize(x, packed=packed, scales=scales)
 
-    print("[bench] timing %d steps after %d warmup" % (args.steps, args.warmup), file=sys.stderr, flush=True)
-    wall, kern_ms = time_launches(step, args.steps, args.warmup)
+    print("[bench] timing %d steps after %d warmup (%.0f ms settle)"
+          % (args.steps, args.warmup, args.settle_ms), file=sys.stderr, flush=True)
+    wall, kern_ms, per = time_launches(step, args.steps, args.warmup, args.settle_ms)
     ms_per_step = wall * 1e3 / args.steps
     value = ALG_BYTES / (wall / args.steps) / 1e9
     achieved = ALG_BYTES / (kern_ms / 1e3) / 1e9
+    print("[bench] fused prefill: %.4f ms/step wall, %.4f ms/launch events, %.1f GB/s"
+          % (ms_per_step, kern_ms, value), file=sys.stderr, flush=True)
 
     secondary = None
     if not args.no_secondary:
-        print("[bench] secondary: quantize, dequantize, copy ceiling", file=sys.stderr, flush=True)
-        secondary = {}
-        sec_steps = args.secondary_steps
-        # standalone quantize of a compact BF16 tensor of the same output shape
-        xq = x.view(torch.int16)[:, :INTER].contiguous().view(torch.bfloat16)
-        pq = torch.empty_like(packed)
-        sq = torch.empty_like(scales)
-        _, mq = time_launches(lambda: M.nvfp4_quantize(xq, packed=pq, scales=sq), sec_steps, 3)
-        secondary["nvfp4_quantize"] = {
-            "shape": [ROWS, INTER], "bytes_per_launch": int(ROWS * INTER * 2.5625),
-            "ms": round(mq, 4), "GB_s": round(ROWS * INTER * 2.5625 / mq / 1e6, 1)}
-        del xq, pq, sq
-        out = torch.empty((ROWS, INTER), dtype=torch.float32, device=dev)
-        _, md = time_launches(lambda: M.nvfp4_dequantize(packed, scales, out=out), sec_steps, 3)
-        secondary["nvfp4_dequantize"] = {
-            "shape": [ROWS, INTER], "bytes_per_launch": int(ROWS * INTER * 4.5625),
-            "ms": round(md, 4), "GB_s": round(ROWS * INTER * 4.5625 / md / 1e6, 1)}
-        del out
-        # in-repo calibration kernels over the same 805 MB input: HBM ceilings
-        calib = load_calib()
-        nbytes = x.numel() * 2
-        scratch = torch.empty(CALIB_BLOCKS * 16, dtype=torch.uint8, device=dev)
-        stream = torch.cuda.current_stream().cuda_stream
-        _, mr = time_launches(lambda: checked(calib.nvfp4_calib_read(
-            x.data_ptr(), scratch.data_ptr(), nbytes, CALIB_BLOCKS, stream)), sec_steps, 3)
-        dst = torch.empty_like(x)
-        _, mc = time_launches(lambda: checked(calib.nvfp4_calib_copy(
-            x.data_ptr(), dst.data_ptr(), nbytes, CALIB_BLOCKS, stream)), sec_steps, 3)
-        del dst, scratch
-        read_gbs = nbytes / mr / 1e6
-        copy_gbs = 2 * nbytes / mc / 1e6
-        secondary["calib_read_ceiling"] = {"bytes_per_launch": nbytes, "ms": round(mr, 4),
-                                           "GB_s": round(read_gbs, 1)}
-        secondary["calib_copy_ceiling"] = {"bytes_per_launch": 2 * nbytes, "ms": round(mc, 4),
-                                           "GB_s": round(copy_gbs, 1)}
-        secondary["fused_frac_of_read_ceiling"] = round(achieved / read_gbs, 4)
-        secondary["fused_frac_of_copy_ceiling"] = round(achieved / copy_gbs, 4)
+        secondary = secondary_figures(M, W, x, packed, scales, args, dev)
+        r = secondary["calib_read_ceiling"]["GB_s"]
+        c = secondary["calib_copy_ceiling"]["GB_s"]
+        secondary["fused_frac_of_read_ceiling"] = round(achieved / r, 4)
+        secondary["fused_frac_of_copy_ceiling"] = round(achieved / c, 4)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -223,13 +327,16 @@ def main():
         "config": {"workload": "prefill-shaped MoE L1 epilogue", "rows": ROWS,
                    "intermediate": INTER, "input": [ROWS, 2 * INTER],
                    "layout": "interleaved [gate x8, up x8]", "global_scale": 1.0,
-                   "alg_bytes_per_step": ALG_BYTES, "parallelism": "single GPU"},
+                   "alg_bytes_per_step": ALG_BYTES, "parallelism": "single GPU",
+                   "settle_ms": args.settle_ms},
         "pct_of_peak": round(100.0 * value / PEAK_HBM_GBS, 2),
         "elements_per_s": round(ROWS * INTER / (wall / args.steps), 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "traffic": measured_traffic(),
-                     "kernel": "quantize_tiles_kernel<FusedBlock, true>", "kernel_ms": round(kern_ms, 5)},
+                     "kernel": "quantize_tiles_kernel<FusedBlock, true>",
+                     "kernel_ms": round(kern_ms, 5),
+                     "kernel_ms_p10_p50_p90": [round(pct(per, q), 5) for q in (0.1, 0.5, 0.9)]},
         "cpu_baseline": cpu,
         "secondary": secondary,
     }

@@ -51,9 +51,10 @@
  *   Every pointer is a DEVICE pointer (HIP/PyTorch allocations), except that
  *   none is dereferenced on the host. The caller owns every buffer. The
  *   library allocates nothing, keeps no state between calls, never
- *   synchronizes, and enqueues exactly one kernel on `stream` (NULL = the
- *   default stream). Inputs and outputs must not overlap. Every byte of the
- *   output regions described above is written.
+ *   synchronizes, and enqueues its kernels on `stream` (NULL = the default
+ *   stream): one kernel per call, three for the global-scale calls. Inputs
+ *   and outputs must not overlap. Every byte of the output regions
+ *   described above is written.
  *
  * Preconditions checked on the host, before any HIP call (so they work on a
  * machine without a GPU) - a failing check returns without launching:
@@ -132,6 +133,39 @@ nvfp4_status_t nvfp4_dequantize(const uint8_t *packed, const uint8_t *scales,
                                 const int32_t *expert_offsets,
                                 int32_t num_experts, float *out,
                                 hipStream_t stream);
+
+/*
+ * Global-scale pre-pass of two-level NVFP4 scaling: per expert (or for the
+ * whole tensor when expert_offsets is NULL) the largest |value| the
+ * quantizer will see, amax_e, and the FP32 global scale
+ *     gs[e] = RN(amax_e / (6 * 448))        (1.0 when amax_e == 0 or the
+ *                                            expert has no rows),
+ * which puts the expert's largest block scale on the FP8 maximum 448.
+ * Page: "NVFP4-1.1_APPROACH_PART_2.md" (the fused kernel's l2_global_scale
+ * parameter, the decode-direction global scale in the FP8 scale rule), with
+ * the per-expert amax / (6 * 448) recipe of the ragged grouped MoE workload.
+ * The values are those of the matching quantize call: BF16 x for
+ * nvfp4_global_scale, y = silu(gate) * up in FP32 (bit-identical to what
+ * swiglu_nvfp4_quantize computes) for swiglu_nvfp4_global_scale. Inputs and
+ * their checks are those of the matching quantize call; rows == 0 still
+ * writes the outputs (amax 0, gs 1.0).
+ *   amax   [G] FP32 output, or NULL (then gs is used as the accumulator)
+ *   gs     [G] FP32 output, required; G = num_experts, or 1 without experts
+ * Outputs must be 4-byte aligned; num_experts <= 1024 (else
+ * NVFP4_ERROR_UNSUPPORTED_SHAPE). Enqueues three kernels on `stream`: zero
+ * the accumulator, reduce the input, write gs. The result does not depend
+ * on the order of the reduction.
+ */
+nvfp4_status_t nvfp4_global_scale(const uint16_t *x, int64_t rows, int64_t cols,
+                                  int64_t ld_x, const int32_t *expert_offsets,
+                                  int32_t num_experts, float *amax, float *gs,
+                                  hipStream_t stream);
+
+nvfp4_status_t swiglu_nvfp4_global_scale(const uint16_t *gate_up, int64_t rows,
+                                         int64_t inter, int64_t ld_in,
+                                         const int32_t *expert_offsets,
+                                         int32_t num_experts, float *amax,
+                                         float *gs, hipStream_t stream);
 
 /* Static English text for a status code (never NULL). */
 const char *nvfp4_status_string(nvfp4_status_t status);

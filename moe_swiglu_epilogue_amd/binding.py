@@ -20,7 +20,7 @@ STATUS = {0: "NVFP4_SUCCESS", 1: "NVFP4_ERROR_INVALID_VALUE",
           4: "NVFP4_ERROR_LAUNCH"}
 
 EXPORTS = ("nvfp4_quantize", "swiglu_nvfp4_quantize", "nvfp4_dequantize",
-           "nvfp4_status_string")
+           "nvfp4_global_scale", "swiglu_nvfp4_global_scale", "nvfp4_status_string")
 
 _LIB = None
 _vp = C.c_void_p
@@ -54,6 +54,9 @@ def _lib():
         L.swiglu_nvfp4_quantize.restype = C.c_int
         L.nvfp4_dequantize.argtypes = [_vp, _vp, _i64, _i64, _vp, _vp, _i32, _vp, _vp]
         L.nvfp4_dequantize.restype = C.c_int
+        for fn in (L.nvfp4_global_scale, L.swiglu_nvfp4_global_scale):
+            fn.argtypes = [_vp, _i64, _i64, _i64, _vp, _i32, _vp, _vp, _vp]
+            fn.restype = C.c_int
         L.nvfp4_status_string.argtypes = [C.c_int]
         L.nvfp4_status_string.restype = C.c_char_p
         _LIB = L
@@ -127,7 +130,7 @@ def _call(fn, what, *args):
         raise Nvfp4Error(st, what)
 
 
-# ---- the three entry points -----------------------------------------------------
+# ---- entry points --------------------------------------------------------------
 def nvfp4_quantize(x: torch.Tensor, gs: torch.Tensor | None = None,
                    expert_offsets: torch.Tensor | None = None, *,
                    packed: torch.Tensor | None = None, scales: torch.Tensor | None = None,
@@ -190,3 +193,41 @@ def nvfp4_dequantize(packed: torch.Tensor, scales: torch.Tensor,
     _call(_lib().nvfp4_dequantize, "nvfp4_dequantize", _ptr(packed), _ptr(scales), rows, cols,
           _ptr(gs), _ptr(expert_offsets), e, _ptr(out), _stream(stream))
     return out
+
+
+def _global_scale(fn, what, x, cols, expert_offsets, amax, gs, stream):
+    rows = x.shape[0]
+    e = _experts(None, expert_offsets, x.device)
+    groups = e if expert_offsets is not None else 1
+    gs = _out(gs, (groups,), torch.float32, x.device, "gs")
+    a = None
+    if amax is True:
+        a = torch.empty((groups,), dtype=torch.float32, device=x.device)
+    elif isinstance(amax, torch.Tensor):
+        a = _out(amax, (groups,), torch.float32, x.device, "amax")
+    _call(fn, what, _ptr(x), rows, cols, _pitch(x), _ptr(expert_offsets), e, _ptr(a), _ptr(gs),
+          _stream(stream))
+    return gs if a is None else (gs, a)
+
+
+def nvfp4_global_scale(x: torch.Tensor, expert_offsets: torch.Tensor | None = None, *,
+                       gs: torch.Tensor | None = None, amax: torch.Tensor | bool | None = None,
+                       stream=None):
+    """BF16 [rows, cols] -> gs float32 [G] (G = experts, or 1), gs = amax / (6*448)
+    per expert; with ``amax`` True or a tensor also returns the FP32 amax [G]."""
+    x = _bf16_matrix(x, "x")
+    return _global_scale(_lib().nvfp4_global_scale, "nvfp4_global_scale", x, x.shape[1],
+                         expert_offsets, amax, gs, stream)
+
+
+def swiglu_nvfp4_global_scale(gate_up: torch.Tensor, expert_offsets: torch.Tensor | None = None,
+                              *, gs: torch.Tensor | None = None,
+                              amax: torch.Tensor | bool | None = None, stream=None):
+    """Interleaved BF16 [rows, 2I] -> gs float32 [G] from the amax of the SwiGLU
+    values (as swiglu_nvfp4_quantize computes them) per expert; with ``amax``
+    True or a tensor also returns the FP32 amax [G]."""
+    x = _bf16_matrix(gate_up, "gate_up")
+    if x.shape[1] % 2:
+        raise ValueError("gate_up must have an even number of columns")
+    return _global_scale(_lib().swiglu_nvfp4_global_scale, "swiglu_nvfp4_global_scale", x,
+                         x.shape[1] // 2, expert_offsets, amax, gs, stream)

@@ -198,44 +198,29 @@ struct PlainBlock {
     }
 };
 
-template <class Block, bool kWide>
-__global__ __launch_bounds__(Block::kWaves * kWave) void quantize_tiles_kernel(
-    const uint16_t* __restrict__ in, int64_t ld_in, Geometry geo,
-    const float* __restrict__ gs, const int32_t* __restrict__ offsets, int num_experts,
-    uint8_t* __restrict__ packed, uint8_t* __restrict__ scales,
-    float* __restrict__ values_out)
+// A wave's walk over its tiles (first `tile`, then every `stride`-th):
+// keeps one tile in flight and calls op(tile, t, b, y) with each lane's block b of
+// tile t and its 16 values y. Loop invariant: tile t is staged in LDS and no
+// loads are in flight. Each pass issues the loads of the next tile first,
+// computes tile t from LDS and runs op, then stages the next tile; op may
+// store (its stores are the only memory operations younger than those
+// loads, so the wait before staging does not wait for them) and may use the
+// wave's LDS area between the two LDS syncs of the pass.
+template <class Block, class Op>
+__device__ __forceinline__ void walk_tiles(const uint16_t* in, int64_t ld_in, const Geometry& geo,
+                                           int tile, int stride, int lane, u32x4* lds,
+                                           const uint8_t* sig, Op&& op)
 {
     constexpr int P = Block::P;
-    constexpr int kWaves = Block::kWaves;
-    __shared__ u32x4 stage[kWaves][kStageSlots(P)];
-    __shared__ float sig[Block::kSigmaTable ? nvfp4::kSigEntries : 1];
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wave = uniform(threadIdx.x / kWave);
-    u32x4* lds = stage[wave];
-    const int cols = geo.bpr * 16;
-    const int stride = gridDim.x * kWaves;
-    int tile = blockIdx.x * kWaves + wave;
-    if constexpr (Block::kSigmaTable) {
-        // Every wave of the workgroup helps fill the table, so the barrier
-        // below is reached by all of them (including waves without a tile).
-        for (int i = threadIdx.x; i < nvfp4::kSigEntries; i += kWaves * kWave)
-            sig[i] = nvfp4::sigma_entry(i);
-        __syncthreads();
-    }
-    if (tile >= geo.tiles)
-        return;
     Tile t = tile_at(tile, geo);
     u32x4 v[P];
     load_tile<P>(v, in, ld_in, t, lane);
-    // Without experts the global scale (and its reciprocal) is the same for
-    // every row: computed once here instead of per tile.
-    nvfp4::RowScale rs = nvfp4::row_scale(gs != nullptr ? gs[0] : 1.0f);
     stage_tile<P>(lds, v, lane);
-    // Loop invariant: tile t is staged in LDS and no loads are in flight.
-    // Each pass issues the loads of the next tile first, computes and stores
-    // tile t, then stages the next tile; the only memory operations younger
-    // than those loads are this tile's stores, so the wait before staging
-    // does not wait for the stores.
+    // Keeps the prologue's staging out of the loop: were the compiler to
+    // merge it with the loop's own staging at the loop head, the merged
+    // wait would have to drain every outstanding memory operation, this
+    // tile's stores included (vmcnt counts stores too), on every pass.
+    wave_lds_sync();
     for (;;) {
         const int next = tile + stride;
         const bool has_next = next < geo.tiles;
@@ -244,20 +229,149 @@ __global__ __launch_bounds__(Block::kWaves * kWave) void quantize_tiles_kernel(
             tn = tile_at(next, geo);
             load_tile<P>(v, in, ld_in, tn, lane);
         }
-        if (offsets != nullptr)
-            rs = nvfp4::row_scale(nvfp4::row_global_scale(gs, offsets, num_experts, t.row));
         wave_lds_sync();
         // In a partial tile the lanes past its end redo the tile's last block
-        // and store the same bytes to the same place: no lane is masked, so
-        // there is no branch around the stores (a branch would make the wait
-        // before the next staging also wait for these stores).
+        // (same values, same output bytes to the same place): no lane is
+        // masked, so there is no branch around op's stores (a branch would
+        // make the wait before the next staging also wait for them).
         const int b = min(lane, t.nblk - 1);
         u32x4 c[P];
 #pragma unroll
         for (int k = 0; k < P; ++k)
             c[k] = lds[lds_slot(b * P + k)];
         float y[16];
-        Block::values(c, y, reinterpret_cast<const uint8_t*>(sig));
+        Block::values(c, y, sig);
+        op(tile, t, b, y);
+        if (!has_next)
+            break;
+        wave_lds_sync();
+        stage_tile<P>(lds, v, lane);
+        tile = next;
+        t = tn;
+    }
+}
+
+// ---- per-expert lookups, batched ---------------------------------------------
+// With experts every tile needs its row's expert (and that expert's global
+// scale). For up to kLdsExperts experts the kernels copy expert_offsets and
+// gs into LDS once per workgroup; then every 64 tiles each lane of a wave
+// looks up the expert of one of the wave's next 64 tiles (tile + lane *
+// stride) with a branch-free binary search in LDS and prepares that tile's
+// scale constants, and each tile reads its lane's values with v_readlane.
+// LDS reads count against lgkmcnt, not vmcnt, so the lookups never wait for
+// the tile loads or stores in flight. More experts fall back to a scalar
+// search per tile.
+constexpr int kLdsExperts = 1024;
+
+struct ExpertTable {
+    int32_t off[kLdsExperts];   // expert_offsets[0 .. E-1]
+    float gs[kLdsExperts];      // gs[e], or 1.0 without gs
+};
+
+template <int kThreadsPerBlock>
+__device__ __forceinline__ void fill_expert_table(ExpertTable& tab, const int32_t* offsets,
+                                                  const float* gs, int num_experts)
+{
+    for (int i = threadIdx.x; i < num_experts; i += kThreadsPerBlock) {
+        tab.off[i] = offsets[i];
+        tab.gs[i] = gs != nullptr ? gs[i] : 1.0f;
+    }
+}
+
+// Largest e < num_experts with off[e] <= row (off[0] = 0 <= row): binary
+// lifting over powers of two, the same number of steps on every lane.
+__device__ __forceinline__ int lds_expert_of(const int32_t* off, int num_experts, int row)
+{
+    int lo = 0;
+    for (int step = 1 << (31 - __builtin_clz(num_experts)); step > 0; step >>= 1) {
+        const int i = lo + step;
+        if (i < num_experts && off[min(i, num_experts - 1)] <= row)
+            lo = i;
+    }
+    return lo;
+}
+
+// Lane j holds the expert (and scale constants) of the wave's tile
+// tile0 + j * stride; tiles past the end get the last row's.
+struct ExpertBatch {
+    int e;
+    float gs, k, rk;
+    __device__ __forceinline__ void refill(const ExpertTable& tab, int num_experts, int tile0,
+                                           int stride, const Geometry& geo, int lane)
+    {
+        const int tj = tile0 + lane * stride;
+        const int row = tj < geo.tiles ? tj / geo.cpr : geo.rows - 1;
+        e = lds_expert_of(tab.off, num_experts, row);
+        const nvfp4::RowScale r = nvfp4::row_scale(tab.gs[e]);
+        gs = r.gs;
+        k = r.k;
+        rk = r.rk;
+    }
+    __device__ __forceinline__ int expert(int j) const { return __builtin_amdgcn_readlane(e, j); }
+    __device__ __forceinline__ nvfp4::RowScale scale(int j) const
+    {
+        nvfp4::RowScale r;
+        r.gs = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gs), j));
+        r.k = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(k), j));
+        r.rk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(rk), j));
+        r.pow2 = (__float_as_uint(r.gs) & 0x007fffffu) == 0;
+        return r;
+    }
+};
+
+// Fills the workgroup's sigmoid table (fused input only). Every wave of the
+// workgroup takes part, so all of them reach the barrier.
+template <class Block>
+__device__ __forceinline__ void fill_sigma_table(float* sig)
+{
+    if constexpr (Block::kSigmaTable) {
+        for (int i = threadIdx.x; i < nvfp4::kSigEntries; i += Block::kWaves * kWave)
+            sig[i] = nvfp4::sigma_entry(i);
+    }
+}
+
+template <class Block, bool kWide>
+__global__ __launch_bounds__(Block::kWaves * kWave) void quantize_tiles_kernel(
+    const uint16_t* __restrict__ in, int64_t ld_in, Geometry geo,
+    const float* __restrict__ gs, const int32_t* __restrict__ offsets, int num_experts,
+    uint8_t* __restrict__ packed, uint8_t* __restrict__ scales,
+    float* __restrict__ values_out)
+{
+    constexpr int kWaves = Block::kWaves;
+    __shared__ u32x4 stage[kWaves][kStageSlots(Block::P)];
+    __shared__ float sig[Block::kSigmaTable ? nvfp4::kSigEntries : 1];
+    __shared__ ExpertTable tab;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = uniform(threadIdx.x / kWave);
+    u32x4* lds = stage[wave];
+    const int cols = geo.bpr * 16;
+    const int tile = blockIdx.x * kWaves + wave;
+    const int stride = gridDim.x * kWaves;
+    const bool lds_experts = offsets != nullptr && num_experts <= kLdsExperts;
+    fill_sigma_table<Block>(sig);
+    if (lds_experts)
+        fill_expert_table<kWaves * kWave>(tab, offsets, gs, num_experts);
+    if (Block::kSigmaTable || lds_experts)
+        __syncthreads();
+    if (tile >= geo.tiles)
+        return;
+    // Without experts the global scale (and its reciprocal) is the same for
+    // every row: computed once here instead of per tile.
+    nvfp4::RowScale rs = nvfp4::row_scale(gs != nullptr ? gs[0] : 1.0f);
+    ExpertBatch batch;
+    int n = 0;   // tiles done by this wave
+    walk_tiles<Block>(in, ld_in, geo, tile, stride, lane, lds,
+                      reinterpret_cast<const uint8_t*>(sig),
+                      [&](int tile_index, const Tile& t, int b, const float (&y)[16]) {
+        if (lds_experts) {
+            const int j = n & (kWave - 1);
+            if (j == 0)
+                batch.refill(tab, num_experts, tile_index, stride, geo, lane);
+            rs = batch.scale(j);
+            ++n;
+        } else if (offsets != nullptr) {
+            rs = nvfp4::row_scale(nvfp4::row_global_scale(gs, offsets, num_experts, t.row));
+        }
         uint32_t sf;
         const uint2 q = nvfp4::quantize16(y, rs, sf);
         store_tile_outputs<kWide>(reinterpret_cast<uint8_t*>(lds), q, sf, t, b, lane, geo,
@@ -269,12 +383,108 @@ __global__ __launch_bounds__(Block::kWaves * kWave) void quantize_tiles_kernel(
             for (int i = 0; i < 4; ++i)
                 dst[i] = f32x4{y[4 * i], y[4 * i + 1], y[4 * i + 2], y[4 * i + 3]};
         }
-        if (!has_next)
-            break;
-        wave_lds_sync();
-        stage_tile<P>(lds, v, lane);
-        tile = next;
-        t = tn;
+    });
+}
+
+// ---------------------------------------------------------------------------
+// Global-scale pre-pass of the two-level scaling: amax of the quantizer's
+// input values (the SwiGLU outputs, or the BF16 values) over the rows of
+// each expert (or of the whole tensor), then gs = amax / (6 * 448).
+// Three launches: zero the accumulator, reduce, finalize. The reduction
+// folds each tile's maximum into a per-workgroup LDS array (one slot per
+// expert) and flushes it with one global atomic max per touched expert.
+// The maxima are non-negative floats, whose order is that of their bit
+// patterns as unsigned integers, so the atomics work on the bits.
+// ---------------------------------------------------------------------------
+constexpr int kMaxScaleGroups = 1024;    // experts per global-scale call (LDS slots)
+constexpr float kFp4Fp8Max = 6.0f * 448.0f;
+
+__device__ __forceinline__ float wave_max(float v)
+{
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1)
+        v = fmaxf(v, __shfl_xor(v, o));
+    return v;
+}
+
+__global__ void fill_u32_kernel(uint32_t* __restrict__ p, int n, uint32_t value)
+{
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x)
+        p[i] = value;
+}
+
+template <class Block>
+__global__ __launch_bounds__(Block::kWaves * kWave) void amax_tiles_kernel(
+    const uint16_t* __restrict__ in, int64_t ld_in, Geometry geo,
+    const int32_t* __restrict__ offsets, int groups, uint32_t* __restrict__ acc)
+{
+    constexpr int kWaves = Block::kWaves;
+    static_assert(kMaxScaleGroups <= kLdsExperts, "experts of a global-scale call fit in LDS");
+    __shared__ u32x4 stage[kWaves][kStageSlots(Block::P)];
+    __shared__ float sig[Block::kSigmaTable ? nvfp4::kSigEntries : 1];
+    __shared__ uint32_t part[kMaxScaleGroups];
+    __shared__ ExpertTable tab;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = uniform(threadIdx.x / kWave);
+    const int tile = blockIdx.x * kWaves + wave;
+    const int stride = gridDim.x * kWaves;
+    fill_sigma_table<Block>(sig);
+    for (int i = threadIdx.x; i < groups; i += kWaves * kWave)
+        part[i] = 0u;
+    if (offsets != nullptr)
+        fill_expert_table<kWaves * kWave>(tab, offsets, nullptr, groups);
+    __syncthreads();
+    if (tile < geo.tiles) {
+        // Each lane keeps a running max over the wave's consecutive tiles of
+        // one expert; the wave reduces it and folds it into the workgroup's
+        // slot when the expert changes, and once at the end.
+        float run = 0.0f;
+        int cur = -1;
+        ExpertBatch batch;
+        int n = 0;
+        auto flush = [&]() {
+            const float m = wave_max(run);
+            if (lane == 0)
+                atomicMax(&part[cur], __float_as_uint(m));
+        };
+        walk_tiles<Block>(in, ld_in, geo, tile, stride, lane, stage[wave],
+                          reinterpret_cast<const uint8_t*>(sig),
+                          [&](int tile_index, const Tile&, int, const float (&y)[16]) {
+            int e = 0;
+            if (offsets != nullptr) {
+                const int j = n & (kWave - 1);
+                if (j == 0)
+                    batch.refill(tab, groups, tile_index, stride, geo, lane);
+                e = batch.expert(j);
+                ++n;
+            }
+            if (e != cur) {
+                if (cur >= 0)
+                    flush();
+                cur = e;
+                run = 0.0f;
+            }
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                run = fmaxf(run, fabsf(y[i]));
+        });
+        flush();
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < groups; i += kWaves * kWave) {
+        const uint32_t m = part[i];
+        if (m != 0u)
+            atomicMax(&acc[i], m);
+    }
+}
+
+// gs[e] = RN(amax[e] / 2688) (IEEE division), 1.0 for an empty or all-zero
+// expert; acc holds the amax bits and may be the gs array itself.
+__global__ void global_scale_kernel(const uint32_t* acc, float* gs, int n)
+{
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) {
+        const float a = __uint_as_float(acc[i]);
+        gs[i] = a > 0.0f ? a / kFp4Fp8Max : 1.0f;
     }
 }
 
@@ -396,6 +606,45 @@ nvfp4_status_t launched()
     return hipGetLastError() == hipSuccess ? NVFP4_SUCCESS : NVFP4_ERROR_LAUNCH;
 }
 
+// Arguments of the global-scale calls beyond the input's: the scale groups
+// (experts, or the whole tensor), at most kMaxScaleGroups, and 4-byte
+// aligned outputs.
+nvfp4_status_t check_scale_outputs(int32_t num_experts, const float* amax, const float* gs)
+{
+    if (!gs)
+        return NVFP4_ERROR_INVALID_VALUE;
+    if (num_experts > kMaxScaleGroups)
+        return NVFP4_ERROR_UNSUPPORTED_SHAPE;
+    if (!aligned(gs, 4) || (amax && !aligned(amax, 4)))
+        return NVFP4_ERROR_MISALIGNED;
+    return NVFP4_SUCCESS;
+}
+
+// Zero the accumulator (amax, or gs itself without amax), reduce the tiles
+// (skipped for an empty input), write gs.
+template <class Block>
+nvfp4_status_t launch_global_scale(const Geometry* g, const uint16_t* in, int64_t ld,
+                                   const int32_t* offsets, int32_t num_experts, float* amax,
+                                   float* gs, hipStream_t stream)
+{
+    const int groups = offsets != nullptr ? num_experts : 1;
+    uint32_t* acc = reinterpret_cast<uint32_t*>(amax != nullptr ? amax : gs);
+    const dim3 small((groups + 255) / 256);
+    hipLaunchKernelGGL(fill_u32_kernel, small, dim3(256), 0, stream, acc, groups, 0u);
+    nvfp4_status_t st = launched();
+    if (st == NVFP4_SUCCESS && g != nullptr) {
+        hipLaunchKernelGGL((amax_tiles_kernel<Block>), persistent_grid_for<Block>(*g),
+                           dim3(Block::kWaves * kWave), 0, stream, in, ld, *g, offsets, groups,
+                           acc);
+        st = launched();
+    }
+    if (st == NVFP4_SUCCESS) {
+        hipLaunchKernelGGL(global_scale_kernel, small, dim3(256), 0, stream, acc, gs, groups);
+        st = launched();
+    }
+    return st;
+}
+
 }  // namespace
 
 extern "C" {
@@ -477,6 +726,61 @@ nvfp4_status_t nvfp4_dequantize(const uint8_t* packed, const uint8_t* scales, in
     hipLaunchKernelGGL(nvfp4_dequantize_kernel, grid_for(g), dim3(kThreads), 0, stream,
                        packed, scales, g, gs, expert_offsets, (int)num_experts, out);
     return launched();
+}
+
+nvfp4_status_t nvfp4_global_scale(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
+                                  const int32_t* expert_offsets, int32_t num_experts,
+                                  float* amax, float* gs, hipStream_t stream)
+{
+    if (rows < 0 || cols < 0 || ld_x < cols)
+        return NVFP4_ERROR_INVALID_VALUE;
+    if (cols % 16 != 0)
+        return NVFP4_ERROR_UNSUPPORTED_SHAPE;
+    nvfp4_status_t st = check_experts(expert_offsets, num_experts);
+    if (st == NVFP4_SUCCESS)
+        st = check_scale_outputs(num_experts, amax, gs);
+    if (st != NVFP4_SUCCESS)
+        return st;
+    Geometry g;
+    const bool empty = rows == 0 || cols == 0;
+    if (!empty) {
+        if (!x)
+            return NVFP4_ERROR_INVALID_VALUE;
+        if (!aligned(x, 16) || (ld_x * 2) % 16 != 0)
+            return NVFP4_ERROR_MISALIGNED;
+        if ((st = make_geometry(rows, cols, g)) != NVFP4_SUCCESS)
+            return st;
+    }
+    return launch_global_scale<PlainBlock>(empty ? nullptr : &g, x, ld_x, expert_offsets,
+                                           num_experts, amax, gs, stream);
+}
+
+nvfp4_status_t swiglu_nvfp4_global_scale(const uint16_t* gate_up, int64_t rows, int64_t inter,
+                                         int64_t ld_in, const int32_t* expert_offsets,
+                                         int32_t num_experts, float* amax, float* gs,
+                                         hipStream_t stream)
+{
+    if (rows < 0 || inter < 0 || inter > INT64_MAX / 2 || ld_in < 2 * inter)
+        return NVFP4_ERROR_INVALID_VALUE;
+    if (inter % 16 != 0)
+        return NVFP4_ERROR_UNSUPPORTED_SHAPE;
+    nvfp4_status_t st = check_experts(expert_offsets, num_experts);
+    if (st == NVFP4_SUCCESS)
+        st = check_scale_outputs(num_experts, amax, gs);
+    if (st != NVFP4_SUCCESS)
+        return st;
+    Geometry g;
+    const bool empty = rows == 0 || inter == 0;
+    if (!empty) {
+        if (!gate_up)
+            return NVFP4_ERROR_INVALID_VALUE;
+        if (!aligned(gate_up, 16) || (ld_in * 2) % 16 != 0)
+            return NVFP4_ERROR_MISALIGNED;
+        if ((st = make_geometry(rows, inter, g)) != NVFP4_SUCCESS)
+            return st;
+    }
+    return launch_global_scale<FusedBlock>(empty ? nullptr : &g, gate_up, ld_in, expert_offsets,
+                                           num_experts, amax, gs, stream);
 }
 
 const char* nvfp4_status_string(nvfp4_status_t status)

@@ -38,7 +38,8 @@ def _exported(lib_path):
 
 def test_header_declares_the_entry_points():
     assert _declared() == sorted(["nvfp4_quantize", "swiglu_nvfp4_quantize",
-                                  "nvfp4_dequantize", "nvfp4_status_string"])
+                                  "nvfp4_dequantize", "nvfp4_global_scale",
+                                  "swiglu_nvfp4_global_scale", "nvfp4_status_string"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -139,6 +140,32 @@ def test_dequant_validation(lib):
     assert d(lib, rows=0, packed=None, scales=None, out=None) == OK
 
 
+def gsc(lib, fused=False, x=A16, rows=4, cols=32, ld=None, offs=None, ne=0, amax=None, gs=A16):
+    if fused:
+        return lib.swiglu_nvfp4_global_scale(x, rows, cols, 2 * cols if ld is None else ld,
+                                             offs, ne, amax, gs, None)
+    return lib.nvfp4_global_scale(x, rows, cols, cols if ld is None else ld, offs, ne, amax,
+                                  gs, None)
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_global_scale_validation(lib, fused):
+    # every failing check returns before the first launch (rows == 0 is not a
+    # no-op for these calls: they still write amax 0 and gs 1.0)
+    assert gsc(lib, fused, rows=-1) == INVALID
+    assert gsc(lib, fused, cols=24, ld=48 if fused else 24) == SHAPE
+    assert gsc(lib, fused, ld=30 if not fused else 62) == INVALID
+    assert gsc(lib, fused, gs=None) == INVALID
+    assert gsc(lib, fused, x=None) == INVALID
+    assert gsc(lib, fused, x=A16 + 2) == MISALIGNED
+    assert gsc(lib, fused, gs=A16 + 2) == MISALIGNED
+    assert gsc(lib, fused, amax=A16 + 1) == MISALIGNED
+    assert gsc(lib, fused, ne=3) == INVALID
+    assert gsc(lib, fused, offs=A16, ne=0) == INVALID
+    assert gsc(lib, fused, offs=A16, ne=1025) == SHAPE
+    assert gsc(lib, fused, rows=2**31, cols=16, ld=32 if fused else 16) == SHAPE
+
+
 def test_binding_rejects_host_tensors():
     import moe_swiglu_epilogue_amd as M
     x = torch.zeros(4, 32, dtype=torch.bfloat16)
@@ -148,3 +175,7 @@ def test_binding_rejects_host_tensors():
         M.swiglu_nvfp4_quantize(torch.zeros(4, 64, dtype=torch.bfloat16))
     with pytest.raises(TypeError):
         M.nvfp4_dequantize(torch.zeros(4, 16, dtype=torch.uint8), torch.zeros(4, 2, dtype=torch.uint8))
+    with pytest.raises(TypeError):
+        M.nvfp4_global_scale(x)
+    with pytest.raises(TypeError):
+        M.swiglu_nvfp4_global_scale(torch.zeros(4, 64, dtype=torch.bfloat16))

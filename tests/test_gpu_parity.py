@@ -218,6 +218,14 @@ def test_fused_ragged_experts_and_dequant(M):
     xt = dev_bf16(w.x)
     gst, offt = gs_tensor(gs), dev(off)
     pt, st = M.swiglu_nvfp4_quantize(xt, gst, offt)
+    # the on-device global-scale pre-pass at full size
+    say("swiglu_nvfp4_global_scale ragged")
+    ggs, gam = M.swiglu_nvfp4_global_scale(xt, offt, amax=True)
+    ggs, gam = host(ggs), host(gam)
+    amax_ref = oracle.group_amax(y_ref, off)
+    assert np.all(np.abs(gam - amax_ref) <= P.SWIGLU_RTOL * amax_ref), "expert amax"
+    P.assert_bytes_equal("gs from the GPU amax", ggs.view(np.uint32),
+                         oracle.expert_global_scale(gam).view(np.uint32))
     del xt
     say("nvfp4_dequantize ragged")
     dq = M.nvfp4_dequantize(pt, st, gst, offt)
@@ -232,6 +240,76 @@ def test_fused_ragged_experts_and_dequant(M):
     # dequant round trip: bit-exact against the oracle's dequant of the GPU bytes
     rdq = oracle.dequantize(p[sel], s[sel], gs_rows[sel])
     P.assert_bytes_equal("dequant", dq[sel].view(np.uint32), rdq.view(np.uint32))
+
+
+# ---- global-scale pre-pass ----------------------------------------------------------------
+def _group_max(y, off):
+    return np.array([np.max(np.abs(y[a:b])) if b > a else 0.0 for a, b in zip(off[:-1], off[1:])],
+                    np.float32)
+
+
+@pytest.mark.parametrize("rows,cols,experts,empty,seed", [
+    (1, 16, 0, 0, 1), (300, 1040, 7, 2, 2), (1024, 2048, 64, 9, 3), (77, 4096, 0, 0, 4)])
+def test_global_scale_plain_exact(M, rows, cols, experts, empty, seed):
+    x = W.random_plain(rows, cols, seed, scale=10.0)
+    off = W.random_offsets(rows, experts, seed, empty=empty) if experts else None
+    # plant each expert's extreme on its first or last row, negative
+    groups = off if off is not None else np.array([0, rows], np.int32)
+    for e, (a, b) in enumerate(zip(groups[:-1], groups[1:])):
+        if b > a:
+            x[b - 1 if e % 2 else a, (7 * e) % cols] = W.to_bf16_bits(np.array([-3.0e4 - e]))[0]
+    xf = W.bf16_bits_to_f32(x)
+    say("nvfp4_global_scale", rows, cols, "experts", experts, "empty", empty)
+    xt = dev_bf16(x)
+    offt = None if off is None else dev(off)
+    gs, am = M.nvfp4_global_scale(xt, offt, amax=True)
+    gs2 = M.nvfp4_global_scale(xt, offt)            # gs doubles as the accumulator
+    gs, am, gs2 = host(gs), host(am), host(gs2)
+    ref_am = oracle.group_amax(xf, groups)
+    P.assert_bytes_equal("amax", am.view(np.uint32), ref_am.view(np.uint32))
+    ref_gs = oracle.expert_global_scale(ref_am)
+    P.assert_bytes_equal("gs", gs.view(np.uint32), ref_gs.view(np.uint32))
+    P.assert_bytes_equal("gs without amax", gs2.view(np.uint32), ref_gs.view(np.uint32))
+
+
+@pytest.mark.parametrize("rows,inter,experts,empty,seed", [
+    (64, 1040, 0, 0, 5), (700, 2048, 32, 5, 6), (513, 3072, 256, 40, 7)])
+def test_global_scale_fused(M, rows, inter, experts, empty, seed):
+    x = W.random_fused(rows, inter, seed, 2.0)
+    off = W.random_offsets(rows, experts, seed, empty=empty) if experts else None
+    groups = off if off is not None else np.array([0, rows], np.int32)
+    say("swiglu_nvfp4_global_scale", rows, inter, "experts", experts, "empty", empty)
+    xt = dev_bf16(x)
+    offt = None if off is None else dev(off)
+    gs, am = M.swiglu_nvfp4_global_scale(xt, offt, amax=True)
+    _, _, y = M.swiglu_nvfp4_quantize(xt, swiglu_out=True)
+    gs, am, y = host(gs), host(am), host(y)
+    # exactly the largest |y| of the quantizer's own FP32 SwiGLU values
+    P.assert_bytes_equal("amax vs the kernel's y", am.view(np.uint32),
+                         _group_max(y, groups).view(np.uint32))
+    ref_am = oracle.group_amax(oracle.swiglu(x), groups)
+    assert np.all(np.abs(am - ref_am) <= P.SWIGLU_RTOL * ref_am), "amax vs oracle"
+    P.assert_bytes_equal("gs", gs.view(np.uint32),
+                         oracle.expert_global_scale(am).view(np.uint32))
+    # the quantize that consumes these scales meets the fused acceptance rules
+    fused_check(M, x, "fused with device global scales", gs=gs if off is not None else gs[0],
+                off=off)
+
+
+def test_global_scale_empty_and_zero(M):
+    for fn, cols in ((M.nvfp4_global_scale, 32), (M.swiglu_nvfp4_global_scale, 64)):
+        gs, am = fn(torch.zeros((0, cols), dtype=torch.bfloat16, device="cuda"), amax=True)
+        assert host(gs).tolist() == [1.0] and host(am).tolist() == [0.0]
+        off = dev(np.zeros(5, np.int32))
+        gs, am = fn(torch.zeros((0, cols), dtype=torch.bfloat16, device="cuda"), off, amax=True)
+        assert host(gs).tolist() == [1.0] * 4 and host(am).tolist() == [0.0] * 4
+        z = torch.zeros((40, cols), dtype=torch.bfloat16, device="cuda")
+        off = dev(np.array([0, 10, 10, 40], np.int32))
+        z[10:40] = 1.0
+        gs, am = fn(z, off, amax=True)
+        gs, am = host(gs), host(am)
+        assert gs[0] == 1.0 and am[0] == 0.0 and gs[1] == 1.0 and am[1] == 0.0
+        assert am[2] > 0 and gs[2] == np.float32(am[2]) / np.float32(2688.0)
 
 
 # ---- dequantize -----------------------------------------------------------------------

@@ -10,6 +10,8 @@ fails. The committed oracle is never modified.
 import os
 import subprocess
 
+import numpy as np
+
 import pytest
 
 import oracle
@@ -33,12 +35,16 @@ MUTANTS = {
     "exp_sign": ("double y = g * u / (1.0 + exp(-g));", "double y = g * u / (1.0 + exp(g));"),
     "no_six_clamp": ("v = 2.0f * fminf(fabsf(s), 6.0f);", "v = fminf(2.0f * fabsf(s), 13.0f);"),
     "t7_toward_zero": ("{0, 1, 2, 3, 4, 4, 5, 6, 6, 6, 6, 7, 7}", "{0, 1, 2, 3, 4, 4, 5, 5, 6, 6, 6, 7, 7}"),
+    "amax_skips_last_row": ("for (int64_t r = offsets[e]; r < offsets[e + 1]; ++r)",
+                            "for (int64_t r = offsets[e]; r + 1 < offsets[e + 1]; ++r)"),
+    "amax_signed": ("float a = fabsf(y[r * cols + c]);", "float a = y[r * cols + c];"),
 }
 
 FAST_PINS = [P.pin_page_facts, P.pin_fp8_decode_vs_torch, P.pin_fp8_saturation,
              P.pin_fp8_roundtrip, P.pin_e2m1_format, P.pin_e2m1_table,
              P.pin_swiglu_vs_torch, P.pin_swiglu_closed_forms,
              P.pin_quantize_vs_twin, P.pin_dequant_closed_form,
+             P.pin_group_amax, P.pin_expert_global_scale,
              lambda: P.pin_fp8_encode_vs_torch(step=997)]
 
 
@@ -67,3 +73,24 @@ def test_pins_catch_mutant(name, tmp_path, monkeypatch):
         assert caught, "no pin caught mutant " + name
     finally:
         monkeypatch.setattr(oracle, "_LIB", real)
+
+
+# The global-scale step lives in the oracle's Python front end: plant its
+# mistakes by swapping in a broken function.
+PY_MUTANTS = {
+    "gs_6x488": lambda a: np.where(a > 0, np.asarray(a, np.float32) / np.float32(6 * 488.0),
+                                   np.float32(1.0)).astype(np.float32),
+    "gs_times_2688": lambda a: np.where(a > 0, np.asarray(a, np.float32) * np.float32(2688.0),
+                                        np.float32(1.0)).astype(np.float32),
+    "gs_zero_for_empty": lambda a: (np.asarray(a, np.float32) / np.float32(2688.0)).astype(np.float32),
+    "gs_reciprocal_multiply": lambda a: np.where(
+        a > 0, np.asarray(a, np.float32) * (np.float32(1.0) / np.float32(2688.0)),
+        np.float32(1.0)).astype(np.float32),
+}
+
+
+@pytest.mark.parametrize("name", sorted(PY_MUTANTS))
+def test_pins_catch_global_scale_mutant(name, monkeypatch):
+    monkeypatch.setattr(oracle, "expert_global_scale", PY_MUTANTS[name])
+    with pytest.raises(AssertionError):
+        P.pin_expert_global_scale()

@@ -236,9 +236,55 @@ def pin_dequant_closed_form():
                 assert out[r, c] == float(want), (r, c, nib, scales[r, 0], gs)
 
 
+def pin_group_amax():
+    """Per-expert max |y| against numpy's own reduction over each expert's
+    rows, with empty experts (amax 0) and each expert's extreme value planted
+    on its first or last row and column, negative."""
+    rng = np.random.default_rng(41)
+    rows, cols = 300, 48
+    y = (rng.standard_normal((rows, cols)) * 10.0 ** rng.uniform(-3, 3, (rows, 1))).astype(np.float32)
+    offsets = np.array([0, 0, 1, 57, 57, 120, 299, 300, 300], np.int32)
+    for e in range(offsets.size - 1):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi > lo:
+            r, c = (hi - 1, cols - 1) if e % 2 else (lo, 0)
+            y[r, c] = np.float32(-1.0e4 * (e + 1))
+    got = oracle.group_amax(y, offsets)
+    for e in range(offsets.size - 1):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        want = np.float32(np.max(np.abs(y[lo:hi]))) if hi > lo else np.float32(0.0)
+        assert got[e] == want, (e, got[e], want)
+
+
+def pin_expert_global_scale():
+    """gs = RN32(amax / (6 * 448)): exact powers of two, 1.0 for an all-zero
+    expert, the nearest binary32 to the exact rational quotient, and the
+    defining property that the expert's largest block gets scale byte 0x7e
+    (the FP8 maximum 448)."""
+    from fractions import Fraction as F
+    ks = np.arange(-20, 21)
+    amax = (2688.0 * 2.0 ** ks).astype(np.float32)
+    assert np.array_equal(oracle.expert_global_scale(amax), (2.0 ** ks).astype(np.float32))
+    assert oracle.expert_global_scale(np.zeros(3, np.float32)).tolist() == [1.0, 1.0, 1.0]
+    rng = np.random.default_rng(43)
+    a = (10.0 ** rng.uniform(-6, 6, 400)).astype(np.float32)
+    gs = oracle.expert_global_scale(a)
+    for ai, gi in zip(a, gs):
+        q = F(float(ai)) / 2688
+        err = abs(F(float(gi)) - q)
+        for nb in (np.nextafter(gi, np.float32(np.inf)), np.nextafter(gi, np.float32(0))):
+            assert err < abs(F(float(nb)) - q), (ai, gi)
+    for ai, gi in zip(a[:100], gs[:100]):
+        x = np.zeros(16, np.float32)
+        x[5] = -ai
+        _, sf, _, _ = oracle.quantize_block(x, float(gi))
+        assert sf == 0x7E, (ai, gi, hex(sf))
+
+
 ALL_PINS = [pin_page_facts, pin_fp8_decode_vs_torch, pin_fp8_saturation,
             pin_fp8_roundtrip, pin_e2m1_format, pin_e2m1_table, pin_swiglu_vs_torch,
-            pin_swiglu_closed_forms, pin_quantize_vs_twin, pin_dequant_closed_form]
+            pin_swiglu_closed_forms, pin_quantize_vs_twin, pin_dequant_closed_form,
+            pin_group_amax, pin_expert_global_scale]
 
 
 # ---- tests --------------------------------------------------------------------
