@@ -3,6 +3,8 @@ profiles/.
 
   stats: kernel-trace statistics (calls, average/min/max duration per kernel)
          from a `rocprofv3 --kernel-trace --stats -f csv` run.
+  counters: the per-dispatch average of every counter in a `--pmc` run, for
+         one kernel.
   pmc:   HBM traffic of one kernel from two counter runs
          (`--pmc FETCH_SIZE`, then `--pmc WRITE_SIZE`, both in KiB per
          dispatch), each scaled by what the same counter reads for the
@@ -10,8 +12,10 @@ profiles/.
 
 Usage:
   python -m moe_swiglu_epilogue_amd.rocprof_summary stats DIR OUT.txt --cmd "..."
+  python -m moe_swiglu_epilogue_amd.rocprof_summary counters DIR [DIR ...] --out OUT.txt \\
+      --kernel K --cmd "..."
   python -m moe_swiglu_epilogue_amd.rocprof_summary pmc FETCH_DIR WRITE_DIR OUT \\
-      --kernel swiglu_nvfp4_kernel --calib calib_copy_kernel --calib-bytes N \\
+      --kernel K --calib calib_copy_kernel --calib-bytes-each-way N \\
       --alg-bytes N --source-sha256 H --cmd "..."
 """
 import argparse
@@ -89,8 +93,8 @@ def pmc(args):
     kw, nkw = avg(write, args.kernel)
     cf, _ = avg(fetch, args.calib)
     cw, _ = avg(write, args.calib)
-    f_scale = args.calib_bytes / (cf * 1024.0)
-    w_scale = args.calib_bytes / (cw * 1024.0)
+    f_scale = args.calib_bytes_each_way / (cf * 1024.0)
+    w_scale = args.calib_bytes_each_way / (cw * 1024.0)
     fetch_b = kf * 1024.0 * f_scale
     write_b = kw * 1024.0 * w_scale
     out = {
@@ -100,7 +104,7 @@ def pmc(args):
         "fetch_kib_per_dispatch": round(kf, 1),
         "write_kib_per_dispatch": round(kw, 1),
         "calib_kernel": args.calib,
-        "calib_bytes_read_and_written": args.calib_bytes,
+        "calib_bytes_read_and_written_each": args.calib_bytes_each_way,
         "calib_fetch_kib": round(cf, 1), "calib_write_kib": round(cw, 1),
         "fetch_scale": round(f_scale, 5), "write_scale": round(w_scale, 5),
         "traffic_bytes_per_launch": int(round(fetch_b + write_b)),
@@ -119,6 +123,26 @@ def pmc(args):
     print("\n".join(text))
 
 
+def counters(args):
+    per = {}
+    for d in args.dirs:
+        for path in _one(d, "counter_collection.csv"):
+            with open(path) as f:
+                for r in csv.DictReader(f):
+                    if _short(r["Kernel_Name"]).startswith(args.kernel):
+                        per.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    if not per:
+        raise SystemExit("kernel %s not found" % args.kernel)
+    lines = ["# rocprofv3 counters: %s (average per dispatch)" % args.kernel, "", "commands:",
+             "  " + args.cmd, "", "%-28s %10s %18s" % ("counter", "dispatches", "average")]
+    for name in sorted(per):
+        lines.append("%-28s %10d %18.2f" % (name, len(per[name]), statistics.mean(per[name])))
+    text = "\n".join(lines) + "\n"
+    with open(args.out, "w") as f:
+        f.write(text)
+    print(text)
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="what", required=True)
@@ -132,12 +156,18 @@ def main(argv=None):
     b.add_argument("out", help="output path without extension (.json and .txt are written)")
     b.add_argument("--kernel", required=True)
     b.add_argument("--calib", required=True)
-    b.add_argument("--calib-bytes", type=int, required=True)
+    b.add_argument("--calib-bytes-each-way", type=int, required=True,
+                   help="bytes the copy kernel reads per dispatch (it writes as many)")
     b.add_argument("--alg-bytes", type=int, required=True)
     b.add_argument("--source-sha256", required=True)
     b.add_argument("--cmd", required=True)
+    c = sub.add_parser("counters")
+    c.add_argument("dirs", nargs="+")
+    c.add_argument("--out", required=True)
+    c.add_argument("--kernel", required=True)
+    c.add_argument("--cmd", required=True)
     args = ap.parse_args(argv)
-    (stats if args.what == "stats" else pmc)(args)
+    {"stats": stats, "pmc": pmc, "counters": counters}[args.what](args)
 
 
 if __name__ == "__main__":
