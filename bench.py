@@ -11,6 +11,7 @@ Prints ONE JSON line with the throughput (HBM GB/s over the algorithmic bytes,
 4.5625 B per output element), the roofline of the fused kernel, the CPU
 oracle's throughput on the host cores, and secondary figures: the standalone
 quantize, the dequantize and the global-scale pre-pass on the same tensor;
+the two-pass ablation (compact BF16 SwiGLU, then the standalone quantize);
 in-repo read / copy kernels over the same input as HBM ceilings; the ragged
 256-expert workload (pre-pass, quantize with per-expert scales, dequantize);
 the decode-shaped workload over 8 rotating buffer sets.
@@ -42,8 +43,8 @@ PMC_SUMMARY = os.path.join(ROOT, "profiles", "fused_quantize_kernel_prefill_pmc.
 # persistent grid of 6 workgroups per CU, the copy with one 4 KB tile per wave)
 CALIB_READ_BLOCKS = (1024, 1536, 8192, 49152)
 CALIB_COPY_BLOCKS = (512, 8192, 49152)
-SECONDARY = ("nvfp4_quantize", "nvfp4_dequantize", "global_scale", "calib_read", "calib_copy",
-             "ragged", "decode")
+SECONDARY = ("nvfp4_quantize", "nvfp4_dequantize", "global_scale", "two_pass", "calib_read",
+             "calib_copy", "ragged", "decode")
 
 
 def load_calib():
@@ -171,6 +172,9 @@ def cpu_baseline(x):
     }
 
 
+kern_ms_headline = []
+
+
 def secondary_figures(M, W, x, packed, scales, args, dev):
     """Other kernels and the other workload shapes (not the headline)."""
     import numpy as np
@@ -199,6 +203,25 @@ def secondary_figures(M, W, x, packed, scales, args, dev):
             "swiglu_nvfp4_global_scale prefill", lambda: M.swiglu_nvfp4_global_scale(x, gs=gsb),
             ROWS * INTER * 4.0, ROWS * INTER, st, ms,
             {"shape": [ROWS, 2 * INTER], "note": "per-tensor amax pre-pass; 3 launches"})
+    if "two_pass" in want:
+        # the ablation that prices the fusion: SwiGLU to compact BF16 (4 B read,
+        # 2 B written per element), then the standalone quantize of it
+        # (2 + 0.5625 B): 8.5625 B per element for the same outputs
+        yb = torch.empty((ROWS, INTER), dtype=torch.bfloat16, device=dev)
+        pq, sq = torch.empty_like(packed), torch.empty_like(scales)
+        sec["swiglu_bf16"] = measure(
+            "swiglu_bf16 prefill", lambda: M.swiglu_bf16(x, out=yb), ROWS * INTER * 6.0,
+            ROWS * INTER, st, ms, {"shape": [ROWS, 2 * INTER]})
+
+        def two_pass():
+            M.swiglu_bf16(x, out=yb)
+            M.nvfp4_quantize(yb, packed=pq, scales=sq)
+        tp = measure("two-pass (swiglu_bf16 + nvfp4_quantize)", two_pass,
+                     ROWS * INTER * 8.5625, ROWS * INTER, st, ms,
+                     {"note": "GB_s over the two passes' own 8.5625 B per element"})
+        tp["fused_speedup"] = round(tp["ms"] / kern_ms_headline[0], 3) if kern_ms_headline else None
+        sec["two_pass"] = tp
+        del yb, pq, sq
     # in-repo calibration kernels over the same 805 MB input: HBM ceilings
     nbytes = x.numel() * 2
     stream = torch.cuda.current_stream().cuda_stream
@@ -318,6 +341,7 @@ def main():
     print("[bench] timing %d steps after %d warmup (%.0f ms settle)"
           % (args.steps, args.warmup, args.settle_ms), file=sys.stderr, flush=True)
     wall, kern_ms, per = time_launches(step, args.steps, args.warmup, args.settle_ms)
+    kern_ms_headline.append(kern_ms)
     ms_per_step = wall * 1e3 / args.steps
     value = ALG_BYTES / (wall / args.steps) / 1e9
     achieved = ALG_BYTES / (kern_ms / 1e3) / 1e9

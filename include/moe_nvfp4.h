@@ -33,7 +33,8 @@
  *   packed        [rows][cols/2] bytes, contiguous (pitch cols/2).
  *   scales        [rows][cols/16] bytes, contiguous (pitch cols/16).
  *   swiglu_out    [rows][inter] FP32, contiguous (optional debug output).
- *   out           [rows][cols] FP32, contiguous.
+ *   out           [rows][cols] FP32, contiguous (dequantize); for
+ *                 swiglu_bf16, [rows][ld_out] BF16.
  *
  * Global scales and experts
  *   gs == NULL                      every row uses 1.0.
@@ -166,6 +167,22 @@ nvfp4_status_t swiglu_nvfp4_global_scale(const uint16_t *gate_up, int64_t rows,
                                          const int32_t *expert_offsets,
                                          int32_t num_experts, float *amax,
                                          float *gs, hipStream_t stream);
+
+/*
+ * Compact SwiGLU output: the first pass of the two-pass variant, in which
+ * the SwiGLU result is written as BF16 and then quantized by nvfp4_quantize.
+ * Page: "NVFP4-1.1_APPROACH.md", "Revised approach: Compact SwiGLU output"
+ * (the target flow: L1 output as compact BF16 SwiGLU values, then the
+ * standalone GPU quantize). Reads gate_up[rows][2*inter] (pitch ld_in,
+ * interleaved as for swiglu_nvfp4_quantize), computes y = silu(gate) * up in
+ * FP32 exactly as swiglu_nvfp4_quantize does, rounds it to BF16 (round to
+ * nearest, ties to even) and writes out[rows][inter] (pitch ld_out
+ * elements). out must be 16-byte aligned with a pitch of a multiple of
+ * 8 elements; inter % 16 == 0. One kernel; rows == 0 is a no-op.
+ */
+nvfp4_status_t swiglu_bf16(const uint16_t *gate_up, int64_t rows, int64_t inter,
+                           int64_t ld_in, uint16_t *out, int64_t ld_out,
+                           hipStream_t stream);
 
 /* Static English text for a status code (never NULL). */
 const char *nvfp4_status_string(nvfp4_status_t status);

@@ -10,7 +10,7 @@ call does, and raises if it is missing.
 import importlib
 
 __all__ = ["nvfp4_quantize", "swiglu_nvfp4_quantize", "nvfp4_dequantize",
-           "nvfp4_global_scale", "swiglu_nvfp4_global_scale",
+           "nvfp4_global_scale", "swiglu_nvfp4_global_scale", "swiglu_bf16",
            "Nvfp4Error", "library_path"]
 
 

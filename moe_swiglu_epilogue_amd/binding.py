@@ -20,7 +20,8 @@ STATUS = {0: "NVFP4_SUCCESS", 1: "NVFP4_ERROR_INVALID_VALUE",
           4: "NVFP4_ERROR_LAUNCH"}
 
 EXPORTS = ("nvfp4_quantize", "swiglu_nvfp4_quantize", "nvfp4_dequantize",
-           "nvfp4_global_scale", "swiglu_nvfp4_global_scale", "nvfp4_status_string")
+           "nvfp4_global_scale", "swiglu_nvfp4_global_scale", "swiglu_bf16",
+           "nvfp4_status_string")
 
 _LIB = None
 _vp = C.c_void_p
@@ -57,6 +58,8 @@ def _lib():
         for fn in (L.nvfp4_global_scale, L.swiglu_nvfp4_global_scale):
             fn.argtypes = [_vp, _i64, _i64, _i64, _vp, _i32, _vp, _vp, _vp]
             fn.restype = C.c_int
+        L.swiglu_bf16.argtypes = [_vp, _i64, _i64, _i64, _vp, _i64, _vp]
+        L.swiglu_bf16.restype = C.c_int
         L.nvfp4_status_string.argtypes = [C.c_int]
         L.nvfp4_status_string.restype = C.c_char_p
         _LIB = L
@@ -231,3 +234,22 @@ def swiglu_nvfp4_global_scale(gate_up: torch.Tensor, expert_offsets: torch.Tenso
         raise ValueError("gate_up must have an even number of columns")
     return _global_scale(_lib().swiglu_nvfp4_global_scale, "swiglu_nvfp4_global_scale", x,
                          x.shape[1] // 2, expert_offsets, amax, gs, stream)
+
+
+def swiglu_bf16(gate_up: torch.Tensor, *, out: torch.Tensor | None = None, stream=None):
+    """Interleaved BF16 [rows, 2I] -> compact BF16 [rows, I]: silu(gate) * up as the
+    fused kernel computes it, rounded to BF16 (the first pass of the two-pass
+    variant; nvfp4_quantize is the second). ``out`` may be a row-pitched view."""
+    x = _bf16_matrix(gate_up, "gate_up")
+    rows, two_i = x.shape
+    if two_i % 2:
+        raise ValueError("gate_up must have an even number of columns")
+    inter = two_i // 2
+    if out is None:
+        out = torch.empty((rows, inter), dtype=torch.bfloat16, device=x.device)
+    if (out.dtype != torch.bfloat16 or out.device != x.device or tuple(out.shape) != (rows, inter)
+            or (inter > 1 and out.stride(1) != 1)):
+        raise ValueError("out must be a bfloat16 tensor of shape (rows, I) with unit column stride")
+    _call(_lib().swiglu_bf16, "swiglu_bf16", _ptr(x), rows, inter, _pitch(x), _ptr(out),
+          _pitch(out), _stream(stream))
+    return out

@@ -35,6 +35,7 @@ struct Geometry {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
@@ -382,6 +383,62 @@ __global__ __launch_bounds__(Block::kWaves * kWave) void quantize_tiles_kernel(
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 dst[i] = f32x4{y[4 * i], y[4 * i + 1], y[4 * i + 2], y[4 * i + 3]};
+        }
+    });
+}
+
+// ---------------------------------------------------------------------------
+// Compact SwiGLU output, the first pass of the two-pass variant (SwiGLU to
+// BF16, then nvfp4_quantize): y = silu(gate) * up exactly as the fused
+// kernel computes it, rounded to BF16 (round to nearest even, by
+// v_cvt_pk_bf16_f32) and written as [rows][ld_out] BF16. A lane's block is
+// 32 output bytes; the wave transposes its tile through LDS and writes it as
+// two coalesced 1 KB stores, through a buffer resource spanning the tile's
+// bytes so that a partial tile's surplus lanes are dropped.
+// ---------------------------------------------------------------------------
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
+{
+    const bf16x2 b = __builtin_convertvector(f32x2{lo, hi}, bf16x2);
+    return __builtin_bit_cast(uint32_t, b);
+}
+
+__global__ __launch_bounds__(FusedBlock::kWaves * kWave) void swiglu_bf16_kernel(
+    const uint16_t* __restrict__ in, int64_t ld_in, Geometry geo, uint16_t* __restrict__ out,
+    int64_t ld_out)
+{
+    using Block = FusedBlock;
+    constexpr int kWaves = Block::kWaves;
+    __shared__ u32x4 stage[kWaves][kStageSlots(Block::P)];
+    __shared__ float sig[nvfp4::kSigEntries];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = uniform(threadIdx.x / kWave);
+    u32x4* lds = stage[wave];
+    const int tile = blockIdx.x * kWaves + wave;
+    fill_sigma_table<Block>(sig);
+    __syncthreads();
+    if (tile >= geo.tiles)
+        return;
+    walk_tiles<Block>(in, ld_in, geo, tile, gridDim.x * kWaves, lane, lds,
+                      reinterpret_cast<const uint8_t*>(sig),
+                      [&](int, const Tile& t, int b, const float (&y)[16]) {
+        u32x4 w[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+            w[h] = u32x4{pack_bf16x2(y[8 * h], y[8 * h + 1]), pack_bf16x2(y[8 * h + 2], y[8 * h + 3]),
+                         pack_bf16x2(y[8 * h + 4], y[8 * h + 5]), pack_bf16x2(y[8 * h + 6], y[8 * h + 7])};
+        wave_lds_sync();
+        lds[lds_slot(2 * b)] = w[0];
+        lds[lds_slot(2 * b + 1)] = w[1];
+        wave_lds_sync();
+        const __amdgpu_buffer_rsrc_t rsrc =
+            buffer_over(out + (int64_t)t.row * ld_out + t.blk0 * 16, t.nblk * 32);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int k = j * kWave + lane;
+            __builtin_amdgcn_raw_buffer_store_b128(lds[lds_slot(k)], rsrc, k * 16, 0,
+                                                   kOutStorePolicy);
         }
     });
 }
@@ -781,6 +838,29 @@ nvfp4_status_t swiglu_nvfp4_global_scale(const uint16_t* gate_up, int64_t rows, 
     }
     return launch_global_scale<FusedBlock>(empty ? nullptr : &g, gate_up, ld_in, expert_offsets,
                                            num_experts, amax, gs, stream);
+}
+
+nvfp4_status_t swiglu_bf16(const uint16_t* gate_up, int64_t rows, int64_t inter, int64_t ld_in,
+                           uint16_t* out, int64_t ld_out, hipStream_t stream)
+{
+    if (rows < 0 || inter < 0 || inter > INT64_MAX / 2 || ld_in < 2 * inter || ld_out < inter)
+        return NVFP4_ERROR_INVALID_VALUE;
+    if (inter % 16 != 0)
+        return NVFP4_ERROR_UNSUPPORTED_SHAPE;
+    if (rows == 0 || inter == 0)
+        return NVFP4_SUCCESS;
+    if (!gate_up || !out)
+        return NVFP4_ERROR_INVALID_VALUE;
+    if (!aligned(gate_up, 16) || (ld_in * 2) % 16 != 0 || !aligned(out, 16) ||
+        (ld_out * 2) % 16 != 0)
+        return NVFP4_ERROR_MISALIGNED;
+    Geometry g;
+    nvfp4_status_t st = make_geometry(rows, inter, g);
+    if (st != NVFP4_SUCCESS)
+        return st;
+    hipLaunchKernelGGL(swiglu_bf16_kernel, persistent_grid_for<FusedBlock>(g),
+                       dim3(FusedBlock::kWaves * kWave), 0, stream, gate_up, ld_in, g, out, ld_out);
+    return launched();
 }
 
 const char* nvfp4_status_string(nvfp4_status_t status)

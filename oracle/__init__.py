@@ -51,6 +51,8 @@ def lib():
         L.oracle_quantize_block.restype = None
         L.oracle_fp8_encode_array.argtypes = [_f32p, _i64, _u8p]
         L.oracle_swiglu_rows.argtypes = [_u16p, _i64, _i64, _i64, _f32p]
+        L.oracle_swiglu_bf16_rows.argtypes = [_u16p, _i64, _i64, _i64, _u16p]
+        L.oracle_f32_to_bf16_array.argtypes = [_f32p, _i64, _u16p]
         L.oracle_quantize_f32_rows.argtypes = [_f32p, _i64, _i64, _i64, _f32p,
                                                _u8p, _u8p, _f32p, _f32p]
         L.oracle_quantize_bf16_rows.argtypes = [_u16p, _i64, _i64, _i64, _f32p,
@@ -149,6 +151,26 @@ def swiglu(gate_up: np.ndarray) -> np.ndarray:
     _check(lib().oracle_swiglu_rows(_p(x, _u16p), rows, inter, two_i, _p(y, _f32p)),
            "swiglu")
     return y
+
+
+def f32_to_bf16(x: np.ndarray) -> np.ndarray:
+    """FP32 values -> BF16 bit patterns (uint16), round to nearest even."""
+    a = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(a.shape, np.uint16)
+    _check(lib().oracle_f32_to_bf16_array(_p(a, _f32p), a.size, _p(out, _u16p)), "f32_to_bf16")
+    return out
+
+
+def swiglu_bf16(gate_up: np.ndarray) -> np.ndarray:
+    """Interleaved BF16 [rows][2I] -> compact BF16 [rows][I] (bit patterns):
+    the SwiGLU values rounded to BF16, the first pass of the two-pass variant."""
+    x = np.ascontiguousarray(gate_up, dtype=np.uint16)
+    rows, two_i = x.shape
+    inter = two_i // 2
+    out = np.empty((rows, inter), np.uint16)
+    _check(lib().oracle_swiglu_bf16_rows(_p(x, _u16p), rows, inter, two_i, _p(out, _u16p)),
+           "swiglu_bf16")
+    return out
 
 
 def quantize_f32(x: np.ndarray, gs_rows=None, diag: bool = False):

@@ -19,6 +19,7 @@
 #include "nvfp4_oracle.h"
 
 #include <math.h>
+#include <stdlib.h>
 #include <string.h>
 #ifdef _OPENMP
 #include <omp.h>
@@ -35,6 +36,39 @@ float oracle_bf16_to_f32(uint16_t bits)
     float f;
     memcpy(&f, &w, sizeof f);
     return f;
+}
+
+/* ------------------------------------------------------------------------
+ * FP32 -> BF16, round to nearest, ties to even. [APPROACH] "Revised
+ * approach: Compact SwiGLU output": the target flow writes the SwiGLU
+ * result as compact BF16 and quantizes that. BF16 has the binary32
+ * exponent range and 8 significant bits for normal values (|x| >= 2^-126);
+ * below 2^-126 its values are the multiples of 2^-133. The nearest one is
+ * found by rounding the scaled magnitude to an integer with rint (ties to
+ * even in the default rounding mode); results of 2^128 or more are
+ * infinite. NaN becomes the quiet NaN with the input's sign.
+ * ---------------------------------------------------------------------- */
+uint16_t oracle_f32_to_bf16(float x)
+{
+    uint32_t w;
+    memcpy(&w, &x, sizeof w);
+    const uint16_t sign = (uint16_t)((w >> 16) & 0x8000u);
+    if (isnan(x))
+        return (uint16_t)(sign | 0x7fc0u);
+    if (isinf(x) || x == 0.0f)
+        return (uint16_t)(w >> 16);             /* exact */
+    double a = fabs((double)x), q;
+    if (a >= ldexp(1.0, -126)) {
+        int e;
+        double m = frexp(a, &e);                /* a = m * 2^e, m in [0.5, 1) */
+        q = ldexp(rint(ldexp(m, 8)), e - 8);    /* 8 significant bits */
+    } else {
+        q = ldexp(rint(ldexp(a, 133)), -133);   /* multiples of 2^-133 */
+    }
+    float r = (float)q;                         /* exact, or inf for q >= 2^128 */
+    uint32_t rw;
+    memcpy(&rw, &r, sizeof rw);
+    return (uint16_t)(sign | (rw >> 16));
 }
 
 /* ------------------------------------------------------------------------
@@ -228,6 +262,47 @@ int oracle_swiglu_rows(const uint16_t *in, int64_t rows, int64_t inter,
             y[r * inter + j] = oracle_swiglu(g, u);
         }
     }
+    return 0;
+}
+
+/* The first pass of the two-pass variant ([APPROACH] "Revised approach:
+ * Compact SwiGLU output", target flow): the SwiGLU of the interleaved input
+ * rounded to BF16, written as a compact [rows][inter] BF16 tensor. */
+int oracle_swiglu_bf16_rows(const uint16_t *in, int64_t rows, int64_t inter,
+                            int64_t ld_in, uint16_t *out)
+{
+    if (rows < 0 || inter < 0 || inter % 8 != 0 || ld_in < 2 * inter)
+        return 1;
+    if (rows == 0 || inter == 0)
+        return 0;
+    if (!in || !out)
+        return 1;
+    int bad = 0;
+#pragma omp parallel reduction(|: bad)
+    {
+        float *y = (float *)malloc((size_t)inter * sizeof(float));
+        if (!y)
+            bad = 1;
+#pragma omp for schedule(static)
+        for (int64_t r = 0; r < rows; ++r) {
+            if (!y)
+                continue;
+            oracle_swiglu_rows(in + r * ld_in, 1, inter, ld_in, y);   /* FP32 SwiGLU of row r */
+            for (int64_t j = 0; j < inter; ++j)
+                out[r * inter + j] = oracle_f32_to_bf16(y[j]);
+        }
+        free(y);
+    }
+    return bad;
+}
+
+int oracle_f32_to_bf16_array(const float *x, int64_t n, uint16_t *out)
+{
+    if (n < 0 || (n > 0 && (!x || !out)))
+        return 1;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = oracle_f32_to_bf16(x[i]);
     return 0;
 }
 

@@ -30,6 +30,7 @@ extern "C" {
 /* ---- scalar primitives ------------------------------------------------ */
 float   oracle_bf16_to_f32(uint16_t bits);
 float   oracle_swiglu(float gate, float up);
+uint16_t oracle_f32_to_bf16(float x);
 uint8_t oracle_fp8_e4m3_encode(float v);
 float   oracle_fp8_e4m3_decode(uint8_t code);
 int     oracle_e2m1_index(int half_step);
@@ -45,6 +46,10 @@ int oracle_fp8_encode_array(const float *v, int64_t n, uint8_t *out);
 
 int oracle_swiglu_rows(const uint16_t *in, int64_t rows, int64_t inter,
                        int64_t ld_in, float *y /* rows x inter */);
+
+int oracle_swiglu_bf16_rows(const uint16_t *in, int64_t rows, int64_t inter,
+                            int64_t ld_in, uint16_t *out /* rows x inter BF16 */);
+int oracle_f32_to_bf16_array(const float *x, int64_t n, uint16_t *out);
 
 int oracle_quantize_f32_rows(const float *x, int64_t rows, int64_t cols,
                              int64_t ld_x, const float *gs_rows,

@@ -39,7 +39,8 @@ def _exported(lib_path):
 def test_header_declares_the_entry_points():
     assert _declared() == sorted(["nvfp4_quantize", "swiglu_nvfp4_quantize",
                                   "nvfp4_dequantize", "nvfp4_global_scale",
-                                  "swiglu_nvfp4_global_scale", "nvfp4_status_string"])
+                                  "swiglu_nvfp4_global_scale", "swiglu_bf16",
+                                  "nvfp4_status_string"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -166,6 +167,25 @@ def test_global_scale_validation(lib, fused):
     assert gsc(lib, fused, rows=2**31, cols=16, ld=32 if fused else 16) == SHAPE
 
 
+def sb(lib, x=A16, rows=4, inter=32, ld=64, out=A16, ld_out=32):
+    return lib.swiglu_bf16(x, rows, inter, ld, out, ld_out, None)
+
+
+def test_swiglu_bf16_validation(lib):
+    assert sb(lib, rows=-1) == INVALID
+    assert sb(lib, inter=8, ld=16, ld_out=8) == SHAPE
+    assert sb(lib, ld=63) == INVALID
+    assert sb(lib, ld_out=31) == INVALID
+    assert sb(lib, x=None) == INVALID
+    assert sb(lib, out=None) == INVALID
+    assert sb(lib, x=A16 + 8) == MISALIGNED
+    assert sb(lib, out=A16 + 8) == MISALIGNED
+    assert sb(lib, ld_out=36) == MISALIGNED      # 72-byte output pitch
+    assert sb(lib, ld=68) == MISALIGNED
+    assert sb(lib, rows=2**31, inter=16, ld=32, ld_out=16) == SHAPE
+    assert sb(lib, rows=0, x=None, out=None) == OK
+
+
 def test_binding_rejects_host_tensors():
     import moe_swiglu_epilogue_amd as M
     x = torch.zeros(4, 32, dtype=torch.bfloat16)
@@ -179,3 +199,5 @@ def test_binding_rejects_host_tensors():
         M.nvfp4_global_scale(x)
     with pytest.raises(TypeError):
         M.swiglu_nvfp4_global_scale(torch.zeros(4, 64, dtype=torch.bfloat16))
+    with pytest.raises(TypeError):
+        M.swiglu_bf16(torch.zeros(4, 64, dtype=torch.bfloat16))

@@ -1,12 +1,14 @@
 """Code generation checks on the gfx950 ISA of the library (CPU only: hipcc
 cross-compiles the device code to assembly).
 
-* The pipelined quantize loop must never wait for its own output stores:
+* The pipelined store loops (quantize, compact SwiGLU) must never wait for
+  their own output stores:
   on gfx9 the vmcnt counter covers stores as well as loads, so the loop
   that holds a wide-store quantize kernel's output stores (found from its
   backward branch) contains no `s_waitcnt vmcnt(0)`. A second one means the compiler merged
   the prologue's LDS staging into the loop and every pass drains the stores
   (measured: 5% slower on the prefill shape).
+* The compact SwiGLU pass rounds with v_cvt_pk_bf16_f32 (8 per lane block).
 * No scalar-memory writes or atomics anywhere in the device code: stores and
   atomics go through the vector memory path only.
 """
@@ -58,10 +60,11 @@ def store_loops(body):
 
 
 def loop_waits_for_stores(isa):
-    """Names of wide-store quantize kernels whose store loop has a vmcnt(0)."""
+    """Names of the pipelined store kernels (wide-store quantize, compact
+    SwiGLU) whose store loop has a vmcnt(0)."""
     ks = {n: body for n, body in _kernels(isa).items()
-          if "quantize_tiles_kernel" in n and "Lb1E" in n}
-    assert len(ks) == 2, sorted(ks)
+          if ("quantize_tiles_kernel" in n and "Lb1E" in n) or "swiglu_bf16_kernel" in n}
+    assert len(ks) == 3, sorted(ks)
     bad = []
     for name, body in ks.items():
         loops = store_loops(body)
@@ -73,6 +76,11 @@ def loop_waits_for_stores(isa):
 
 def test_wide_quantize_loops_do_not_wait_for_stores(isa):
     assert loop_waits_for_stores(isa) == []
+
+
+def test_bf16_rounding_is_the_hardware_convert(isa):
+    body = next(b for n, b in _kernels(isa).items() if "swiglu_bf16_kernel" in n)
+    assert sum(l.startswith("v_cvt_pk_bf16_f32") for l in body) == 8
 
 
 def test_no_scalar_memory_writes(isa):

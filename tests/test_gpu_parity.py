@@ -312,6 +312,74 @@ def test_global_scale_empty_and_zero(M):
         assert am[2] > 0 and gs[2] == np.float32(am[2]) / np.float32(2688.0)
 
 
+# ---- compact SwiGLU pass (two-pass variant) -------------------------------------------
+def bf16_check(M, x, what, ld_out=None, quantize_cols=None):
+    rows, inter = x.shape[0], x.shape[1] // 2
+    xt = dev_bf16(x)
+    if ld_out is None:
+        buf = None
+        out = torch.empty((rows, inter), dtype=torch.bfloat16, device="cuda")
+    else:
+        buf = torch.full((rows, ld_out), float("nan"), dtype=torch.bfloat16, device="cuda")
+        out = buf[:, :inter]
+    say("swiglu_bf16", what, x.shape, "ld_out", ld_out)
+    M.swiglu_bf16(xt, out=out)
+    got = host(out.contiguous().view(torch.int16)).view(np.uint16)
+    rep = P.bf16_report(got, oracle.swiglu_bf16(x), oracle.swiglu(x))
+    say(what, rep)
+    assert rep.ok(), "%s: %s" % (what, rep)
+    if buf is not None:     # the pitch padding is untouched
+        pad = host(buf[:, inter:].contiguous().view(torch.int16)).view(np.uint16)
+        assert np.all(pad == 0x7FC0), "padding written"
+    # second pass: the standalone quantize of the GPU's own BF16 values, bit-exact
+    # (over the first quantize_cols columns: infinite values are outside the
+    # quantizer's contract)
+    qc = inter if quantize_cols is None else quantize_cols
+    p, s = M.nvfp4_quantize(out[:, :qc])
+    rp, rs = oracle.quantize_bf16(np.ascontiguousarray(got[:, :qc]))
+    P.assert_bytes_equal(what + " two-pass scales", host(s), rs)
+    P.assert_bytes_equal(what + " two-pass packed", host(p), rp)
+    return got
+
+
+def test_swiglu_bf16_exact_products(M):
+    """Gates >= 256 make sigma exactly 1 in FP32, so y = gate * up is the exact
+    product of two BF16 values (16 significant bits): the BF16 rounding of
+    every pair of significands is checked bit for bit, with 3132 exact ties,
+    mantissa carries, both signs and the overflow to inf."""
+    i = np.arange(128)
+    gate = (256.0 * (1 + i / 128.0)).reshape(-1, 1)
+    ups = []
+    for e in (0, -3, 9, -120, 100, 119):
+        for sign in (1.0, -1.0):
+            ups.append(sign * (1 + i / 128.0) * 2.0 ** e)
+    up = np.concatenate(ups).reshape(1, -1)
+    g = np.broadcast_to(gate, (128, up.shape[1]))
+    u = np.broadcast_to(up, (128, up.shape[1]))
+    x = W.to_bf16_bits(W.interleave(g, u))
+    y = oracle.swiglu(x)
+    with np.errstate(over="ignore"):
+        exact = (g.astype(np.float64) * u.astype(np.float64)).astype(np.float32)
+    assert np.array_equal(y, exact)
+    assert ((y.view(np.uint32) & 0xFFFF) == 0x8000).sum() > 3000 and np.isinf(y).any()
+    finite = up.shape[1] - 256             # the last exponent's columns overflow
+    assert np.isfinite(y[:, :finite]).all() and np.isinf(y[:, finite:]).any()
+    got = bf16_check(M, x, "exact products", quantize_cols=finite)
+    P.assert_bytes_equal("exact products", got, oracle.swiglu_bf16(x))
+
+
+def test_swiglu_bf16_workloads(M):
+    bf16_check(M, W.fused_small().x, "fused_small 512x4096")
+    bf16_check(M, W.decode().x, "decode 8192x4096")
+
+
+@pytest.mark.parametrize("rows,inter,seed,scale,ld_out", [
+    (1, 16, 1, 1.0, None), (5, 48, 2, 30.0, 56), (33, 1040, 3, 1.0, None),
+    (130, 3072, 4, 0.01, 3136), (64, 8192, 5, 4.0, None)])
+def test_swiglu_bf16_shapes(M, rows, inter, seed, scale, ld_out):
+    bf16_check(M, W.random_fused(rows, inter, seed, scale), "random %dx%d" % (rows, inter), ld_out)
+
+
 # ---- dequantize -----------------------------------------------------------------------
 @pytest.mark.parametrize("rows,cols,seed", [(1, 16, 1), (9, 1040, 2), (513, 4096, 3)])
 def test_dequant_bit_exact(M, rows, cols, seed):

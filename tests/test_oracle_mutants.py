@@ -38,13 +38,21 @@ MUTANTS = {
     "amax_skips_last_row": ("for (int64_t r = offsets[e]; r < offsets[e + 1]; ++r)",
                             "for (int64_t r = offsets[e]; r + 1 < offsets[e + 1]; ++r)"),
     "amax_signed": ("float a = fabsf(y[r * cols + c]);", "float a = y[r * cols + c];"),
+    "bf16_half_up": ("q = ldexp(rint(ldexp(m, 8)), e - 8);", "q = ldexp(floor(ldexp(m, 8) + 0.5), e - 8);"),
+    "bf16_truncate": ("q = ldexp(rint(ldexp(m, 8)), e - 8);", "q = ldexp(floor(ldexp(m, 8)), e - 8);"),
+    "bf16_7_bits": ("q = ldexp(rint(ldexp(m, 8)), e - 8);", "q = ldexp(rint(ldexp(m, 7)), e - 7);"),
+    "bf16_subnormal_8_bits": ("q = ldexp(rint(ldexp(a, 133)), -133);",
+                              "{ int e2; double m2 = frexp(a, &e2); q = ldexp(rint(ldexp(m2, 8)), e2 - 8); }"),
+    "swiglu_bf16_shifted": ("out[r * inter + j] = oracle_f32_to_bf16(y[j]);",
+                            "out[r * inter + j] = oracle_f32_to_bf16(y[j ^ 1]);"),
 }
 
 FAST_PINS = [P.pin_page_facts, P.pin_fp8_decode_vs_torch, P.pin_fp8_saturation,
              P.pin_fp8_roundtrip, P.pin_e2m1_format, P.pin_e2m1_table,
              P.pin_swiglu_vs_torch, P.pin_swiglu_closed_forms,
              P.pin_quantize_vs_twin, P.pin_dequant_closed_form,
-             P.pin_group_amax, P.pin_expert_global_scale,
+             P.pin_group_amax, P.pin_expert_global_scale, P.pin_bf16_ties,
+             P.pin_swiglu_bf16_vs_torch, lambda: P.pin_bf16_vs_torch(step=9973),
              lambda: P.pin_fp8_encode_vs_torch(step=997)]
 
 

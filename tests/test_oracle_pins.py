@@ -281,10 +281,50 @@ def pin_expert_global_scale():
         assert sf == 0x7E, (ai, gi, hex(sf))
 
 
+def pin_bf16_vs_torch(step: int = 997, chunk: int = 1 << 24):
+    """FP32 -> BF16 rounding against PyTorch's conversion (a library routine)
+    over every step-th binary32 bit pattern (step 1: all of them)."""
+    for start in range(0, 1 << 32, chunk * step):
+        stop = min(1 << 32, start + chunk * step)
+        a = np.arange(start, stop, step, dtype=np.uint64).astype(np.uint32).view(np.float32)
+        got = oracle.f32_to_bf16(a)
+        ref = torch.from_numpy(a).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        nan = np.isnan(a)
+        assert np.all((got[nan] & 0x7FFF) > 0x7F80)
+        bad = np.nonzero((got != ref) & ~nan)[0]
+        assert bad.size == 0, ("bf16 differs from torch", a[bad[:5]], got[bad[:5]], ref[bad[:5]])
+
+
+def pin_bf16_ties():
+    """Closed form at exact ties (low 16 bits 0x8000): round to the even
+    neighbour; just above or below a tie, to the nearer one. Covers normal,
+    subnormal and the overflow to infinity."""
+    rng = np.random.default_rng(51)
+    hi = np.concatenate([rng.integers(0, 0x7F80, 20000), np.arange(0, 0x100),
+                         np.arange(0x7F00, 0x7F80)]).astype(np.uint32)
+    for sign in (0, 0x8000):
+        h = hi | sign
+        tie = ((h << 16) | 0x8000).view(np.float32)
+        want = (h + (h & 1)).astype(np.uint16)
+        assert np.array_equal(oracle.f32_to_bf16(tie), want)
+        above = ((h << 16) | 0x8001).view(np.float32)
+        assert np.array_equal(oracle.f32_to_bf16(above), (h + 1).astype(np.uint16))
+        below = ((h << 16) | 0x7FFF).view(np.float32)
+        assert np.array_equal(oracle.f32_to_bf16(below), h.astype(np.uint16))
+
+
+def pin_swiglu_bf16_vs_torch():
+    """The compact pass equals the (pinned) FP32 SwiGLU rounded by PyTorch."""
+    x = W.random_fused(37, 1040, 61, 3.0)
+    ref = torch.from_numpy(oracle.swiglu(x)).to(torch.bfloat16).view(torch.int16).numpy()
+    assert np.array_equal(oracle.swiglu_bf16(x), ref.view(np.uint16))
+
+
 ALL_PINS = [pin_page_facts, pin_fp8_decode_vs_torch, pin_fp8_saturation,
             pin_fp8_roundtrip, pin_e2m1_format, pin_e2m1_table, pin_swiglu_vs_torch,
             pin_swiglu_closed_forms, pin_quantize_vs_twin, pin_dequant_closed_form,
-            pin_group_amax, pin_expert_global_scale]
+            pin_group_amax, pin_expert_global_scale, pin_bf16_vs_torch, pin_bf16_ties,
+            pin_swiglu_bf16_vs_torch]
 
 
 # ---- tests --------------------------------------------------------------------
@@ -376,3 +416,8 @@ def test_zero_blocks_and_signs():
     x = _block_with(-0.1)
     p, _, _, _ = oracle.quantize_block(x)
     assert p[0] >> 4 == 0x8
+
+
+@pytest.mark.slow
+def test_bf16_exhaustive_vs_torch():
+    pin_bf16_vs_torch(step=1)
