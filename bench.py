@@ -86,6 +86,84 @@ def checked(rc):
         raise RuntimeError("calibration kernel returned %d" % rc)
 
 
+class GpuStateSampler:
+    """Samples the GPU's clock level, board power and temperatures from sysfs
+    (read-only) every 10 ms in a background thread while a measurement runs,
+    so that the result can be reported with the clock and power state it was
+    taken at. Nothing is pinned or changed."""
+
+    def __init__(self):
+        import glob
+        import threading
+        dev = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+        self.base = os.path.dirname(dev[0]) if dev else None
+        hw = sorted(glob.glob(os.path.join(self.base, "hwmon", "hwmon*"))) if self.base else []
+        self.hwmon = hw[0] if hw else None
+        self.samples = []
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    def _read(self, path):
+        try:
+            with open(path) as f:
+                return f.read()
+        except OSError:
+            return None
+
+    def _sample(self):
+        out = {}
+        t = self._read(os.path.join(self.base, "pp_dpm_sclk"))
+        if t:
+            cur = [l.split(":", 1)[1].strip(" *") for l in t.splitlines() if l.endswith("*")]
+            out["sclk"] = cur[0] if cur else None
+        if self.hwmon:
+            pw = self._read(os.path.join(self.hwmon, "power1_input"))
+            out["power_W"] = int(pw) / 1e6 if pw else None
+        return out
+
+    def _run(self):
+        while not self._stop.wait(0.01):
+            self.samples.append(self._sample())
+
+    def __enter__(self):
+        if self.base:
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self._thread.is_alive():
+            self._thread.join()
+
+    def report(self):
+        if not self.base:
+            return None
+        rep = {"samples": len(self.samples)}
+        levels = {}
+        for smp in self.samples:
+            if smp.get("sclk"):
+                levels[smp["sclk"]] = levels.get(smp["sclk"], 0) + 1
+        rep["sclk_level_counts"] = levels
+        pw = [smp["power_W"] for smp in self.samples if smp.get("power_W")]
+        if pw:
+            rep["power_W_min_mean_max"] = [round(min(pw), 1), round(sum(pw) / len(pw), 1),
+                                           round(max(pw), 1)]
+        mclk = self._read(os.path.join(self.base, "pp_dpm_mclk"))
+        if mclk:
+            rep["mclk"] = [l.split(":", 1)[1].strip(" *") for l in mclk.splitlines()
+                           if l.endswith("*")]
+        if self.hwmon:
+            cap = self._read(os.path.join(self.hwmon, "power1_cap"))
+            rep["power_cap_W"] = int(cap) / 1e6 if cap else None
+            for lab in sorted(os.listdir(self.hwmon)):
+                if lab.startswith("temp") and lab.endswith("_label"):
+                    name = (self._read(os.path.join(self.hwmon, lab)) or "").strip()
+                    val = self._read(os.path.join(self.hwmon, lab.replace("_label", "_input")))
+                    if name and val:
+                        rep.setdefault("temp_C_after", {})[name] = int(val) / 1e3
+        return rep
+
+
 def settle(fn, settle_ms):
     """Run fn back to back for settle_ms of wall time (untimed). Under
     sustained load the GPU's clocks need about 30 ms to reach their steady
@@ -161,14 +239,20 @@ def cpu_baseline(x):
     one = time.perf_counter() - t
     oracle.set_num_threads(threads)
     one_elem = sub.shape[0] * (sub.shape[1] // 2)
+    model = "unknown CPU"
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next(l.split(":", 1)[1].strip() for l in f if l.startswith("model name"))
+    except (OSError, StopIteration):
+        pass
     return {
         "value": round(n_elem * BYTES_PER_ELEM / med / 1e9, 3),
         "unit": "GB/s",
         "cores": threads,
         "kind": "oracle",
         "sample": "full prefill workload 65536x6144 BF16, median of 3 passes on %d threads "
-                  "(%.2f s each); 1 thread over 16384 rows: %.3f GB/s"
-                  % (threads, med, one_elem * BYTES_PER_ELEM / one / 1e9),
+                  "(%.2f s each); 1 thread over 16384 rows: %.3f GB/s; host CPU: %s"
+                  % (threads, med, one_elem * BYTES_PER_ELEM / one / 1e9, model),
     }
 
 
@@ -340,7 +424,9 @@ def main():
 
     print("[bench] timing %d steps after %d warmup (%.0f ms settle)"
           % (args.steps, args.warmup, args.settle_ms), file=sys.stderr, flush=True)
-    wall, kern_ms, per = time_launches(step, args.steps, args.warmup, args.settle_ms)
+    with GpuStateSampler() as sampler:
+        wall, kern_ms, per = time_launches(step, args.steps, args.warmup, args.settle_ms)
+    gpu_state = sampler.report()
     kern_ms_headline.append(kern_ms)
     ms_per_step = wall * 1e3 / args.steps
     value = ALG_BYTES / (wall / args.steps) / 1e9
@@ -390,6 +476,7 @@ def main():
                      "kernel_ms": round(kern_ms, 5),
                      "kernel_ms_p10_p50_p90": [round(pct(per, q), 5) for q in (0.1, 0.5, 0.9)]},
         "cpu_baseline": cpu,
+        "gpu_state": gpu_state,
         "secondary": secondary,
     }
     print(json.dumps(line), flush=True)
