@@ -184,6 +184,52 @@ nvfp4_status_t swiglu_bf16(const uint16_t *gate_up, int64_t rows, int64_t inter,
                            int64_t ld_in, uint16_t *out, int64_t ld_out,
                            hipStream_t stream);
 
+/*
+ * MoE L1 grouped GEMM with the SwiGLU + NVFP4 quantize fused into its
+ * epilogue: the L1 output never reaches memory.
+ * Page: "NVFP4-1.1_APPROACH_PART_2.md", fused-epilogue design (SiLU(gate) and
+ * SwiGLU of the FP32 accumulators in registers, two 8-wide up subtiles per
+ * FP4 block, a 128-row CTA tile holding 512 blocks) and "2026-05-28_STATUS.md"
+ * (BLOCKED row "Priority 3: NVFP4-1.1 FP4 quant in MoE epilogue").
+ *   x       [tokens][ld_x] BF16 activations, rows grouped by expert
+ *   w1      [E][2*inter][ld_w] BF16 weights: row n of expert e is GEMM
+ *           output column n (weights stored [out][in]); output columns are
+ *           interleaved [gate x8, up x8, ...] as for swiglu_nvfp4_quantize
+ *   acc[t][n] = sum_k x[t][k] * w1[e(t)][n][k] in FP32 (matrix cores); then
+ *   y = silu(acc_gate) * acc_up in FP32 and NVFP4 blocks of 16 y values as
+ *   in swiglu_nvfp4_quantize (gs per expert, or NULL for 1.0); writes
+ *   packed[tokens][inter/2], scales[tokens][inter/16] and, if swiglu_out is
+ *   not NULL, y [tokens][inter] FP32.
+ * expert_offsets: as above (NULL: one expert, w1[0], owns every row);
+ * num_experts <= 1024. Shapes: hidden % 64 == 0, inter % 64 == 0, ld_x and
+ * ld_w >= hidden and multiples of 8; x and w1 16-byte aligned. One kernel.
+ * hidden == 0 is NVFP4_ERROR_UNSUPPORTED_SHAPE; tokens == 0 or inter == 0
+ * is a no-op.
+ */
+nvfp4_status_t moe_l1_gemm_swiglu_nvfp4(const uint16_t *x, const uint16_t *w1,
+                                        int64_t tokens, int64_t hidden,
+                                        int64_t inter, int64_t ld_x, int64_t ld_w,
+                                        const int32_t *expert_offsets,
+                                        int32_t num_experts, const float *gs,
+                                        uint8_t *packed, uint8_t *scales,
+                                        float *swiglu_out, hipStream_t stream);
+
+/*
+ * The same grouped GEMM with a plain epilogue: the L1 output rounded to BF16
+ * (round to nearest even), out[tokens][ld_out] with n columns (n = 2*inter in
+ * the interleaved layout; n % 128 == 0, ld_out >= n, multiple of 8, out
+ * 16-byte aligned). This is the producer of the unfused flow
+ * (moe_l1_gemm_bf16, then swiglu_nvfp4_quantize), kept to measure what the
+ * fusion saves. Page: "NVFP4-1.1_APPROACH.md", "Revised approach" (current
+ * flow: L1 GEMM -> BF16 interleaved -> quantize).
+ */
+nvfp4_status_t moe_l1_gemm_bf16(const uint16_t *x, const uint16_t *w1,
+                                int64_t tokens, int64_t hidden, int64_t n,
+                                int64_t ld_x, int64_t ld_w,
+                                const int32_t *expert_offsets,
+                                int32_t num_experts, uint16_t *out,
+                                int64_t ld_out, hipStream_t stream);
+
 /* Static English text for a status code (never NULL). */
 const char *nvfp4_status_string(nvfp4_status_t status);
 

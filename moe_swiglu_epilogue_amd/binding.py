@@ -21,7 +21,7 @@ STATUS = {0: "NVFP4_SUCCESS", 1: "NVFP4_ERROR_INVALID_VALUE",
 
 EXPORTS = ("nvfp4_quantize", "swiglu_nvfp4_quantize", "nvfp4_dequantize",
            "nvfp4_global_scale", "swiglu_nvfp4_global_scale", "swiglu_bf16",
-           "nvfp4_status_string")
+           "moe_l1_gemm_swiglu_nvfp4", "moe_l1_gemm_bf16", "nvfp4_status_string")
 
 _LIB = None
 _vp = C.c_void_p
@@ -60,6 +60,12 @@ def _lib():
             fn.restype = C.c_int
         L.swiglu_bf16.argtypes = [_vp, _i64, _i64, _i64, _vp, _i64, _vp]
         L.swiglu_bf16.restype = C.c_int
+        L.moe_l1_gemm_swiglu_nvfp4.argtypes = [_vp, _vp, _i64, _i64, _i64, _i64, _i64, _vp,
+                                               _i32, _vp, _vp, _vp, _vp, _vp]
+        L.moe_l1_gemm_swiglu_nvfp4.restype = C.c_int
+        L.moe_l1_gemm_bf16.argtypes = [_vp, _vp, _i64, _i64, _i64, _i64, _i64, _vp, _i32, _vp,
+                                       _i64, _vp]
+        L.moe_l1_gemm_bf16.restype = C.c_int
         L.nvfp4_status_string.argtypes = [C.c_int]
         L.nvfp4_status_string.restype = C.c_char_p
         _LIB = L
@@ -252,4 +258,69 @@ def swiglu_bf16(gate_up: torch.Tensor, *, out: torch.Tensor | None = None, strea
         raise ValueError("out must be a bfloat16 tensor of shape (rows, I) with unit column stride")
     _call(_lib().swiglu_bf16, "swiglu_bf16", _ptr(x), rows, inter, _pitch(x), _ptr(out),
           _pitch(out), _stream(stream))
+    return out
+
+
+def _weights(w1: torch.Tensor, x: torch.Tensor):
+    if w1.dtype == torch.bfloat16:
+        w1 = w1.view(torch.int16)
+    if w1.dtype not in (torch.int16, torch.uint16) or w1.device != x.device:
+        raise TypeError("w1 must be bfloat16 on the activations' device")
+    if w1.dim() == 2:
+        w1 = w1.unsqueeze(0)
+    if w1.dim() != 3 or w1.stride(2) != 1 or w1.stride(0) != w1.shape[1] * w1.stride(1):
+        raise ValueError("w1 must be [E, n, hidden] with unit column stride and packed experts")
+    return w1
+
+
+def moe_l1_gemm_swiglu_nvfp4(x: torch.Tensor, w1: torch.Tensor,
+                             expert_offsets: torch.Tensor | None = None,
+                             gs: torch.Tensor | None = None, *,
+                             packed: torch.Tensor | None = None,
+                             scales: torch.Tensor | None = None,
+                             swiglu_out: torch.Tensor | bool | None = None, stream=None):
+    """x BF16 [tokens, hidden], w1 BF16 [E, 2I, hidden] (rows = interleaved output
+    columns) -> (packed [tokens, I/2], scales [tokens, I/16]) and, when
+    ``swiglu_out`` is True or a tensor, y FP32 [tokens, I]."""
+    x = _bf16_matrix(x, "x")
+    w = _weights(w1, x)
+    tokens, hidden = x.shape
+    n = w.shape[1]
+    if w.shape[2] != hidden:
+        raise ValueError("w1 must be [E, 2I, hidden]")
+    inter = n // 2
+    e = _experts(gs, expert_offsets, x.device)
+    packed = _out(packed, (tokens, inter // 2), torch.uint8, x.device, "packed")
+    scales = _out(scales, (tokens, inter // 16), torch.uint8, x.device, "scales")
+    y = None
+    if swiglu_out is True:
+        y = torch.empty((tokens, inter), dtype=torch.float32, device=x.device)
+    elif isinstance(swiglu_out, torch.Tensor):
+        y = _out(swiglu_out, (tokens, inter), torch.float32, x.device, "swiglu_out")
+    _call(_lib().moe_l1_gemm_swiglu_nvfp4, "moe_l1_gemm_swiglu_nvfp4", _ptr(x), _ptr(w), tokens,
+          hidden, inter, _pitch(x), w.stride(1), _ptr(expert_offsets), e, _ptr(gs), _ptr(packed),
+          _ptr(scales), _ptr(y), _stream(stream))
+    return (packed, scales) if y is None else (packed, scales, y)
+
+
+def moe_l1_gemm_bf16(x: torch.Tensor, w1: torch.Tensor,
+                     expert_offsets: torch.Tensor | None = None, *,
+                     out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """x BF16 [tokens, hidden], w1 BF16 [E, n, hidden] -> BF16 [tokens, n]: the L1
+    GEMM output (interleaved [gate x8, up x8, ...]) of the unfused flow."""
+    x = _bf16_matrix(x, "x")
+    w = _weights(w1, x)
+    tokens, hidden = x.shape
+    n = w.shape[1]
+    if w.shape[2] != hidden:
+        raise ValueError("w1 must be [E, n, hidden]")
+    e = _experts(None, expert_offsets, x.device)
+    if out is None:
+        out = torch.empty((tokens, n), dtype=torch.bfloat16, device=x.device)
+    if (out.dtype != torch.bfloat16 or out.device != x.device or tuple(out.shape) != (tokens, n)
+            or (n > 1 and out.stride(1) != 1)):
+        raise ValueError("out must be a bfloat16 tensor of shape (tokens, n) with unit column stride")
+    _call(_lib().moe_l1_gemm_bf16, "moe_l1_gemm_bf16", _ptr(x), _ptr(w), tokens, hidden, n,
+          _pitch(x), w.stride(1), _ptr(expert_offsets), e, _ptr(out), _pitch(out),
+          _stream(stream))
     return out

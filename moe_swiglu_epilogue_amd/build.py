@@ -11,6 +11,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SRC = os.path.join(HERE, "csrc", "moe_nvfp4.hip")
+GEMM_SRC = os.path.join(HERE, "csrc", "moe_gemm.hip")
 LIB = os.path.join(HERE, "libmoe_nvfp4.so")
 CALIB_SRC = os.path.join(HERE, "csrc", "calib.hip")
 CALIB_LIB = os.path.join(HERE, "libnvfp4_calib.so")
@@ -28,13 +29,13 @@ FLAGS = [
 
 def build(verbose: bool = False) -> str:
     """Build both libraries; return the path of libmoe_nvfp4.so."""
-    _build_one(CALIB_SRC, CALIB_LIB, verbose)
-    return _build_one(SRC, LIB, verbose)
+    _build_one([CALIB_SRC], CALIB_LIB, verbose)
+    return _build_one([SRC, GEMM_SRC], LIB, verbose)
 
 
-def _build_one(src: str, lib: str, verbose: bool) -> str:
+def _build_one(srcs, lib: str, verbose: bool) -> str:
     tmp = lib + ".tmp%d" % os.getpid()
-    cmd = [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), src, "-o", tmp]
+    cmd = [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), *srcs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -48,10 +49,10 @@ def _build_one(src: str, lib: str, verbose: bool) -> str:
     return lib
 
 
-def asm(out_path: str) -> None:
-    """Write the gfx950 assembly of the kernels (for inspection)."""
+def asm(out_path: str, src: str = SRC) -> None:
+    """Write the gfx950 assembly of one source's kernels (for inspection)."""
     cmd = [HIPCC, *[f for f in FLAGS if f not in ("-shared", "-fPIC")], "-I",
-           os.path.join(ROOT, "include"), "--cuda-device-only", "-S", SRC, "-o", out_path]
+           os.path.join(ROOT, "include"), "--cuda-device-only", "-S", src, "-o", out_path]
     subprocess.run(cmd, check=True, capture_output=True)
 
 

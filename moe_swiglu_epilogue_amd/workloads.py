@@ -21,6 +21,11 @@ Workloads (rows x interleaved BF16 columns):
 * ``ragged``      131072 x 4096 (I = 2048), 256 experts with Zipf(1.1) row
   counts (rows grouped by expert, int32 offsets[257]), N(0,1) times a
   per-expert lognormal(0,1) factor.
+* ``moe_gemm``    inputs of the MoE L1 grouped GEMM: activations
+  x[tokens][hidden] ~ N(0,1), weights w1[E][2I][hidden] ~ N(0, 1/hidden)
+  (so the accumulators are about N(0,1)), Zipf(1.1) expert row counts;
+  ``exact=True`` draws x from multiples of 1/8 in [-2, 2] and w1 from
+  multiples of 1/16 in [-1, 1], whose FP32 sums are exact in any order.
 """
 from __future__ import annotations
 
@@ -235,6 +240,42 @@ def ragged(seed: int = 5, rows: int = 131072, inter: int = 2048,
     _run_chunks(fill, n_chunks)
     return Workload("ragged", x, fused=True, offsets=off,
                     meta={"seed": seed, "experts": experts})
+
+
+@dataclass
+class GemmWorkload:
+    x: np.ndarray            # BF16 bits [tokens][hidden]
+    w1: np.ndarray           # BF16 bits [experts][2 inter][hidden]
+    offsets: np.ndarray      # int32 [experts + 1]
+    inter: int
+
+
+def moe_gemm(seed: int = 6, tokens: int = 32768, hidden: int = 7168, inter: int = 3072,
+             experts: int = 8, exact: bool = False) -> GemmWorkload:
+    off = ragged_offsets(seed, tokens, experts)
+    ss = np.random.SeedSequence(seed).spawn(3)
+    n = 2 * inter
+    x = np.empty((tokens, hidden), np.uint16)
+    w = np.empty((experts, n, hidden), np.uint16)
+    xc = ss[1].spawn((tokens + CHUNK_ROWS - 1) // CHUNK_ROWS)
+    wc = ss[2].spawn(experts)
+
+    def draw(rng, shape, std, den, top):
+        if exact:
+            return rng.integers(-top, top + 1, shape).astype(np.float64) / den
+        return rng.standard_normal(shape) * std
+
+    def fill_x(k):
+        r0, r1 = k * CHUNK_ROWS, min(tokens, (k + 1) * CHUNK_ROWS)
+        x[r0:r1] = to_bf16_bits(draw(np.random.default_rng(xc[k]), (r1 - r0, hidden), 1.0, 8, 16))
+
+    def fill_w(e):
+        w[e] = to_bf16_bits(draw(np.random.default_rng(wc[e]), (n, hidden),
+                                 1.0 / np.sqrt(hidden), 16, 16))
+
+    _run_chunks(fill_x, len(xc))
+    _run_chunks(fill_w, experts)
+    return GemmWorkload(x, w, off, inter)
 
 
 # ---- small edge-case generators ----------------------------------------------

@@ -52,6 +52,7 @@ def lib():
         L.oracle_fp8_encode_array.argtypes = [_f32p, _i64, _u8p]
         L.oracle_swiglu_rows.argtypes = [_u16p, _i64, _i64, _i64, _f32p]
         L.oracle_swiglu_bf16_rows.argtypes = [_u16p, _i64, _i64, _i64, _u16p]
+        L.oracle_swiglu_f32_rows.argtypes = [_f32p, _i64, _i64, _i64, _f32p]
         L.oracle_f32_to_bf16_array.argtypes = [_f32p, _i64, _u16p]
         L.oracle_quantize_f32_rows.argtypes = [_f32p, _i64, _i64, _i64, _f32p,
                                                _u8p, _u8p, _f32p, _f32p]
@@ -151,6 +152,41 @@ def swiglu(gate_up: np.ndarray) -> np.ndarray:
     _check(lib().oracle_swiglu_rows(_p(x, _u16p), rows, inter, two_i, _p(y, _f32p)),
            "swiglu")
     return y
+
+
+def swiglu_f32(acc: np.ndarray) -> np.ndarray:
+    """FP32 [rows][2I] interleaved accumulators -> FP32 SwiGLU [rows][I]."""
+    a = np.ascontiguousarray(acc, dtype=np.float32)
+    rows, two_i = a.shape
+    inter = two_i // 2
+    y = np.empty((rows, inter), np.float32)
+    _check(lib().oracle_swiglu_f32_rows(_p(a, _f32p), rows, inter, two_i, _p(y, _f32p)),
+           "swiglu_f32")
+    return y
+
+
+def moe_l1_gemm(x: np.ndarray, w1: np.ndarray, offsets=None, rows=None) -> np.ndarray:
+    """The MoE L1 grouped GEMM in float64: acc[t][n] = sum_k x[t][k] w1[e(t)][n][k]
+    with BF16 bit patterns x [tokens][hidden] and w1 [E][n][hidden], e(t) the
+    expert holding row t (offsets [E+1]; None: one expert). Every product of
+    two BF16 values is exact in float64 and the sums carry about 1e-16
+    relative error. ``rows``: only these token rows (in that order)."""
+    xs = np.asarray(x, np.uint16)
+    ws = np.asarray(w1, np.uint16)
+    if ws.ndim == 2:
+        ws = ws[None]
+    t_all = np.arange(xs.shape[0]) if rows is None else np.asarray(rows)
+    if offsets is None:
+        e_of = np.zeros(t_all.size, np.int64)
+    else:
+        e_of = np.searchsorted(np.asarray(offsets, np.int64), t_all, side="right") - 1
+    out = np.empty((t_all.size, ws.shape[1]), np.float64)
+    for e in np.unique(e_of):
+        sel = np.nonzero(e_of == e)[0]
+        xf = (xs[t_all[sel]].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        wf = (ws[e].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        out[sel] = xf @ wf.T
+    return out
 
 
 def f32_to_bf16(x: np.ndarray) -> np.ndarray:

@@ -265,6 +265,30 @@ int oracle_swiglu_rows(const uint16_t *in, int64_t rows, int64_t inter,
     return 0;
 }
 
+/* De-interleave + SwiGLU of FP32 inputs: the L1 GEMM's FP32 accumulators in
+ * the fused-epilogue design ([APPROACH-2]: SiLU(gate) and SwiGLU computed
+ * from the accumulators, before any BF16 rounding). Same column mapping as
+ * oracle_swiglu_rows. */
+int oracle_swiglu_f32_rows(const float *acc, int64_t rows, int64_t inter,
+                           int64_t ld_acc, float *y)
+{
+    if (rows < 0 || inter < 0 || inter % 8 != 0 || ld_acc < 2 * inter)
+        return 1;
+    if (rows == 0 || inter == 0)
+        return 0;
+    if (!acc || !y)
+        return 1;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        const float *a = acc + r * ld_acc;
+        for (int64_t j = 0; j < inter; ++j) {
+            int64_t col = 16 * (j / 8) + j % 8;          /* gate column; up is col + 8 */
+            y[r * inter + j] = oracle_swiglu(a[col], a[col + 8]);
+        }
+    }
+    return 0;
+}
+
 /* The first pass of the two-pass variant ([APPROACH] "Revised approach:
  * Compact SwiGLU output", target flow): the SwiGLU of the interleaved input
  * rounded to BF16, written as a compact [rows][inter] BF16 tensor. */

@@ -47,6 +47,8 @@ int oracle_fp8_encode_array(const float *v, int64_t n, uint8_t *out);
 int oracle_swiglu_rows(const uint16_t *in, int64_t rows, int64_t inter,
                        int64_t ld_in, float *y /* rows x inter */);
 
+int oracle_swiglu_f32_rows(const float *acc, int64_t rows, int64_t inter,
+                           int64_t ld_acc, float *y /* rows x inter */);
 int oracle_swiglu_bf16_rows(const uint16_t *in, int64_t rows, int64_t inter,
                             int64_t ld_in, uint16_t *out /* rows x inter BF16 */);
 int oracle_f32_to_bf16_array(const float *x, int64_t n, uint16_t *out);

@@ -40,6 +40,7 @@ def test_header_declares_the_entry_points():
     assert _declared() == sorted(["nvfp4_quantize", "swiglu_nvfp4_quantize",
                                   "nvfp4_dequantize", "nvfp4_global_scale",
                                   "swiglu_nvfp4_global_scale", "swiglu_bf16",
+                                  "moe_l1_gemm_swiglu_nvfp4", "moe_l1_gemm_bf16",
                                   "nvfp4_status_string"])
 
 
@@ -184,6 +185,43 @@ def test_swiglu_bf16_validation(lib):
     assert sb(lib, ld=68) == MISALIGNED
     assert sb(lib, rows=2**31, inter=16, ld=32, ld_out=16) == SHAPE
     assert sb(lib, rows=0, x=None, out=None) == OK
+
+
+def gf(lib, x=A16, w=A16, tokens=4, hidden=64, inter=64, ld_x=64, ld_w=64, offs=None, ne=0,
+       gs=None, packed=A16, scales=A16, y=None):
+    return lib.moe_l1_gemm_swiglu_nvfp4(x, w, tokens, hidden, inter, ld_x, ld_w, offs, ne, gs,
+                                        packed, scales, y, None)
+
+
+def gb(lib, x=A16, w=A16, tokens=4, hidden=64, n=128, ld_x=64, ld_w=64, offs=None, ne=0,
+       out=A16, ld_out=128):
+    return lib.moe_l1_gemm_bf16(x, w, tokens, hidden, n, ld_x, ld_w, offs, ne, out, ld_out, None)
+
+
+def test_gemm_validation(lib):
+    for f in (gf, gb):
+        assert f(lib, tokens=-1) == INVALID
+        assert f(lib, ld_x=32) == INVALID
+        assert f(lib, ld_w=32) == INVALID
+        assert f(lib, hidden=96, ld_x=96, ld_w=96) == SHAPE         # hidden % 64
+        assert f(lib, ne=2) == INVALID
+        assert f(lib, offs=A16, ne=0) == INVALID
+        assert f(lib, offs=A16, ne=1025) == SHAPE
+        assert f(lib, x=A16 + 8) == MISALIGNED
+        assert f(lib, w=A16 + 8) == MISALIGNED
+        assert f(lib, ld_x=68) == MISALIGNED
+        assert f(lib, x=None) == INVALID
+        assert f(lib, hidden=0, ld_x=0, ld_w=0) == SHAPE
+        assert f(lib, tokens=2**31) == SHAPE
+    assert gf(lib, inter=32) == SHAPE                              # 2 * inter % 128
+    assert gf(lib, packed=None) == INVALID
+    assert gf(lib, packed=A16 + 4) == MISALIGNED
+    assert gf(lib, y=A16 + 8) == MISALIGNED
+    assert gf(lib, tokens=0, x=None, w=None, packed=None, scales=None) == OK
+    assert gb(lib, n=64) == SHAPE
+    assert gb(lib, ld_out=64) == INVALID
+    assert gb(lib, out=A16 + 8) == MISALIGNED
+    assert gb(lib, tokens=0, x=None, w=None, out=None) == OK
 
 
 def test_binding_rejects_host_tensors():

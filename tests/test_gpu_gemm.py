@@ -1,0 +1,168 @@
+"""Parity of the MoE L1 grouped GEMM (matrix cores) and its fused SwiGLU +
+NVFP4 epilogue with the oracle: a float64 GEMM of the same BF16 operands,
+rounded to FP32 accumulators, then the oracle's SwiGLU and quantizer.
+
+* Exact-arithmetic operands (multiples of 1/8 and 1/16): every FP32 sum is
+  exact in any order, so the GPU accumulators equal the oracle's bit for bit.
+  The BF16 GEMM output is then bit-exact, and the fused path follows the fused
+  acceptance rules of tests/parity.py (SwiGLU within 2e-6, codes exact
+  outside rounding boundaries, zero-tolerance re-quantize).
+* Random operands: the accumulators differ from the exact sums by rounding.
+  Each is checked against the bound hidden * 2^-24 * sum_k |x_k w_k| (FP32
+  summation in any order), the SwiGLU values against that bound propagated
+  through silu(g) u, and the quantized bytes by re-quantizing the kernel's
+  own FP32 SwiGLU values (zero tolerance).
+* The production launch (no FP32 debug output) writes the same bytes.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import parity as P
+from moe_swiglu_epilogue_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print("[gpu]", *a, flush=True)
+
+
+@pytest.fixture(scope="module")
+def M():
+    import moe_swiglu_epilogue_amd as M
+    assert torch.cuda.is_available()
+    M.binding.raw()
+    return M
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def dev_bf16(bits):
+    return dev(np.asarray(bits).view(np.int16)).view(torch.bfloat16)
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def run(M, g, gs=None, offsets=True):
+    x, w = dev_bf16(g.x), dev_bf16(g.w1)
+    off = dev(g.offsets) if offsets else None
+    gst = None if gs is None else dev(np.asarray(gs, np.float32))
+    out = M.moe_l1_gemm_bf16(x, w if offsets else w[0], off)
+    p, s, y = M.moe_l1_gemm_swiglu_nvfp4(x, w if offsets else w[0], off, gst, swiglu_out=True)
+    p2, s2 = M.moe_l1_gemm_swiglu_nvfp4(x, w if offsets else w[0], off, gst)
+    res = dict(bf16=host(out.view(torch.int16)).view(np.uint16), p=host(p), s=host(s), y=host(y),
+               p2=host(p2), s2=host(s2))
+    P.assert_bytes_equal("production packed", res["p2"], res["p"])
+    P.assert_bytes_equal("production scales", res["s2"], res["s"])
+    return res
+
+
+def gs_rows_of(g, gs, rows=None):
+    if gs is None:
+        return None
+    r = oracle.rows_global_scale(np.asarray(gs, np.float32), g.offsets, g.x.shape[0])
+    return r if rows is None else r[rows]
+
+
+@pytest.mark.parametrize("tokens,hidden,inter,experts,seed", [
+    (300, 256, 128, 5, 1), (1000, 512, 192, 9, 2), (129, 64, 64, 1, 3), (513, 1024, 256, 3, 4),
+    (256, 4096, 128, 2, 5)])
+def test_gemm_exact_operands(M, tokens, hidden, inter, experts, seed):
+    g = W.moe_gemm(seed, tokens, hidden, inter, experts, exact=True)
+    acc = oracle.moe_l1_gemm(g.x, g.w1, g.offsets)
+    acc32 = acc.astype(np.float32)
+    assert np.array_equal(acc32.astype(np.float64), acc), "operands must sum exactly"
+    gs = np.float32(np.random.default_rng(seed).uniform(0.01, 2.0, experts))
+    say("moe_l1_gemm exact", tokens, hidden, inter, "experts", experts, g.offsets[:6])
+    r = run(M, g, gs)
+    P.assert_bytes_equal("bf16 GEMM", r["bf16"], oracle.f32_to_bf16(acc32))
+    ry = oracle.swiglu_f32(acc32)
+    gsr = gs_rows_of(g, gs)
+    rp, rs, rbsf, rv = oracle.quantize_f32(ry, gsr, diag=True)
+    rep = P.fused_report(r["p"], r["s"], r["y"], rp, rs, ry, rbsf, rv, gsr)
+    say("fused GEMM exact", rep)
+    if rep.swiglu_bad:
+        yg, yr = r["y"].astype(np.float64), ry.astype(np.float64)
+        bad = np.argwhere(~((np.abs(yg - yr) <= 2e-6 * np.abs(yr)) |
+                            ((np.abs(yr) < 1e-30) & (np.signbit(yg) == np.signbit(yr)))))
+        for t, j in bad[:8]:
+            col = 16 * (j // 8) + j % 8
+            say("swiglu outlier: g %r u %r gpu %r ref %r rel %.3g" % (
+                float(acc32[t, col]), float(acc32[t, col + 8]), float(yg[t, j]), float(yr[t, j]),
+                abs(yg[t, j] - yr[t, j]) / max(abs(yr[t, j]), 1e-45)))
+    P.assert_fused_ok(rep, "fused GEMM exact operands")
+
+
+def test_gemm_single_expert_no_offsets(M):
+    g = W.moe_gemm(5, 200, 128, 64, 1, exact=True)
+    acc32 = oracle.moe_l1_gemm(g.x, g.w1[0], None).astype(np.float32)
+    r = run(M, g, None, offsets=False)
+    P.assert_bytes_equal("bf16 GEMM, one expert", r["bf16"], oracle.f32_to_bf16(acc32))
+    ry = oracle.swiglu_f32(acc32)
+    rp, rs, rbsf, rv = oracle.quantize_f32(ry, None, diag=True)
+    P.assert_fused_ok(P.fused_report(r["p"], r["s"], r["y"], rp, rs, ry, rbsf, rv), "one expert")
+
+
+def check_random(g, r, rows, gs=None):
+    """Bound checks of a random-operand run on the given token rows."""
+    acc = oracle.moe_l1_gemm(g.x, g.w1, g.offsets, rows=rows)
+    mag = oracle.moe_l1_gemm(g.x & np.uint16(0x7FFF), g.w1 & np.uint16(0x7FFF), g.offsets, rows=rows)
+    hidden = g.x.shape[1]
+    bound = hidden * 2.0 ** -24 * mag + 1e-30
+    # BF16 output: within half a BF16 ulp of the exact sum, plus the bound
+    got = (r["bf16"][rows].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    half_ulp = np.abs(acc) * 2.0 ** -8 + 2.0 ** -134
+    assert np.all(np.abs(got - acc) <= half_ulp + bound), "bf16 GEMM outside the bound"
+    # SwiGLU: |dy| <= |u| |silu'(g)| dg + |silu(g)| du, silu'(g) = s (1 + g (1 - s))
+    n = acc.shape[1]
+    gi = np.concatenate([np.arange(16 * b, 16 * b + 8) for b in range(n // 16)])
+    gg, uu = acc[:, gi], acc[:, gi + 8]
+    bg, bu = bound[:, gi], bound[:, gi + 8]
+    sg = 1.0 / (1.0 + np.exp(-np.clip(gg, -700, 700)))
+    y_ref = gg * sg * uu
+    tol = (np.abs(uu) * np.abs(sg * (1 + gg * (1 - sg))) * bg + np.abs(gg * sg) * bu
+           + 2e-6 * np.abs(y_ref) + 1e-30)
+    err = np.abs(r["y"][rows].astype(np.float64) - y_ref)
+    assert np.all(err <= tol), ("swiglu outside the bound", float((err / tol).max()))
+    # bytes: the oracle quantizer on the kernel's own FP32 SwiGLU values
+    qp, qs = oracle.quantize_f32(r["y"][rows], gs_rows_of(g, gs, rows))
+    P.assert_bytes_equal("requantize packed", r["p"][rows], qp)
+    P.assert_bytes_equal("requantize scales", r["s"][rows], qs)
+    # code agreement with the oracle's own SwiGLU of the exact sums (reported)
+    rp, rs = oracle.quantize_f32(oracle.swiglu_f32(acc.astype(np.float32)), gs_rows_of(g, gs, rows))
+    return (float(np.mean(P.nibbles(rp) != P.nibbles(r["p"][rows]))),
+            float(np.mean(rs != r["s"][rows])), float((err / tol).max()))
+
+
+@pytest.mark.parametrize("tokens,hidden,inter,experts,seed", [
+    (700, 1024, 256, 6, 11), (2048, 2048, 512, 16, 12)])
+def test_gemm_random_operands(M, tokens, hidden, inter, experts, seed):
+    g = W.moe_gemm(seed, tokens, hidden, inter, experts)
+    say("moe_l1_gemm random", tokens, hidden, inter, "experts", experts)
+    r = run(M, g)
+    codes, scl, worst = check_random(g, r, np.arange(tokens))
+    say("random: code mismatch %.2e, scale mismatch %.2e vs the exact-sum oracle; worst err/tol %.3f"
+        % (codes, scl, worst))
+
+
+def test_gemm_prefill_shape_sampled(M):
+    """32768 token rows, hidden 7168, I = 3072, 8 experts (Zipf): sampled rows
+    (random, every expert's first and last row, the first rows of row tiles)."""
+    g = W.moe_gemm()
+    tokens = g.x.shape[0]
+    say("moe_l1_gemm prefill-shaped", g.x.shape, g.w1.shape)
+    r = run(M, g)
+    rng = np.random.default_rng(66)
+    extra = np.concatenate([g.offsets[:-1], g.offsets[1:] - 1, g.offsets[:-1] + 128])
+    rows = np.unique(np.concatenate([rng.choice(tokens, 192, replace=False),
+                                     extra[(extra >= 0) & (extra < tokens)]]))
+    codes, scl, worst = check_random(g, r, rows)
+    say("prefill-shaped sampled rows %d: code mismatch %.2e, scale mismatch %.2e; worst err/tol %.3f"
+        % (rows.size, codes, scl, worst))

@@ -43,6 +43,9 @@ MUTANTS = {
     "bf16_7_bits": ("q = ldexp(rint(ldexp(m, 8)), e - 8);", "q = ldexp(rint(ldexp(m, 7)), e - 7);"),
     "bf16_subnormal_8_bits": ("q = ldexp(rint(ldexp(a, 133)), -133);",
                               "{ int e2; double m2 = frexp(a, &e2); q = ldexp(rint(ldexp(m2, 8)), e2 - 8); }"),
+    "swiglu_f32_swapped": ("y[r * inter + j] = oracle_swiglu(a[col], a[col + 8]);",
+                           "y[r * inter + j] = oracle_swiglu(a[col + 8], a[col]);"),
+    "swiglu_f32_stride": ("int64_t col = 16 * (j / 8) + j % 8;", "int64_t col = 8 * (j / 8) + j % 8;"),
     "swiglu_bf16_shifted": ("out[r * inter + j] = oracle_f32_to_bf16(y[j]);",
                             "out[r * inter + j] = oracle_f32_to_bf16(y[j ^ 1]);"),
 }
@@ -53,6 +56,7 @@ FAST_PINS = [P.pin_page_facts, P.pin_fp8_decode_vs_torch, P.pin_fp8_saturation,
              P.pin_quantize_vs_twin, P.pin_dequant_closed_form,
              P.pin_group_amax, P.pin_expert_global_scale, P.pin_bf16_ties,
              P.pin_swiglu_bf16_vs_torch, lambda: P.pin_bf16_vs_torch(step=9973),
+             P.pin_swiglu_f32, P.pin_moe_l1_gemm,
              lambda: P.pin_fp8_encode_vs_torch(step=997)]
 
 
@@ -102,3 +106,35 @@ def test_pins_catch_global_scale_mutant(name, monkeypatch):
     monkeypatch.setattr(oracle, "expert_global_scale", PY_MUTANTS[name])
     with pytest.raises(AssertionError):
         P.pin_expert_global_scale()
+
+
+def _gemm_left(x, w1, offsets=None, rows=None):
+    """moe_l1_gemm with the expert lookup off by one at boundaries."""
+    xs, ws = np.asarray(x, np.uint16), np.asarray(w1, np.uint16)
+    if ws.ndim == 2:
+        ws = ws[None]
+    t_all = np.arange(xs.shape[0]) if rows is None else np.asarray(rows)
+    e_of = (np.zeros(t_all.size, np.int64) if offsets is None else
+            np.clip(np.searchsorted(np.asarray(offsets, np.int64), t_all, side="left") - 1, 0, None))
+    out = np.empty((t_all.size, ws.shape[1]), np.float64)
+    for e in np.unique(e_of):
+        sel = np.nonzero(e_of == e)[0]
+        xf = (xs[t_all[sel]].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        wf = (ws[e].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        out[sel] = xf @ wf.T
+    return out
+
+
+GEMM_MUTANTS = {
+    "gemm_expert_left": _gemm_left,
+    "gemm_float32": lambda x, w1, offsets=None, rows=None: _REAL_GEMM(x, w1, offsets, rows).astype(np.float32).astype(np.float64) + 1e-9,
+    "gemm_untransposed_ok_shape": lambda x, w1, offsets=None, rows=None: _REAL_GEMM(x, np.asarray(w1)[..., ::-1], offsets, rows),
+}
+_REAL_GEMM = oracle.moe_l1_gemm
+
+
+@pytest.mark.parametrize("name", sorted(GEMM_MUTANTS))
+def test_pins_catch_gemm_mutant(name, monkeypatch):
+    monkeypatch.setattr(oracle, "moe_l1_gemm", GEMM_MUTANTS[name])
+    with pytest.raises(AssertionError):
+        P.pin_moe_l1_gemm()

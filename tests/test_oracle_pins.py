@@ -320,11 +320,53 @@ def pin_swiglu_bf16_vs_torch():
     assert np.array_equal(oracle.swiglu_bf16(x), ref.view(np.uint16))
 
 
+def pin_swiglu_f32():
+    """The FP32-input driver (fused-GEMM epilogue reference): bit-exact with
+    the pinned BF16 driver on BF16-representable inputs, and within 1 ulp of
+    PyTorch's float64 SiLU on arbitrary FP32 accumulators."""
+    x = W.random_fused(11, 1040, 71, 2.0)
+    assert np.array_equal(oracle.swiglu_f32(W.bf16_bits_to_f32(x)).view(np.uint32),
+                          oracle.swiglu(x).view(np.uint32))
+    rng = np.random.default_rng(72)
+    acc = (rng.standard_normal((13, 2 * 1040)) * 4).astype(np.float32)
+    y = oracle.swiglu_f32(acc)
+    g = np.concatenate([acc[:, 16 * b: 16 * b + 8] for b in range(1040 // 8)], axis=1)
+    u = np.concatenate([acc[:, 16 * b + 8: 16 * b + 16] for b in range(1040 // 8)], axis=1)
+    ref = (torch.nn.functional.silu(torch.from_numpy(g.astype(np.float64))) *
+           torch.from_numpy(u.astype(np.float64))).to(torch.float32).numpy()
+    ulps = np.abs(y.view(np.int32).astype(np.int64) - ref.view(np.int32).astype(np.int64))
+    assert np.all(ulps <= 1), ulps.max()
+
+
+def pin_moe_l1_gemm():
+    """The grouped float64 GEMM against a brute-force loop (every product and
+    sum written out) on a tiny ragged case with empty experts, and its row
+    selection against the full result."""
+    rng = np.random.default_rng(73)
+    tokens, hidden, n, experts = 11, 8, 6, 4
+    x = W.to_bf16_bits(rng.standard_normal((tokens, hidden)))
+    w = W.to_bf16_bits(rng.standard_normal((experts, n, hidden)))
+    off = np.array([0, 0, 4, 4, 11], np.int32)
+    got = oracle.moe_l1_gemm(x, w, off)
+    xf, wf = W.bf16_bits_to_f32(x).astype(float), W.bf16_bits_to_f32(w).astype(float)
+    for t in range(tokens):
+        e = max(i for i in range(experts) if off[i] <= t and off[i + 1] > t)
+        for j in range(n):
+            want = 0.0
+            for k in range(hidden):
+                want += xf[t, k] * wf[e, j, k]
+            assert abs(got[t, j] - want) <= 1e-12 * (1 + abs(want)), (t, j)
+    sel = np.array([10, 3, 4, 0])
+    assert np.array_equal(oracle.moe_l1_gemm(x, w, off, rows=sel), got[sel])
+    one = oracle.moe_l1_gemm(x, w[1], None)
+    assert np.allclose(one, xf @ wf[1].T, rtol=0, atol=1e-12)
+
+
 ALL_PINS = [pin_page_facts, pin_fp8_decode_vs_torch, pin_fp8_saturation,
             pin_fp8_roundtrip, pin_e2m1_format, pin_e2m1_table, pin_swiglu_vs_torch,
             pin_swiglu_closed_forms, pin_quantize_vs_twin, pin_dequant_closed_form,
             pin_group_amax, pin_expert_global_scale, pin_bf16_vs_torch, pin_bf16_ties,
-            pin_swiglu_bf16_vs_torch]
+            pin_swiglu_bf16_vs_torch, pin_swiglu_f32, pin_moe_l1_gemm]
 
 
 # ---- tests --------------------------------------------------------------------
