@@ -14,7 +14,8 @@ quantize, the dequantize and the global-scale pre-pass on the same tensor;
 the two-pass ablation (compact BF16 SwiGLU, then the standalone quantize);
 in-repo read / copy kernels over the same input as HBM ceilings; the ragged
 256-expert workload (pre-pass, quantize with per-expert scales, dequantize);
-the decode-shaped workload over 8 rotating buffer sets.
+the decode-shaped workload over 8 rotating buffer sets; the MoE L1 grouped
+GEMM with the fused epilogue against the unfused flow and hipBLASLt.
 
 Every timed region is preceded by --settle-ms of untimed back-to-back
 launches (the clocks need ~30 ms of load to settle) and the warmup steps.
@@ -44,7 +45,8 @@ PMC_SUMMARY = os.path.join(ROOT, "profiles", "fused_quantize_kernel_prefill_pmc.
 CALIB_READ_BLOCKS = (1024, 1536, 8192, 49152)
 CALIB_COPY_BLOCKS = (512, 8192, 49152)
 SECONDARY = ("nvfp4_quantize", "nvfp4_dequantize", "global_scale", "two_pass", "calib_read",
-             "calib_copy", "ragged", "decode")
+             "calib_copy", "ragged", "decode", "gemm")
+PEAK_BF16_TFLOPS = 2500.0           # MI355X dense BF16 matrix peak
 
 
 def load_calib():
@@ -383,7 +385,60 @@ def secondary_figures(M, W, x, packed, scales, args, dev):
             "decode-shaped swiglu_nvfp4_quantize", rotating, dr * di * BYTES_PER_ELEM, dr * di,
             max(st, 80), ms, {"shape": [dr, 2 * di], "note": "8 rotating input/output sets"})
         del sets
+    if "gemm" in want:
+        sec["moe_l1_gemm"] = gemm_figures(M, W, args)
     return sec
+
+
+def gemm_figures(M, W, args):
+    """The MoE L1 grouped GEMM with the fused SwiGLU + NVFP4 epilogue against
+    the unfused flow on the same GEMM core (BF16 L1 output, then
+    swiglu_nvfp4_quantize), and hipBLASLt's plain BF16 GEMM (torch.matmul per
+    expert) for context: 32768 token rows, hidden 7168, I = 3072, 8 experts."""
+    import numpy as np
+    import torch
+    print("[bench] generating MoE L1 GEMM workload", file=sys.stderr, flush=True)
+    g = W.moe_gemm()
+    T, H = g.x.shape
+    N = g.w1.shape[1]
+    inter = N // 2
+    E = g.w1.shape[0]
+    dev = torch.device("cuda:0")
+    x = torch.from_numpy(g.x.view(np.int16)).to(dev).view(torch.bfloat16)
+    w = torch.from_numpy(g.w1.view(np.int16)).to(dev).view(torch.bfloat16)
+    off = torch.from_numpy(g.offsets).to(dev)
+    offs = g.offsets.tolist()
+    del g
+    flop = 2.0 * T * H * N
+    p = torch.empty((T, inter // 2), dtype=torch.uint8, device=dev)
+    sc = torch.empty((T, inter // 16), dtype=torch.uint8, device=dev)
+    yb = torch.empty((T, N), dtype=torch.bfloat16, device=dev)
+    outs = [yb[offs[e]:offs[e + 1]] for e in range(E)]
+    wt = [w[e].t() for e in range(E)]
+
+    def fused():
+        M.moe_l1_gemm_swiglu_nvfp4(x, w, off, packed=p, scales=sc)
+
+    def unfused():
+        M.moe_l1_gemm_bf16(x, w, off, out=yb)
+        M.swiglu_nvfp4_quantize(yb, packed=p, scales=sc)
+
+    def library():
+        for e in range(E):
+            torch.matmul(x[offs[e]:offs[e + 1]], wt[e], out=outs[e])
+
+    res = {"shape": {"tokens": T, "hidden": H, "inter": inter, "experts": E},
+           "flop_per_launch": flop}
+    steps = max(5, args.secondary_steps // 4)
+    for name, fn in (("fused", fused), ("unfused", unfused), ("hipblaslt_bf16_gemm_only", library)):
+        _, ms, per = time_launches(fn, steps, 2, args.settle_ms)
+        res[name] = {"ms": round(ms, 4), "TFLOP_s": round(flop / ms / 1e9, 1),
+                     "frac_of_bf16_peak": round(flop / ms / 1e9 / PEAK_BF16_TFLOPS, 4),
+                     "ms_p10_p50_p90": [round(pct(per, q), 4) for q in (0.1, 0.5, 0.9)]}
+        print("[bench] MoE L1 GEMM %-26s %8.4f ms  %7.1f TFLOP/s" % (name, ms, flop / ms / 1e9),
+              file=sys.stderr, flush=True)
+    res["fusion_speedup"] = round(res["unfused"]["ms"] / res["fused"]["ms"], 4)
+    return res
 
 
 def main():

@@ -201,7 +201,7 @@ nvfp4_status_t swiglu_bf16(const uint16_t *gate_up, int64_t rows, int64_t inter,
  *   packed[tokens][inter/2], scales[tokens][inter/16] and, if swiglu_out is
  *   not NULL, y [tokens][inter] FP32.
  * expert_offsets: as above (NULL: one expert, w1[0], owns every row);
- * num_experts <= 1024. Shapes: hidden % 64 == 0, inter % 64 == 0, ld_x and
+ * num_experts <= 512. Shapes: hidden % 64 == 0, inter % 128 == 0, ld_x and
  * ld_w >= hidden and multiples of 8; x and w1 16-byte aligned. One kernel.
  * hidden == 0 is NVFP4_ERROR_UNSUPPORTED_SHAPE; tokens == 0 or inter == 0
  * is a no-op.
@@ -217,7 +217,7 @@ nvfp4_status_t moe_l1_gemm_swiglu_nvfp4(const uint16_t *x, const uint16_t *w1,
 /*
  * The same grouped GEMM with a plain epilogue: the L1 output rounded to BF16
  * (round to nearest even), out[tokens][ld_out] with n columns (n = 2*inter in
- * the interleaved layout; n % 128 == 0, ld_out >= n, multiple of 8, out
+ * the interleaved layout; n % 256 == 0, ld_out >= n, multiple of 8, out
  * 16-byte aligned). This is the producer of the unfused flow
  * (moe_l1_gemm_bf16, then swiglu_nvfp4_quantize), kept to measure what the
  * fusion saves. Page: "NVFP4-1.1_APPROACH.md", "Revised approach" (current

@@ -19,13 +19,17 @@
 // output column n (the weight stored [out][in], K contiguous). Output column
 // n of the L1 GEMM follows the interleaved layout [gate x8, up x8, ...].
 //
-// Decomposition: a workgroup of 4 waves computes 128 x 128 output tiles; wave
-// (wm, wn) owns the 64 x 64 quarter (wm, wn) as 2 x 2 MFMA tiles of 32 x 32.
-// The K loop stages 128 x 64 slices of x and w in LDS (double-buffered, XOR
-// swizzled 16-byte chunks) and prefetches the next slice into registers while
-// the matrix cores work on the current one. Tiles are enumerated per expert
-// (ceil(rows_e / 128) row tiles each, from a prefix sum the workgroup builds
-// once in LDS) and handed to a persistent grid.
+// Decomposition: one workgroup of 8 waves per CU computes 256 x 256 output
+// tiles; wave (wm, wn) owns rows 64 wm .. +64 and columns 128 wn .. +128 as
+// 2 x 4 MFMA tiles of 32 x 32. The K loop stages 256 x 64 slices of x and w
+// in LDS (double-buffered, rows padded against bank conflicts) and
+// prefetches the next slice into registers while the matrix cores work on
+// the current one. 256 x 256 tiles halve the operand traffic per FLOP of
+// 128 x 128 ones (measured: 128 x 128 tiles pulled 13 TB/s through L2 and
+// held the matrix cores at 35%). Tiles are enumerated per expert
+// (ceil(rows_e / 256) row tiles each, from a prefix sum the workgroup builds
+// once in LDS) and handed to a persistent, XCD-aware grid. The epilogue runs
+// in four 64-row passes through an LDS buffer that overlays the stages.
 #include "../../include/moe_nvfp4.h"
 #include "nvfp4_device.hpp"
 
@@ -35,16 +39,19 @@
 namespace {
 
 constexpr int kWave = 64;
-constexpr int kBM = 128, kBN = 128, kBK = 64;
-constexpr int kThreads = 256;
-constexpr int kMaxExperts = 1024;
-constexpr int kRowBytes = kBK * 2;                        // one staged row: 8 chunks of 16 B
-constexpr int kStageBytes = (kBM + kBN) * kRowBytes;      // 32 KB: x slice then w slice
-constexpr int kCPitch = kBN + 4;                          // floats per LDS row of the C tile
-constexpr int kCTileBytes = kBM * kCPitch * 4;            // 67,584 B
-constexpr int kLdsBytes = kCTileBytes > 2 * kStageBytes ? kCTileBytes : 2 * kStageBytes;
+constexpr int kBM = 256, kBN = 256, kBK = 64;
+constexpr int kThreads = 512;                             // 8 waves: 4 x 2 wave tiles of 64 x 128
+constexpr int kMaxExperts = 512;
+constexpr int kRowBytes = kBK * 2;                        // 128 data bytes per staged row
+constexpr int kRowPitch = kRowBytes + 16;                 // one 16-byte pad per row
+constexpr int kStageBytes = (kBM + kBN) * kRowPitch;      // 73,728 B: x slice then w slice
+constexpr int kPassRows = 64;                             // epilogue rows per pass
+constexpr int kCPitch = kBN + 4;                          // floats per LDS row of the C buffer
+constexpr int kCBytes = kPassRows * kCPitch * 4;          // 66,560 B
+constexpr int kLdsBytes = 2 * kStageBytes;
+static_assert(kCBytes <= kLdsBytes, "the C buffer overlays the operand stages");
 constexpr int kMi355xCUs = 256;
-constexpr int kBlocksPerCU = 2;
+constexpr int kXcds = 8;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -54,10 +61,12 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
-// Byte offset of 16-byte chunk c (0..7) of staged row r: the chunk index is
-// XORed with r mod 8, so the 32 rows a wave reads at one chunk position land
-// in 8 different bank groups per 8 consecutive rows.
-__device__ __forceinline__ int chunk_at(int r, int c) { return r * kRowBytes + ((c ^ (r & 7)) << 4); }
+// Byte offset of 16-byte chunk c (0..7) of staged row r. Rows are padded to
+// 144 bytes, so the 16 rows whose chunks one LDS cycle serves (a wave reads
+// 32 rows at one chunk position) start in 16 different 4-bank groups (no
+// bank conflicts), and a lane's chunk for each K step is its row base plus
+// an immediate offset.
+__device__ __forceinline__ int chunk_at(int r, int c) { return r * kRowPitch + (c << 4); }
 
 struct Gemm {
     const uint16_t* x;
@@ -72,12 +81,13 @@ struct Gemm {
 struct TileRef {
     int e;          // expert
     int row0;       // first token row
-    int rows;       // valid rows (1..128)
+    int rows;       // valid rows (1..256)
     int n0;         // first output column
 };
 
 // Tile prefix in LDS: off[e] (clamped to [0, tokens]) and pre[e] = row tiles
-// of experts 0..e-1. Returns the total number of row tiles.
+// of experts 0..e-1 (thread t counts expert t; Hillis-Steele scan). Returns
+// the total number of row tiles.
 __device__ int build_tile_prefix(const Gemm& g, int* off, int* pre, int* part)
 {
     const int t = threadIdx.x;
@@ -87,19 +97,8 @@ __device__ int build_tile_prefix(const Gemm& g, int* off, int* pre, int* part)
         off[i] = min(max(o, 0), g.tokens);
     }
     __syncthreads();
-    // each thread counts 4 consecutive experts; Hillis-Steele scan of the sums
-    int loc[4];
-    int s = 0;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int e = 4 * t + q;
-        if (e < E) {
-            const int rows = max(off[e + 1] - off[e], 0);
-            s += (rows + kBM - 1) / kBM;
-        }
-        loc[q] = s;
-    }
-    part[t] = s;
+    const int cnt = t < E ? (max(off[t + 1] - off[t], 0) + kBM - 1) / kBM : 0;
+    part[t] = cnt;
     __syncthreads();
     for (int d = 1; d < kThreads; d <<= 1) {
         const int v = t >= d ? part[t - d] : 0;
@@ -107,13 +106,8 @@ __device__ int build_tile_prefix(const Gemm& g, int* off, int* pre, int* part)
         part[t] += v;
         __syncthreads();
     }
-    const int excl = part[t] - s;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int e = 4 * t + q;
-        if (e < E)
-            pre[e + 1] = excl + loc[q];
-    }
+    if (t < E)
+        pre[t + 1] = part[t];
     if (t == 0)
         pre[0] = 0;
     __syncthreads();
@@ -125,8 +119,6 @@ __device__ __forceinline__ TileRef tile_ref(const Gemm& g, const int* off, const
 {
     const int nt = g.n / kBN;
     const int mt = tile / nt;
-    TileRef r;
-    r.n0 = (tile - mt * nt) * kBN;
     int lo = 0, hi = g.experts;                 // largest e with pre[e] <= mt
     while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
@@ -135,16 +127,17 @@ __device__ __forceinline__ TileRef tile_ref(const Gemm& g, const int* off, const
         else
             hi = mid;
     }
+    TileRef r;
     r.e = uniform(lo);
     r.row0 = uniform(off[lo] + (mt - pre[lo]) * kBM);
     r.rows = uniform(min(kBM, off[lo + 1] - r.row0));
-    r.n0 = uniform(r.n0);
+    r.n0 = uniform((tile - mt * nt) * kBN);
     return r;
 }
 
-// 128 x 64 slices of x (rows row0.., clamped to the tile's valid rows) and
+// 256 x 64 slices of x (rows row0.., clamped to the tile's valid rows) and
 // w (rows n0..) at K offset k0: thread t loads 16-byte chunk t % 8 of rows
-// t / 8 + 32 j, j = 0..3, of each.
+// t / 8 + 64 j, j = 0..3, of each.
 struct Slice {
     u32x4 a[4], b[4];
 };
@@ -157,7 +150,7 @@ __device__ __forceinline__ void load_slice(Slice& s, const Gemm& g, const TileRe
     const uint16_t* xb = g.x + k0 + 8 * c;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        const int r = r0 + 32 * j;
+        const int r = r0 + 64 * j;
         const int xr = tr.row0 + min(r, tr.rows - 1);
         s.a[j] = *reinterpret_cast<const u32x4*>(xb + (int64_t)xr * g.ld_x);
         s.b[j] = *reinterpret_cast<const u32x4*>(wb + (int64_t)r * g.ld_w);
@@ -170,48 +163,46 @@ __device__ __forceinline__ void store_slice(uint8_t* stage, const Slice& s)
     const int r0 = threadIdx.x >> 3;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        const int r = r0 + 32 * j;
+        const int r = r0 + 64 * j;
         *reinterpret_cast<u32x4*>(stage + chunk_at(r, c)) = s.a[j];
-        *reinterpret_cast<u32x4*>(stage + kBM * kRowBytes + chunk_at(r, c)) = s.b[j];
+        *reinterpret_cast<u32x4*>(stage + kBM * kRowPitch + chunk_at(r, c)) = s.b[j];
     }
 }
 
-// acc[tm][tn] += the wave's quarter of the staged slice (4 steps of K = 16).
-__device__ __forceinline__ void mma_slice(f32x16 (&acc)[2][2], const uint8_t* stage, int wm,
+// acc[tm][tn] += the wave's 64 x 128 part of the staged slice (4 K steps of
+// 16): per step 2 A and 4 B fragments feed 8 MFMAs.
+__device__ __forceinline__ void mma_slice(f32x16 (&acc)[2][4], const uint8_t* stage, int wm,
                                           int wn, int lane)
 {
 #pragma unroll
     for (int kk = 0; kk < kBK / 16; ++kk) {
         const int c = 2 * kk + (lane >> 5);
-        bf16x8 a[2], b[2];
+        bf16x8 a[2], b[4];
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            const int ra = 64 * wm + 32 * t + (lane & 31);
-            const int rb = 64 * wn + 32 * t + (lane & 31);
-            a[t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(stage + chunk_at(ra, c)));
-            b[t] = __builtin_bit_cast(
-                bf16x8, *reinterpret_cast<const u32x4*>(stage + kBM * kRowBytes + chunk_at(rb, c)));
-        }
+        for (int t = 0; t < 2; ++t)
+            a[t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
+                                                   stage + chunk_at(64 * wm + 32 * t + (lane & 31), c)));
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+            b[t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
+                                                   stage + kBM * kRowPitch +
+                                                   chunk_at(128 * wn + 32 * t + (lane & 31), c)));
 #pragma unroll
         for (int tm = 0; tm < 2; ++tm)
 #pragma unroll
-            for (int tn = 0; tn < 2; ++tn)
+            for (int tn = 0; tn < 4; ++tn)
                 acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[tm], b[tn], acc[tm][tn], 0, 0, 0);
     }
 }
 
-// The K loop of one tile; leaves the FP32 tile in LDS as c[128][kCPitch].
+// The K loop of one tile. Ends with a barrier after the last slice's reads.
 __device__ __forceinline__ void gemm_tile(const Gemm& g, const TileRef& tr, uint8_t* smem,
-                                          float* c)
+                                          f32x16 (&acc)[2][4], int wm, int wn, int lane)
 {
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wave = uniform(threadIdx.x / kWave);
-    const int wm = wave >> 1, wn = wave & 1;
-    f32x16 acc[2][2];
 #pragma unroll
     for (int tm = 0; tm < 2; ++tm)
 #pragma unroll
-        for (int tn = 0; tn < 2; ++tn)
+        for (int tn = 0; tn < 4; ++tn)
             acc[tm][tn] = f32x16{};
     const int kb_count = g.k / kBK;
     Slice s;
@@ -227,19 +218,24 @@ __device__ __forceinline__ void gemm_tile(const Gemm& g, const TileRef& tr, uint
             store_slice(smem + ((kb + 1) & 1) * kStageBytes, s);
         __syncthreads();
     }
-    // accumulators -> LDS (the C tile overlays the operand stages, whose last
-    // reads finished at the barrier above)
+}
+
+// The waves of row band p (wm == p) write their 64 x 128 accumulator parts
+// into the C buffer: row 32 tm + 8 (i / 4) + 4 (lane / 32) + i % 4, column
+// 128 wn + 32 tn + lane % 32 (the v_mfma_f32_32x32x16 result layout).
+__device__ __forceinline__ void stage_accumulators(float* c, const f32x16 (&acc)[2][4], int wn,
+                                                   int lane)
+{
 #pragma unroll
     for (int tm = 0; tm < 2; ++tm)
 #pragma unroll
-        for (int tn = 0; tn < 2; ++tn)
+        for (int tn = 0; tn < 4; ++tn)
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const int row = 64 * wm + 32 * tm + (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3);
-                const int col = 64 * wn + 32 * tn + (lane & 31);
+                const int row = 32 * tm + (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3);
+                const int col = 128 * wn + 32 * tn + (lane & 31);
                 c[row * kCPitch + col] = acc[tm][tn][i];
             }
-    __syncthreads();
 }
 
 // ---- SwiGLU of FP32 values -------------------------------------------------
@@ -282,70 +278,80 @@ struct Bf16Out {
     int64_t ld_out;
 };
 
-// Fused epilogue of one tile: 128 rows x 4 NVFP4 blocks (each block = 32
-// interleaved accumulator columns [g x8, u x8, g x8, u x8] -> 16 outputs).
-// Thread t takes block t % 4 of rows t / 4 and t / 4 + 64.
-__device__ __forceinline__ void epilogue(const Gemm& g, const TileRef& tr, const float* c,
-                                         const FusedOut& o)
+// Fused epilogue of one 64-row pass: 64 rows x 8 NVFP4 blocks (each block =
+// 32 interleaved accumulator columns [g x8, u x8, g x8, u x8] -> 16
+// outputs); thread t takes block t % 8 of row t / 8.
+__device__ __forceinline__ void epilogue(const Gemm& g, const TileRef& tr, int pass,
+                                         const float* c, const FusedOut& o,
+                                         const nvfp4::RowScale& rs)
 {
-    const nvfp4::RowScale rs = nvfp4::row_scale(o.gs != nullptr ? o.gs[tr.e] : 1.0f);
-    const int bl = threadIdx.x & 3;
+    const int bl = threadIdx.x & 7;
+    const int row = threadIdx.x >> 3;
     const int inter = g.n / 2;
+    const float* src = c + row * kCPitch + 32 * bl;
+    float v[32];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const int row = (threadIdx.x >> 2) + 64 * h;
-        const float* src = c + row * kCPitch + 32 * bl;
-        float v[32];
+    for (int q = 0; q < 8; ++q) {
+        const float4 f = *reinterpret_cast<const float4*>(src + 4 * q);
+        v[4 * q] = f.x;
+        v[4 * q + 1] = f.y;
+        v[4 * q + 2] = f.z;
+        v[4 * q + 3] = f.w;
+    }
+    float y[16];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            const float4 f = *reinterpret_cast<const float4*>(src + 4 * q);
-            v[4 * q] = f.x;
-            v[4 * q + 1] = f.y;
-            v[4 * q + 2] = f.z;
-            v[4 * q + 3] = f.w;
-        }
-        float y[16];
+    for (int j = 0; j < 8; ++j) {
+        y[j] = swiglu_f32(v[j], v[8 + j]);
+        y[8 + j] = swiglu_f32(v[16 + j], v[24 + j]);
+    }
+    uint32_t sf;
+    const uint2 q = nvfp4::quantize16(y, rs, sf);
+    const int trow = kPassRows * pass + row;
+    if (trow < tr.rows) {
+        const int64_t grow = tr.row0 + trow;
+        const int64_t blk = grow * (inter / 16) + tr.n0 / 32 + bl;
+        *reinterpret_cast<uint2*>(o.packed + blk * 8) = q;
+        o.scales[blk] = (uint8_t)sf;
+        if (o.swiglu_out != nullptr) {
+            float* d = o.swiglu_out + grow * inter + tr.n0 / 2 + 16 * bl;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            y[j] = swiglu_f32(v[j], v[8 + j]);
-            y[8 + j] = swiglu_f32(v[16 + j], v[24 + j]);
-        }
-        uint32_t sf;
-        const uint2 q = nvfp4::quantize16(y, rs, sf);
-        if (row < tr.rows) {
-            const int64_t grow = tr.row0 + row;
-            const int64_t blk = grow * (inter / 16) + tr.n0 / 32 + bl;
-            *reinterpret_cast<uint2*>(o.packed + blk * 8) = q;
-            o.scales[blk] = (uint8_t)sf;
-            if (o.swiglu_out != nullptr) {
-                float* d = o.swiglu_out + grow * inter + tr.n0 / 2 + 16 * bl;
-#pragma unroll
-                for (int j = 0; j < 16; j += 4)
-                    *reinterpret_cast<float4*>(d + j) = make_float4(y[j], y[j + 1], y[j + 2], y[j + 3]);
-            }
+            for (int j = 0; j < 16; j += 4)
+                *reinterpret_cast<float4*>(d + j) = make_float4(y[j], y[j + 1], y[j + 2], y[j + 3]);
         }
     }
 }
 
-// BF16 epilogue: thread t writes 16-byte chunks t + 256 j (j = 0..7) of the
-// tile, chunk q = row q / 16, columns 8 (q % 16) .. +8.
-__device__ __forceinline__ void epilogue(const Gemm&, const TileRef& tr, const float* c,
-                                         const Bf16Out& o)
+// BF16 epilogue of one pass: thread t writes 16-byte chunks t + 512 j
+// (j = 0..3) of the 64 x 256 pass, chunk q = row q / 32, columns 8 (q % 32).
+__device__ __forceinline__ void epilogue(const Gemm&, const TileRef& tr, int pass, const float* c,
+                                         const Bf16Out& o, const nvfp4::RowScale&)
 {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < 4; ++j) {
         const int q = threadIdx.x + kThreads * j;
-        const int row = q >> 4;
-        const int col = 8 * (q & 15);
+        const int row = q >> 5;
+        const int col = 8 * (q & 31);
         const float4 f0 = *reinterpret_cast<const float4*>(c + row * kCPitch + col);
         const float4 f1 = *reinterpret_cast<const float4*>(c + row * kCPitch + col + 4);
         const u32x4 w = {pack_bf16x2(f0.x, f0.y), pack_bf16x2(f0.z, f0.w), pack_bf16x2(f1.x, f1.y),
                          pack_bf16x2(f1.z, f1.w)};
-        if (row < tr.rows)
-            *reinterpret_cast<u32x4*>(o.out + (int64_t)(tr.row0 + row) * o.ld_out + tr.n0 + col) = w;
+        const int trow = kPassRows * pass + row;
+        if (trow < tr.rows)
+            *reinterpret_cast<u32x4*>(o.out + (int64_t)(tr.row0 + trow) * o.ld_out + tr.n0 + col) = w;
     }
 }
 
+__device__ __forceinline__ float expert_scale(const FusedOut& o, int e)
+{
+    return o.gs != nullptr ? o.gs[e] : 1.0f;
+}
+__device__ __forceinline__ float expert_scale(const Bf16Out&, int) { return 1.0f; }
+
+// Persistent walk over the tiles. With a grid of a multiple of 8 workgroups
+// (one per CU, dealt round-robin to the 8 XCDs), XCD x takes the x-th eighth
+// of the tile list and its workgroups stride through it: concurrently
+// running workgroups of one XCD work on neighbouring tiles (the same row
+// tile, successive column tiles), which share their x rows in that XCD's L2.
 template <class Out>
 __global__ __launch_bounds__(kThreads) void moe_gemm_kernel(Gemm g, Out o)
 {
@@ -355,12 +361,30 @@ __global__ __launch_bounds__(kThreads) void moe_gemm_kernel(Gemm g, Out o)
     __shared__ int part[kThreads];
     const int row_tiles = build_tile_prefix(g, off, pre, part);
     const int tiles = row_tiles * (g.n / kBN);
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = uniform(threadIdx.x / kWave);
+    const int wm = wave >> 1, wn = wave & 1;
     float* c = reinterpret_cast<float*>(smem);
-    for (int tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
+    int first = blockIdx.x, step = gridDim.x, end = tiles;
+    if (gridDim.x % kXcds == 0) {
+        const int per = (tiles + kXcds - 1) / kXcds;
+        const int xcd = blockIdx.x % kXcds;
+        first = xcd * per + blockIdx.x / kXcds;
+        step = gridDim.x / kXcds;
+        end = min(tiles, (xcd + 1) * per);
+    }
+    f32x16 acc[2][4];
+    for (int tile = first; tile < end; tile += step) {
         const TileRef tr = tile_ref(g, off, pre, tile);
-        gemm_tile(g, tr, smem, c);
-        epilogue(g, tr, c, o);
-        __syncthreads();   // the next tile's operand stages overwrite the C tile
+        gemm_tile(g, tr, smem, acc, wm, wn, lane);
+        const nvfp4::RowScale rs = nvfp4::row_scale(expert_scale(o, tr.e));
+        for (int pass = 0; pass < kBM / kPassRows; ++pass) {
+            if (wm == pass)
+                stage_accumulators(c, acc, wn, lane);
+            __syncthreads();
+            epilogue(g, tr, pass, c, o, rs);
+            __syncthreads();   // the next pass (or tile) overwrites the buffer
+        }
     }
 }
 
@@ -403,7 +427,7 @@ nvfp4_status_t make_gemm(const uint16_t* x, const uint16_t* w, int64_t tokens, i
     g.n = (int)n;
     g.offsets = offsets;
     g.experts = experts;
-    const int64_t cap = (int64_t)kMi355xCUs * kBlocksPerCU;
+    const int64_t cap = kMi355xCUs;
     grid = (int)(bound < cap ? bound : cap);
     return NVFP4_SUCCESS;
 }

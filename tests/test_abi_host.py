@@ -187,14 +187,14 @@ def test_swiglu_bf16_validation(lib):
     assert sb(lib, rows=0, x=None, out=None) == OK
 
 
-def gf(lib, x=A16, w=A16, tokens=4, hidden=64, inter=64, ld_x=64, ld_w=64, offs=None, ne=0,
+def gf(lib, x=A16, w=A16, tokens=4, hidden=64, inter=128, ld_x=64, ld_w=64, offs=None, ne=0,
        gs=None, packed=A16, scales=A16, y=None):
     return lib.moe_l1_gemm_swiglu_nvfp4(x, w, tokens, hidden, inter, ld_x, ld_w, offs, ne, gs,
                                         packed, scales, y, None)
 
 
-def gb(lib, x=A16, w=A16, tokens=4, hidden=64, n=128, ld_x=64, ld_w=64, offs=None, ne=0,
-       out=A16, ld_out=128):
+def gb(lib, x=A16, w=A16, tokens=4, hidden=64, n=256, ld_x=64, ld_w=64, offs=None, ne=0,
+       out=A16, ld_out=256):
     return lib.moe_l1_gemm_bf16(x, w, tokens, hidden, n, ld_x, ld_w, offs, ne, out, ld_out, None)
 
 
@@ -206,20 +206,20 @@ def test_gemm_validation(lib):
         assert f(lib, hidden=96, ld_x=96, ld_w=96) == SHAPE         # hidden % 64
         assert f(lib, ne=2) == INVALID
         assert f(lib, offs=A16, ne=0) == INVALID
-        assert f(lib, offs=A16, ne=1025) == SHAPE
+        assert f(lib, offs=A16, ne=513) == SHAPE
         assert f(lib, x=A16 + 8) == MISALIGNED
         assert f(lib, w=A16 + 8) == MISALIGNED
         assert f(lib, ld_x=68) == MISALIGNED
         assert f(lib, x=None) == INVALID
         assert f(lib, hidden=0, ld_x=0, ld_w=0) == SHAPE
         assert f(lib, tokens=2**31) == SHAPE
-    assert gf(lib, inter=32) == SHAPE                              # 2 * inter % 128
+    assert gf(lib, inter=64) == SHAPE                              # 2 * inter % 256
     assert gf(lib, packed=None) == INVALID
     assert gf(lib, packed=A16 + 4) == MISALIGNED
     assert gf(lib, y=A16 + 8) == MISALIGNED
     assert gf(lib, tokens=0, x=None, w=None, packed=None, scales=None) == OK
-    assert gb(lib, n=64) == SHAPE
-    assert gb(lib, ld_out=64) == INVALID
+    assert gb(lib, n=128, ld_out=128) == SHAPE
+    assert gb(lib, ld_out=128) == INVALID
     assert gb(lib, out=A16 + 8) == MISALIGNED
     assert gb(lib, tokens=0, x=None, w=None, out=None) == OK
 

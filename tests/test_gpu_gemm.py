@@ -72,7 +72,7 @@ def gs_rows_of(g, gs, rows=None):
 
 
 @pytest.mark.parametrize("tokens,hidden,inter,experts,seed", [
-    (300, 256, 128, 5, 1), (1000, 512, 192, 9, 2), (129, 64, 64, 1, 3), (513, 1024, 256, 3, 4),
+    (300, 256, 128, 5, 1), (1000, 512, 384, 9, 2), (257, 64, 128, 1, 3), (513, 1024, 256, 3, 4),
     (256, 4096, 128, 2, 5)])
 def test_gemm_exact_operands(M, tokens, hidden, inter, experts, seed):
     g = W.moe_gemm(seed, tokens, hidden, inter, experts, exact=True)
@@ -101,7 +101,7 @@ def test_gemm_exact_operands(M, tokens, hidden, inter, experts, seed):
 
 
 def test_gemm_single_expert_no_offsets(M):
-    g = W.moe_gemm(5, 200, 128, 64, 1, exact=True)
+    g = W.moe_gemm(5, 200, 128, 128, 1, exact=True)
     acc32 = oracle.moe_l1_gemm(g.x, g.w1[0], None).astype(np.float32)
     r = run(M, g, None, offsets=False)
     P.assert_bytes_equal("bf16 GEMM, one expert", r["bf16"], oracle.f32_to_bf16(acc32))
