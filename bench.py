@@ -89,8 +89,8 @@ def checked(rc):
 
 
 class GpuStateSampler:
-    """Samples the GPU's clock level, board power and temperatures from sysfs
-    (read-only) every 10 ms in a background thread while a measurement runs,
+    """Samples the GPU's shader clock and board power from sysfs (read-only)
+    every 5 ms in a background thread while a measurement runs,
     so that the result can be reported with the clock and power state it was
     taken at. Nothing is pinned or changed."""
 
@@ -102,6 +102,7 @@ class GpuStateSampler:
         hw = sorted(glob.glob(os.path.join(self.base, "hwmon", "hwmon*"))) if self.base else []
         self.hwmon = hw[0] if hw else None
         self.samples = []
+        self.timed = False
         self._stop = threading.Event()
         self._thread = threading.Thread(target=self._run, daemon=True)
 
@@ -113,43 +114,52 @@ class GpuStateSampler:
             return None
 
     def _sample(self):
-        out = {}
+        out = {"timed": self.timed}
         t = self._read(os.path.join(self.base, "pp_dpm_sclk"))
         if t:
-            cur = [l.split(":", 1)[1].strip(" *") for l in t.splitlines() if l.endswith("*")]
-            out["sclk"] = cur[0] if cur else None
+            cur = [l.split(":", 1)[1].strip(" *").lower().replace("mhz", "") for l in t.splitlines()
+                   if l.endswith("*")]
+            out["sclk_MHz"] = float(cur[0]) if cur and cur[0].replace(".", "").isdigit() else None
         if self.hwmon:
             pw = self._read(os.path.join(self.hwmon, "power1_input"))
             out["power_W"] = int(pw) / 1e6 if pw else None
         return out
 
     def _run(self):
-        while not self._stop.wait(0.01):
+        while not self._stop.wait(0.005):
             self.samples.append(self._sample())
 
     def __enter__(self):
+        self.timed = False
         if self.base:
             self._thread.start()
         return self
+
+    def mark_timed(self, on: bool):
+        """Tag the following samples as taken inside (or outside) the timed region."""
+        self.timed = on
 
     def __exit__(self, *exc):
         self._stop.set()
         if self._thread.is_alive():
             self._thread.join()
 
+    @staticmethod
+    def _stats(v):
+        v = sorted(v)
+        return [round(v[0], 1), round(v[len(v) // 2], 1), round(v[-1], 1)] if v else None
+
     def report(self):
         if not self.base:
             return None
-        rep = {"samples": len(self.samples)}
-        levels = {}
-        for smp in self.samples:
-            if smp.get("sclk"):
-                levels[smp["sclk"]] = levels.get(smp["sclk"], 0) + 1
-        rep["sclk_level_counts"] = levels
-        pw = [smp["power_W"] for smp in self.samples if smp.get("power_W")]
-        if pw:
-            rep["power_W_min_mean_max"] = [round(min(pw), 1), round(sum(pw) / len(pw), 1),
-                                           round(max(pw), 1)]
+        rep = {}
+        for label, want in (("timed", True), ("settle_and_warmup", False)):
+            smp = [x for x in self.samples if x["timed"] == want]
+            rep[label] = {
+                "samples": len(smp),
+                "sclk_MHz_min_median_max": self._stats([x["sclk_MHz"] for x in smp if x.get("sclk_MHz")]),
+                "power_W_min_median_max": self._stats([x["power_W"] for x in smp if x.get("power_W")]),
+            }
         mclk = self._read(os.path.join(self.base, "pp_dpm_mclk"))
         if mclk:
             rep["mclk"] = [l.split(":", 1)[1].strip(" *") for l in mclk.splitlines()
@@ -179,7 +189,7 @@ def settle(fn, settle_ms):
         torch.cuda.synchronize()
 
 
-def time_launches(fn, steps, warmup, settle_ms=0.0, chunks=10):
+def time_launches(fn, steps, warmup, settle_ms=0.0, chunks=10, sampler=None):
     """Settle, warm up, then time `steps` back-to-back launches. Returns
     (wall seconds between two device synchronizations, device ms per launch
     from HIP events recorded on the launch stream around the whole region,
@@ -193,6 +203,8 @@ def time_launches(fn, steps, warmup, settle_ms=0.0, chunks=10):
     n_chunks = max(1, min(chunks, steps))
     bounds = [round(i * steps / n_chunks) for i in range(n_chunks + 1)]
     ev = [torch.cuda.Event(enable_timing=True) for _ in bounds]
+    if sampler is not None:
+        sampler.mark_timed(True)
     t0 = time.perf_counter()
     ev[0].record()
     for c in range(n_chunks):
@@ -201,6 +213,8 @@ def time_launches(fn, steps, warmup, settle_ms=0.0, chunks=10):
         ev[c + 1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    if sampler is not None:
+        sampler.mark_timed(False)
     per = [ev[c].elapsed_time(ev[c + 1]) / (bounds[c + 1] - bounds[c]) for c in range(n_chunks)]
     return wall, ev[0].elapsed_time(ev[-1]) / steps, per
 
@@ -480,7 +494,8 @@ def main():
     print("[bench] timing %d steps after %d warmup (%.0f ms settle)"
           % (args.steps, args.warmup, args.settle_ms), file=sys.stderr, flush=True)
     with GpuStateSampler() as sampler:
-        wall, kern_ms, per = time_launches(step, args.steps, args.warmup, args.settle_ms)
+        wall, kern_ms, per = time_launches(step, args.steps, args.warmup, args.settle_ms,
+                                           sampler=sampler)
     gpu_state = sampler.report()
     kern_ms_headline.append(kern_ms)
     ms_per_step = wall * 1e3 / args.steps
