@@ -11,6 +11,7 @@ cross-compiles the device code to assembly).
 * The compact SwiGLU pass rounds with v_cvt_pk_bf16_f32 (8 per lane block).
 * No scalar-memory writes or atomics anywhere in the device code: stores and
   atomics go through the vector memory path only.
+* No kernel uses scratch memory (no register spills), in either source.
 """
 import os
 import re
@@ -87,3 +88,16 @@ def test_no_scalar_memory_writes(isa):
     bad = sorted(set(re.findall(r"\bs_(?:store|atomic|buffer_store|buffer_atomic|dcache_wb|"
                                 r"scratch_store)\w*", isa)))
     assert not bad, bad
+
+
+def test_no_scratch_in_any_kernel(tmp_path):
+    from moe_swiglu_epilogue_amd import build as B
+    for src in (B.SRC, B.GEMM_SRC):
+        out = tmp_path / (os.path.basename(src) + ".o")
+        r = subprocess.run([B.HIPCC, *B.FLAGS, "-I", os.path.join(ROOT, "include"),
+                            "-Rpass-analysis=kernel-resource-usage", "--cuda-device-only", "-c", src,
+                            "-o", str(out)], capture_output=True, text=True, check=True)
+        sizes = re.findall(r"ScratchSize \[bytes/lane\]: (\d+)", r.stderr)
+        names = re.findall(r"Function Name: (\S+)", r.stderr)
+        assert sizes and len(sizes) == len(names), src
+        assert all(int(v) == 0 for v in sizes), list(zip(names, sizes))
