@@ -62,11 +62,18 @@ def load_calib():
 
 
 def kernel_source_hash() -> str:
+    """SHA-256 of the quantize kernels' sources with comments and blank lines
+    removed: any change to the code itself invalidates the stored counter
+    summary, an edit of a comment does not."""
+    import re
     h = hashlib.sha256()
     for rel in ("moe_swiglu_epilogue_amd/csrc/moe_nvfp4.hip",
                 "moe_swiglu_epilogue_amd/csrc/nvfp4_device.hpp"):
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        lines = [re.sub(r"//.*$", "", l).rstrip() for l in text.splitlines()]
+        h.update("\n".join(l for l in lines if l.strip()).encode())
     return h.hexdigest()
 
 

@@ -1,11 +1,18 @@
 // libmoe_nvfp4.so: HIP kernels for gfx950 and the C ABI declared in
 // include/moe_nvfp4.h.
 //
-// Work decomposition (all three kernels): one lane owns one NVFP4 block of
-// 16 output values; one wave64 owns a "tile" of 64 consecutive blocks of one
-// row, so the row index, its global scale and its base addresses are
-// wave-uniform (scalar registers). Tiles are numbered row-major and handed
-// to waves with a grid-stride loop.
+// Kernels: the fused SwiGLU + NVFP4 quantize and the standalone quantize
+// (quantize_tiles_kernel), the dequantize, the global-scale pre-pass
+// (amax_tiles_kernel and two small helpers) and the compact BF16 SwiGLU pass.
+// The grouped GEMM with the fused epilogue is in moe_gemm.hip.
+//
+// Work decomposition: one lane owns one NVFP4 block of 16 output values; one
+// wave64 owns a "tile" of 64 consecutive blocks of one row, so the row index
+// and its base addresses are wave-uniform (scalar registers). Tiles are
+// numbered row-major and handed to waves with a grid-stride loop: the
+// quantize, pre-pass and compact kernels walk them with a persistent grid
+// sized per kernel (workgroup waves and workgroups per CU measured on
+// MI355X), the dequantize with one tile per wave.
 //
 // Method: "nvfp4-megamoe-kernel" log, "NVFP4-1.1_APPROACH_PART_2.md"
 // (fused-epilogue design: SiLU(gate) and SwiGLU in FP32 registers, every two
@@ -21,7 +28,7 @@
 namespace {
 
 constexpr int kWave = 64;
-constexpr int kWavesPerBlock = 4;
+constexpr int kWavesPerBlock = 4;                  // dequantize workgroups
 constexpr int kThreads = kWave * kWavesPerBlock;
 constexpr int kTileBlocks = kWave;   // NVFP4 blocks per wave tile
 
