@@ -152,6 +152,30 @@ def test_gemm_random_operands(M, tokens, hidden, inter, experts, seed):
         % (codes, scl, worst))
 
 
+def test_gemm_many_small_experts(M):
+    """256 experts with Zipf(1.1) row counts over 16384 rows: most experts are
+    one partial 256-row tile, some are empty."""
+    g = W.moe_gemm(21, 16384, 512, 256, 256, exact=True)
+    counts = np.diff(g.offsets)
+    say("moe_l1_gemm 256 experts exact: rows per expert min %d max %d, empty %d"
+        % (counts.min(), counts.max(), (counts == 0).sum()))
+    acc32 = oracle.moe_l1_gemm(g.x, g.w1, g.offsets).astype(np.float32)
+    gs = np.float32(np.random.default_rng(21).uniform(0.05, 1.0, 256))
+    r = run(M, g, gs)
+    P.assert_bytes_equal("bf16 GEMM, 256 experts", r["bf16"], oracle.f32_to_bf16(acc32))
+    ry = oracle.swiglu_f32(acc32)
+    gsr = gs_rows_of(g, gs)
+    rp, rs, rbsf, rv = oracle.quantize_f32(ry, gsr, diag=True)
+    rep = P.fused_report(r["p"], r["s"], r["y"], rp, rs, ry, rbsf, rv, gsr)
+    say("256 experts exact", rep)
+    P.assert_fused_ok(rep, "fused GEMM, 256 experts")
+    gr = W.moe_gemm(22, 16384, 512, 256, 256)
+    rr = run(M, gr)
+    codes, scl, worst = check_random(gr, rr, np.arange(16384))
+    say("256 experts random: code mismatch %.2e, scale mismatch %.2e; worst err/tol %.3f"
+        % (codes, scl, worst))
+
+
 def test_gemm_prefill_shape_sampled(M):
     """32768 token rows, hidden 7168, I = 3072, 8 experts (Zipf): sampled rows
     (random, every expert's first and last row, the first rows of row tiles)."""
