@@ -543,7 +543,7 @@ def main():
                    "intermediate": INTER, "input": [ROWS, 2 * INTER],
                    "layout": "interleaved [gate x8, up x8]", "global_scale": 1.0,
                    "alg_bytes_per_step": ALG_BYTES, "parallelism": "single GPU",
-                   "settle_ms": args.settle_ms},
+                   "settle_ms": args.settle_ms, "input_sha256": W.sha256(w.x)},
         "pct_of_peak": round(100.0 * value / PEAK_HBM_GBS, 2),
         "elements_per_s": round(ROWS * INTER / (wall / args.steps), 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS,

@@ -1,0 +1,61 @@
+"""Brute force of the standalone quantizer on the GPU against the oracle, bit
+for bit, over the BF16 value space:
+
+* every positive finite BF16 value as a block's amax (so every block-scale
+  computation and FP8 encode the quantizer can reach from a BF16 input),
+  each block holding 15 neighbouring values below the amax with
+  alternating signs;
+* one amax per BF16 exponent with every smaller BF16 magnitude as elements
+  (random signs): about 2 million element quotients across 127 scales.
+
+Both runs use a power-of-two global scale (the v_rcp_f32 path of the element
+quotient) and a general one (the IEEE-division path)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import parity as P
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print("[gpu]", *a, flush=True)
+
+
+def amax_sweep_blocks():
+    a = np.arange(0x0001, 0x7F80, dtype=np.int64)             # positive finite BF16
+    j = np.arange(1, 16, dtype=np.int64)
+    vals = np.maximum(a[:, None] - 37 * j[None, :], 0)          # smaller patterns
+    sign = np.where(j % 2 == 1, 0x8000, 0)[None, :]
+    blocks = np.concatenate([a[:, None], vals | sign], axis=1)
+    return blocks.astype(np.uint16)
+
+
+def element_sweep_blocks(seed=5):
+    rng = np.random.default_rng(seed)
+    out = []
+    for amax in range(0x0100, 0x7F80, 0x100):                # one per exponent
+        v = np.arange(0, amax, dtype=np.int64)
+        v = v[:v.size - v.size % 15].reshape(-1, 15)
+        v |= np.where(rng.random(v.shape) < 0.5, 0x8000, 0)
+        out.append(np.concatenate([np.full((v.shape[0], 1), amax), v], axis=1))
+    return np.concatenate(out).astype(np.uint16)
+
+
+@pytest.mark.parametrize("gs", [1.0, 0.7], ids=["gs_pow2", "gs_general"])
+def test_standalone_quantize_over_bf16_space(gs):
+    import moe_swiglu_epilogue_amd as M
+    blocks = np.concatenate([amax_sweep_blocks(), element_sweep_blocks()])
+    nb = blocks.shape[0] - blocks.shape[0] % 16
+    x = blocks[:nb].reshape(-1, 256)                            # 16 blocks per row
+    say("standalone quantize over the BF16 space: %d blocks, gs %r" % (nb, gs))
+    xt = torch.from_numpy(x.view(np.int16)).cuda().view(torch.bfloat16)
+    g = np.float32(gs)
+    p, s = M.nvfp4_quantize(xt, torch.tensor([g], device="cuda"))
+    torch.cuda.synchronize()
+    rp, rs = oracle.quantize_bf16(x, np.full(x.shape[0], g, np.float32))
+    P.assert_bytes_equal("scales", s.cpu().numpy(), rs)
+    P.assert_bytes_equal("packed", p.cpu().numpy(), rp)
+    say("bit-exact: %d elements, %d distinct scale bytes" % (x.size, np.unique(rs).size))
