@@ -60,6 +60,7 @@
  * Preconditions checked on the host, before any HIP call (so they work on a
  * machine without a GPU) - a failing check returns without launching:
  *   rows, cols/inter >= 0; cols (inter) % 16 == 0; ld >= used columns;
+ *   the byte extent rows * ld * 2 of every strided buffer fits in int64;
  *   required pointers non-NULL; BF16 input base and row pitch 16-byte
  *   aligned; packed 8-byte aligned; FP32 outputs 16-byte aligned;
  *   num_experts >= 1 exactly when expert_offsets != NULL; rows < 2^31 and

@@ -406,6 +406,11 @@ nvfp4_status_t make_gemm(const uint16_t* x, const uint16_t* w, int64_t tokens, i
     if (tokens > INT32_MAX || hidden > INT32_MAX || n > INT32_MAX)
         return NVFP4_ERROR_UNSUPPORTED_SHAPE;
     const int experts = offsets != nullptr ? num_experts : 1;
+    // byte extents of x and of the weight stack must be addressable with
+    // int64 offsets, or no such buffers can exist
+    if ((tokens > 1 && ld_x > INT64_MAX / 2 / tokens) ||
+        (n > 0 && ld_w > INT64_MAX / 2 / (experts * n)))
+        return NVFP4_ERROR_INVALID_VALUE;
     // upper bound of the tiles the kernel will find: every expert may end in
     // a partial row tile
     const int64_t bound = ((tokens + kBM - 1) / kBM + experts) * (n / kBN);
@@ -479,7 +484,7 @@ nvfp4_status_t moe_l1_gemm_bf16(const uint16_t* x, const uint16_t* w1, int64_t t
                                   num_experts, g, grid);
     if (st != NVFP4_SUCCESS)
         return st;
-    if (ld_out < n)
+    if (ld_out < n || (tokens > 1 && ld_out > INT64_MAX / 2 / tokens))
         return NVFP4_ERROR_INVALID_VALUE;
     if (tokens == 0 || n == 0)
         return NVFP4_SUCCESS;

@@ -598,6 +598,10 @@ __global__ __launch_bounds__(kThreads) void nvfp4_dequantize_kernel(
 // ---------------------------------------------------------------------------
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
+// rows rows of pitch ld BF16 elements (rows, ld >= 0): the byte extent must be
+// addressable with int64 offsets, or no such buffer can exist.
+bool extent_ok(int64_t rows, int64_t ld) { return rows <= 1 || ld <= INT64_MAX / 2 / rows; }
+
 nvfp4_status_t check_experts(const int32_t* offsets, int32_t num_experts)
 {
     if (num_experts < 0)
@@ -718,7 +722,7 @@ nvfp4_status_t nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, int
                               int32_t num_experts, uint8_t* packed, uint8_t* scales,
                               hipStream_t stream)
 {
-    if (rows < 0 || cols < 0 || ld_x < cols)
+    if (rows < 0 || cols < 0 || ld_x < cols || !extent_ok(rows, ld_x))
         return NVFP4_ERROR_INVALID_VALUE;
     if (cols % 16 != 0)
         return NVFP4_ERROR_UNSUPPORTED_SHAPE;
@@ -729,7 +733,7 @@ nvfp4_status_t nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, int
         return NVFP4_SUCCESS;
     if (!x || !packed || !scales)
         return NVFP4_ERROR_INVALID_VALUE;
-    if (!aligned(x, 16) || (ld_x * 2) % 16 != 0 || !aligned(packed, 8))
+    if (!aligned(x, 16) || ld_x % 8 != 0 || !aligned(packed, 8))
         return NVFP4_ERROR_MISALIGNED;
     Geometry g;
     if ((st = make_geometry(rows, cols, g)) != NVFP4_SUCCESS)
@@ -745,7 +749,8 @@ nvfp4_status_t swiglu_nvfp4_quantize(const uint16_t* gate_up, int64_t rows, int6
                                      uint8_t* packed, uint8_t* scales, float* swiglu_out,
                                      hipStream_t stream)
 {
-    if (rows < 0 || inter < 0 || inter > INT64_MAX / 2 || ld_in < 2 * inter)
+    if (rows < 0 || inter < 0 || inter > INT64_MAX / 2 || ld_in < 2 * inter ||
+        !extent_ok(rows, ld_in))
         return NVFP4_ERROR_INVALID_VALUE;
     if (inter % 16 != 0)
         return NVFP4_ERROR_UNSUPPORTED_SHAPE;
@@ -756,7 +761,7 @@ nvfp4_status_t swiglu_nvfp4_quantize(const uint16_t* gate_up, int64_t rows, int6
         return NVFP4_SUCCESS;
     if (!gate_up || !packed || !scales)
         return NVFP4_ERROR_INVALID_VALUE;
-    if (!aligned(gate_up, 16) || (ld_in * 2) % 16 != 0 || !aligned(packed, 8) ||
+    if (!aligned(gate_up, 16) || ld_in % 8 != 0 || !aligned(packed, 8) ||
         (swiglu_out && !aligned(swiglu_out, 16)))
         return NVFP4_ERROR_MISALIGNED;
     Geometry g;
@@ -796,7 +801,7 @@ nvfp4_status_t nvfp4_global_scale(const uint16_t* x, int64_t rows, int64_t cols,
                                   const int32_t* expert_offsets, int32_t num_experts,
                                   float* amax, float* gs, hipStream_t stream)
 {
-    if (rows < 0 || cols < 0 || ld_x < cols)
+    if (rows < 0 || cols < 0 || ld_x < cols || !extent_ok(rows, ld_x))
         return NVFP4_ERROR_INVALID_VALUE;
     if (cols % 16 != 0)
         return NVFP4_ERROR_UNSUPPORTED_SHAPE;
@@ -810,7 +815,7 @@ nvfp4_status_t nvfp4_global_scale(const uint16_t* x, int64_t rows, int64_t cols,
     if (!empty) {
         if (!x)
             return NVFP4_ERROR_INVALID_VALUE;
-        if (!aligned(x, 16) || (ld_x * 2) % 16 != 0)
+        if (!aligned(x, 16) || ld_x % 8 != 0)
             return NVFP4_ERROR_MISALIGNED;
         if ((st = make_geometry(rows, cols, g)) != NVFP4_SUCCESS)
             return st;
@@ -824,7 +829,8 @@ nvfp4_status_t swiglu_nvfp4_global_scale(const uint16_t* gate_up, int64_t rows, 
                                          int32_t num_experts, float* amax, float* gs,
                                          hipStream_t stream)
 {
-    if (rows < 0 || inter < 0 || inter > INT64_MAX / 2 || ld_in < 2 * inter)
+    if (rows < 0 || inter < 0 || inter > INT64_MAX / 2 || ld_in < 2 * inter ||
+        !extent_ok(rows, ld_in))
         return NVFP4_ERROR_INVALID_VALUE;
     if (inter % 16 != 0)
         return NVFP4_ERROR_UNSUPPORTED_SHAPE;
@@ -838,7 +844,7 @@ nvfp4_status_t swiglu_nvfp4_global_scale(const uint16_t* gate_up, int64_t rows, 
     if (!empty) {
         if (!gate_up)
             return NVFP4_ERROR_INVALID_VALUE;
-        if (!aligned(gate_up, 16) || (ld_in * 2) % 16 != 0)
+        if (!aligned(gate_up, 16) || ld_in % 8 != 0)
             return NVFP4_ERROR_MISALIGNED;
         if ((st = make_geometry(rows, inter, g)) != NVFP4_SUCCESS)
             return st;
@@ -850,7 +856,8 @@ nvfp4_status_t swiglu_nvfp4_global_scale(const uint16_t* gate_up, int64_t rows, 
 nvfp4_status_t swiglu_bf16(const uint16_t* gate_up, int64_t rows, int64_t inter, int64_t ld_in,
                            uint16_t* out, int64_t ld_out, hipStream_t stream)
 {
-    if (rows < 0 || inter < 0 || inter > INT64_MAX / 2 || ld_in < 2 * inter || ld_out < inter)
+    if (rows < 0 || inter < 0 || inter > INT64_MAX / 2 || ld_in < 2 * inter || ld_out < inter ||
+        !extent_ok(rows, ld_in) || !extent_ok(rows, ld_out))
         return NVFP4_ERROR_INVALID_VALUE;
     if (inter % 16 != 0)
         return NVFP4_ERROR_UNSUPPORTED_SHAPE;
@@ -858,8 +865,8 @@ nvfp4_status_t swiglu_bf16(const uint16_t* gate_up, int64_t rows, int64_t inter,
         return NVFP4_SUCCESS;
     if (!gate_up || !out)
         return NVFP4_ERROR_INVALID_VALUE;
-    if (!aligned(gate_up, 16) || (ld_in * 2) % 16 != 0 || !aligned(out, 16) ||
-        (ld_out * 2) % 16 != 0)
+    if (!aligned(gate_up, 16) || ld_in % 8 != 0 || !aligned(out, 16) ||
+        ld_out % 8 != 0)
         return NVFP4_ERROR_MISALIGNED;
     Geometry g;
     nvfp4_status_t st = make_geometry(rows, inter, g);

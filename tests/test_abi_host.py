@@ -224,6 +224,27 @@ def test_gemm_validation(lib):
     assert gb(lib, tokens=0, x=None, w=None, out=None) == OK
 
 
+def test_pitch_extent_overflow_is_rejected(lib):
+    """A row pitch whose byte extent rows * ld * 2 leaves int64 cannot
+    describe a real buffer: every entry point says INVALID and computes
+    nothing with it (the sanitizer build checks that no arithmetic
+    overflows on the way)."""
+    big = 2**63 - 8
+    assert q(lib, ld=big) == INVALID
+    assert f(lib, ld=big) == INVALID
+    assert sb(lib, ld=big) == INVALID
+    assert sb(lib, ld_out=big) == INVALID
+    for fused in (False, True):
+        assert gsc(lib, fused, ld=big) == INVALID
+    for g in (gf, gb):
+        assert g(lib, ld_x=big) == INVALID
+        assert g(lib, ld_w=big) == INVALID
+        assert g(lib, offs=A16, ne=512, ld_w=2**63 // (2 * 512 * 256) + 8) == INVALID
+    assert gb(lib, ld_out=big) == INVALID
+    # one row has no extent beyond its own columns
+    assert q(lib, rows=1, ld=big, x=None) == INVALID   # still reaches the NULL check
+
+
 def test_binding_rejects_host_tensors():
     import moe_swiglu_epilogue_amd as M
     x = torch.zeros(4, 32, dtype=torch.bfloat16)
