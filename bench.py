@@ -14,8 +14,10 @@ quantize, the dequantize and the global-scale pre-pass on the same tensor;
 the two-pass ablation (compact BF16 SwiGLU, then the standalone quantize);
 in-repo read / copy kernels over the same input as HBM ceilings; the ragged
 256-expert workload (pre-pass, quantize with per-expert scales, dequantize);
-the decode-shaped workload over 8 rotating buffer sets; the MoE L1 grouped
-GEMM with the fused epilogue against the unfused flow and hipBLASLt.
+the decode-shaped workload over 8 rotating buffer sets; the two small
+cache-resident shapes (standalone 128 x 256, fused 512 x 4096) as launch
+rates; the MoE L1 grouped GEMM with the fused epilogue against the unfused
+flow and hipBLASLt.
 
 Every timed region is preceded by --settle-ms of untimed back-to-back
 launches (the clocks need ~30 ms of load to settle) and the warmup steps.
@@ -45,7 +47,7 @@ PMC_SUMMARY = os.path.join(ROOT, "profiles", "fused_quantize_kernel_prefill_pmc.
 CALIB_READ_BLOCKS = (1024, 1536, 8192, 49152)
 CALIB_COPY_BLOCKS = (512, 8192, 49152)
 SECONDARY = ("nvfp4_quantize", "nvfp4_dequantize", "global_scale", "two_pass", "calib_read",
-             "calib_copy", "ragged", "decode", "gemm")
+             "calib_copy", "ragged", "decode", "small", "gemm")
 PEAK_BF16_TFLOPS = 2500.0           # MI355X dense BF16 matrix peak
 
 
@@ -243,6 +245,32 @@ def measure(name, fn, nbytes, elems, steps, settle_ms, extra=None):
     return out
 
 
+def graph_ms(fn, launches=50, replays=20):
+    """Device ms per launch of `fn` captured `launches` times into one HIP
+    graph and replayed `replays` times (events around the replays): what a
+    launch costs without the host's enqueue work, for launch-bound shapes."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(3):
+            fn()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(launches):
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(replays):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / (launches * replays)
+
+
 def cpu_baseline(x):
     """The CPU oracle on the same prefill input: all host threads over the
     whole workload (median of 3), plus one thread over 16384 rows."""
@@ -406,6 +434,37 @@ def secondary_figures(M, W, x, packed, scales, args, dev):
             "decode-shaped swiglu_nvfp4_quantize", rotating, dr * di * BYTES_PER_ELEM, dr * di,
             max(st, 80), ms, {"shape": [dr, 2 * di], "note": "8 rotating input/output sets"})
         del sets
+    if "small" in want:
+        # the two small shapes: 128 x 256 standalone (84 KB moved) and
+        # 512 x 4096 fused (4.8 MB). Both live in the Infinity Cache and a
+        # launch is a few microseconds, so these are back-to-back launch
+        # rates, not HBM figures.
+        w = W.standalone()
+        xs = torch.from_numpy(w.x.view(np.int16)).to(dev).view(torch.bfloat16)
+        ps = torch.empty((w.rows, w.out_cols // 2), dtype=torch.uint8, device=dev)
+        ss = torch.empty((w.rows, w.out_cols // 16), dtype=torch.uint8, device=dev)
+        def small(name, fn, nbytes, elems, shape):
+            r = measure(name, fn, nbytes, elems, max(st, 200), ms,
+                        {"shape": shape, "note": "cache-resident, launch-bound; ms is the eager "
+                         "launch rate through the Python binding, graph_ms the device time per "
+                         "launch inside a HIP graph of 50 launches"})
+            gm = graph_ms(fn)
+            r["graph_ms"] = round(gm, 5)
+            r["graph_elements_per_s"] = round(elems / gm * 1e3, 1)
+            r["graph_GB_s"] = round(nbytes / gm / 1e6, 1)
+            return r
+        sec["small_standalone"] = small(
+            "standalone 128x256 nvfp4_quantize", lambda: M.nvfp4_quantize(xs, packed=ps, scales=ss),
+            w.rows * w.out_cols * 2.5625, w.rows * w.out_cols, [w.rows, w.out_cols])
+        w = W.fused_small()
+        xf = torch.from_numpy(w.x.view(np.int16)).to(dev).view(torch.bfloat16)
+        pf = torch.empty((w.rows, w.out_cols // 2), dtype=torch.uint8, device=dev)
+        sf = torch.empty((w.rows, w.out_cols // 16), dtype=torch.uint8, device=dev)
+        sec["small_fused"] = small(
+            "fused 512x4096 swiglu_nvfp4_quantize",
+            lambda: M.swiglu_nvfp4_quantize(xf, packed=pf, scales=sf),
+            w.rows * w.out_cols * BYTES_PER_ELEM, w.rows * w.out_cols, [w.rows, 2 * w.out_cols])
+        del xs, ps, ss, xf, pf, sf
     if "gemm" in want:
         sec["moe_l1_gemm"] = gemm_figures(M, W, args)
     return sec

@@ -171,7 +171,7 @@ struct FusedBlock {
     // the prefill shape, 12 or 16 waves per CU are 4-6% slower and 4 waves
     // per CU 25% slower.
     static constexpr int kWaves = 8;
-    static constexpr int kBlocksPerCU = 1;   // 32 KB sigma table + 8 x 4.25 KB staging
+    static constexpr int kBlocksPerCU = 1;   // 48 KB sigma table + 8 x 4.25 KB staging
     static constexpr bool kSigmaTable = true;
     // y = silu(gate) * up = (gate * up) * sigma(gate) for the 16 outputs.
     __device__ static __forceinline__ void values(const u32x4 (&c)[4], float (&y)[16],
@@ -181,8 +181,12 @@ struct FusedBlock {
         const uint32_t uw[8] = {c[1].x, c[1].y, c[1].z, c[1].w, c[3].x, c[3].y, c[3].z, c[3].w};
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const float s0 = *reinterpret_cast<const float*>(sig + nvfp4::sigma_offset<0>(gw[i]));
-            const float s1 = *reinterpret_cast<const float*>(sig + nvfp4::sigma_offset<16>(gw[i]));
+            uint32_t o = nvfp4::sigma_offsets(gw[i]);
+            // keep o whole: one shift-or builds it, then one mask and one
+            // shift split it (the compiler would otherwise rebuild each half)
+            asm("" : "+v"(o));
+            const float s0 = *reinterpret_cast<const float*>(sig + (o & 0xffffu));
+            const float s1 = *reinterpret_cast<const float*>(sig + (o >> 16));
             y[2 * i] = (nvfp4::bf16_lo(gw[i]) * nvfp4::bf16_lo(uw[i])) * s0;
             y[2 * i + 1] = (nvfp4::bf16_hi(gw[i]) * nvfp4::bf16_hi(uw[i])) * s1;
         }
@@ -333,8 +337,11 @@ template <class Block>
 __device__ __forceinline__ void fill_sigma_table(float* sig)
 {
     if constexpr (Block::kSigmaTable) {
-        for (int i = threadIdx.x; i < nvfp4::kSigEntries; i += Block::kWaves * kWave)
-            sig[i] = nvfp4::sigma_entry(i);
+        for (int i = threadIdx.x; i < 2 * nvfp4::kSigSpan; i += Block::kWaves * kWave) {
+            const int m = i & (nvfp4::kSigSpan - 1);
+            const bool neg = i >= nvfp4::kSigSpan;
+            sig[m + (neg ? nvfp4::kSigNeg : 0)] = nvfp4::sigma_entry(m, neg);
+        }
     }
 }
 
@@ -347,7 +354,7 @@ __global__ __launch_bounds__(Block::kWaves * kWave) void quantize_tiles_kernel(
 {
     constexpr int kWaves = Block::kWaves;
     __shared__ u32x4 stage[kWaves][kStageSlots(Block::P)];
-    __shared__ float sig[Block::kSigmaTable ? nvfp4::kSigEntries : 1];
+    __shared__ float sig[Block::kSigmaTable ? nvfp4::kSigFloats : 1];
     __shared__ ExpertTable tab;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = uniform(threadIdx.x / kWave);
@@ -418,7 +425,7 @@ __global__ __launch_bounds__(FusedBlock::kWaves * kWave) void swiglu_bf16_kernel
     using Block = FusedBlock;
     constexpr int kWaves = Block::kWaves;
     __shared__ u32x4 stage[kWaves][kStageSlots(Block::P)];
-    __shared__ float sig[nvfp4::kSigEntries];
+    __shared__ float sig[nvfp4::kSigFloats];
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = uniform(threadIdx.x / kWave);
     u32x4* lds = stage[wave];
@@ -485,7 +492,7 @@ __global__ __launch_bounds__(Block::kWaves * kWave) void amax_tiles_kernel(
     constexpr int kWaves = Block::kWaves;
     static_assert(kMaxScaleGroups <= kLdsExperts, "experts of a global-scale call fit in LDS");
     __shared__ u32x4 stage[kWaves][kStageSlots(Block::P)];
-    __shared__ float sig[Block::kSigmaTable ? nvfp4::kSigEntries : 1];
+    __shared__ float sig[Block::kSigmaTable ? nvfp4::kSigFloats : 1];
     __shared__ uint32_t part[kMaxScaleGroups];
     __shared__ ExpertTable tab;
     const int lane = threadIdx.x & (kWave - 1);

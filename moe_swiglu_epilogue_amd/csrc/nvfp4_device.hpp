@@ -42,39 +42,51 @@ __device__ __forceinline__ float swiglu_bf16(float g, float u)
 // ---- SwiGLU through a table of sigmoid values ------------------------------
 // A BF16 gate has 65536 values; sigma(g) = 1 / (1 + e^-g) only varies in FP32
 // for 2^-24 <= |g| < 256. The table holds sigma for every BF16 magnitude in
-// that range (exponent field 103..134, all 128 mantissas) and both signs:
-// entry 2 (x - kSigLo) + sign, x = the 15 magnitude bits. Magnitudes below
-// the range read the first row (sigma rounds to 1/2 there: |sigma - 1/2| <
-// 2^-26), magnitudes above it the last (sigma is 1, or below the FP32 range
-// for negative g). Entries are computed once per workgroup with
-// sigma_entry(); a lookup then replaces exp and rcp per element.
+// that range (exponent field 103..134, all 128 mantissas: kSigSpan values)
+// and both signs. Positive gates use floats [0, kSigSpan), negative ones
+// [kSigNeg, kSigNeg + kSigSpan): kSigNeg * 4 = 32768 is bit 15 of a BF16
+// half-word, so the sign bit serves as the sign's byte offset where it
+// stands (the floats in between are unused). Magnitudes below the range read
+// the first entry (sigma rounds to 1/2 there: |sigma - 1/2| < 2^-26),
+// magnitudes above it the last (sigma is 1, or below the FP32 range for
+// negative g). Entries are computed once per workgroup with sigma_entry(); a
+// lookup then replaces exp and rcp per element.
 constexpr uint32_t kSigLo = 103u << 7;
 constexpr uint32_t kSigHi = (134u << 7) | 127u;
-constexpr int kSigEntries = 2 * (int)(kSigHi - kSigLo + 1);   // 8192 (32 KB)
+constexpr int kSigSpan = (int)(kSigHi - kSigLo + 1);   // 4096
+constexpr int kSigNeg = 8192;
+constexpr int kSigFloats = kSigNeg + kSigSpan;         // 12288 (48 KB, 16 KB unused)
+static_assert(kSigNeg * 4 == 0x8000 && kSigSpan * 4 <= 0x8000, "sign bit is the offset");
 
-// sigma(g) for table entry i: the exp2 argument -g * kLog2eHi is exact for a
-// BF16 gate, its tail is folded in by one fma, and the final reciprocal is a
-// correctly rounded division (about 2 ulp overall).
-__device__ __forceinline__ float sigma_entry(int i)
+// sigma(g) for magnitude index m (g's 15 magnitude bits less kSigLo) and
+// sign neg: the exp2 argument -g * kLog2eHi is exact for a BF16 gate, its
+// tail is folded in by one fma, and the final reciprocal is a correctly
+// rounded division (about 2 ulp overall).
+__device__ __forceinline__ float sigma_entry(int m, bool neg)
 {
     const float kLog2eHi = 0x1.7154p+0f;          // log2 e to 16 bits
     const float kLog2eLoLn2 = 0x1.480fb6p-18f;    // (log2 e - kLog2eHi) ln 2
-    const float a = __uint_as_float((kSigLo + (uint32_t)(i >> 1)) << 16);
-    const float g = (i & 1) ? -a : a;
+    const float a = __uint_as_float((kSigLo + (uint32_t)m) << 16);
+    const float g = neg ? -a : a;
     const float e = __builtin_amdgcn_exp2f(-g * kLog2eHi);
     const float c = __builtin_fmaf(-g, kLog2eLoLn2, 1.0f);
     return 1.0f / __builtin_fmaf(e, c, 1.0f);
 }
 
-// Byte offset of the table entry for the BF16 gate held in bits [lo, lo+16)
-// of w (lo = 0 or 16).
-template <int lo>
-__device__ __forceinline__ uint32_t sigma_offset(uint32_t w)
+// Byte offsets of the table entries for the two BF16 gates of w, in the
+// matching halves of the result. Both halves are done at once in packed
+// 16-bit arithmetic: magnitude bits less kSigLo saturating at 0
+// (v_pk_sub_u16 with clamp), capped at kSigSpan - 1 (v_pk_min_u16), times 4
+// (at most 14 bits, so one 32-bit shift cannot carry across halves), and the
+// sign bits kept in place.
+__device__ __forceinline__ uint32_t sigma_offsets(uint32_t w)
 {
-    const uint32_t x = lo == 0 ? (w & 0x7fffu) : ((w >> 16) & 0x7fffu);
-    const uint32_t xc = min(max(x, kSigLo), kSigHi);   // v_med3_u32
-    const uint32_t sign4 = lo == 0 ? ((w >> 13) & 4u) : ((w >> 29) & 4u);
-    return (xc - kSigLo) * 8u + sign4;
+    typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+    const u16x2 lo = {(unsigned short)kSigLo, (unsigned short)kSigLo};
+    const u16x2 top = {(unsigned short)(kSigSpan - 1), (unsigned short)(kSigSpan - 1)};
+    u16x2 m = __builtin_bit_cast(u16x2, w & 0x7fff7fffu);
+    m = __builtin_elementwise_min(__builtin_elementwise_sub_sat(m, lo), top);
+    return (__builtin_bit_cast(uint32_t, m) << 2) | (w & 0x80008000u);
 }
 
 // ---- FP8 E4M3 ("fn") encode of a non-negative block scale -------------------
