@@ -203,7 +203,9 @@ nvfp4_status_t swiglu_bf16(const uint16_t *gate_up, int64_t rows, int64_t inter,
  *   not NULL, y [tokens][inter] FP32.
  * expert_offsets: as above (NULL: one expert, w1[0], owns every row);
  * num_experts <= 512. Shapes: hidden % 64 == 0, inter % 128 == 0, ld_x and
- * ld_w >= hidden and multiples of 8; x and w1 16-byte aligned. One kernel.
+ * ld_w >= hidden, multiples of 8 and below 2^22 (NVFP4_ERROR_UNSUPPORTED_SHAPE
+ * otherwise: a 256-row operand window is addressed with 32-bit offsets); x
+ * and w1 16-byte aligned. One kernel.
  * hidden == 0 is NVFP4_ERROR_UNSUPPORTED_SHAPE; tokens == 0 or inter == 0
  * is a no-op.
  */

@@ -19,17 +19,28 @@
 // output column n (the weight stored [out][in], K contiguous). Output column
 // n of the L1 GEMM follows the interleaved layout [gate x8, up x8, ...].
 //
-// Decomposition: one workgroup of 8 waves per CU computes 256 x 256 output
-// tiles; wave (wm, wn) owns rows 64 wm .. +64 and columns 128 wn .. +128 as
-// 2 x 4 MFMA tiles of 32 x 32. The K loop stages 256 x 64 slices of x and w
-// in LDS (double-buffered, rows padded against bank conflicts) and
-// prefetches the next slice into registers while the matrix cores work on
-// the current one. 256 x 256 tiles halve the operand traffic per FLOP of
-// 128 x 128 ones (measured: 128 x 128 tiles pulled 13 TB/s through L2 and
-// held the matrix cores at 35%). Tiles are enumerated per expert
-// (ceil(rows_e / 256) row tiles each, from a prefix sum the workgroup builds
-// once in LDS) and handed to a persistent, XCD-aware grid. The epilogue runs
-// in four 64-row passes through an LDS buffer that overlays the stages.
+// Decomposition: one workgroup of 4 waves per CU (one wave per SIMD)
+// computes 256 x 256 output tiles; wave (wm, wn) owns rows 128 wm .. +128
+// and columns 128 wn .. +128 as 4 x 4 MFMA tiles of 32 x 32, whose 256
+// accumulator registers per lane sit in the SIMD's accumulation registers.
+// The K loop stages 256 x 64 slices of x and w in LDS (double-buffered, rows
+// padded against bank conflicts); the slices arrive by buffer loads two
+// slices ahead, through two register sets, and each pass is
+// software-pipelined by hand (fragment reads for the next K step and the LDS
+// writes of the next slice interleaved with the MFMAs).
+//
+// What bounds it: a 256 x 256 tile does 128 FLOP per byte of operand slices,
+// so the matrix-core peak would need about 19 TB/s of operands from L2. With
+// the loads taken out (a timing probe) the kernel runs at 60% of the BF16
+// peak, with the loads and LDS traffic out at 83%. The operand reads
+// therefore set the pace, and the walk order is chosen for cache reuse:
+// tiles of the same row group and expert run together on every XCD. 256 x
+// 256 is the largest tile the accumulation registers hold (4 SIMDs x 64 KB).
+//
+// Tiles are enumerated per expert (ceil(rows_e / 256) row tiles each, from a
+// prefix sum the workgroup builds once in LDS) and handed to a persistent,
+// XCD-aware grid. The epilogue runs in four 64-row passes through an LDS
+// buffer that overlays the stages.
 #include "../../include/moe_nvfp4.h"
 #include "nvfp4_device.hpp"
 
@@ -40,7 +51,11 @@ namespace {
 
 constexpr int kWave = 64;
 constexpr int kBM = 256, kBN = 256, kBK = 64;
-constexpr int kThreads = 512;                             // 8 waves: 4 x 2 wave tiles of 64 x 128
+constexpr int kThreads = 256;                             // 4 waves: 2 x 2 wave tiles of 128 x 128
+constexpr int kWaveM = 128, kWaveN = 128;
+constexpr int kTM = kWaveM / 32, kTN = kWaveN / 32;       // 4 x 4 MFMA tiles per wave
+constexpr int kLoadRows = kThreads / 8;                   // rows one slice load instruction covers
+constexpr int kSliceLoads = kBM / kLoadRows;              // 16-byte chunks of x (and of w) per thread
 constexpr int kMaxExperts = 512;
 constexpr int kRowBytes = kBK * 2;                        // 128 data bytes per staged row
 constexpr int kRowPitch = kRowBytes + 16;                 // one 16-byte pad per row
@@ -52,6 +67,7 @@ constexpr int kLdsBytes = 2 * kStageBytes;
 static_assert(kCBytes <= kLdsBytes, "the C buffer overlays the operand stages");
 constexpr int kMi355xCUs = 256;
 constexpr int kXcds = 8;
+constexpr int64_t kMaxPitch = int64_t(1) << 22;            // elements; 256 rows < 2^31 bytes
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -60,6 +76,11 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+template <int v>
+struct Int {
+    static constexpr int value = v;
+};
 
 // Byte offset of 16-byte chunk c (0..7) of staged row r. Rows are padded to
 // 144 bytes, so the 16 rows whose chunks one LDS cycle serves (a wave reads
@@ -86,8 +107,9 @@ struct TileRef {
 };
 
 // Tile prefix in LDS: off[e] (clamped to [0, tokens]) and pre[e] = row tiles
-// of experts 0..e-1 (thread t counts expert t; Hillis-Steele scan). Returns
-// the total number of row tiles.
+// of experts 0..e-1 (thread t counts experts 2t and 2t + 1; Hillis-Steele
+// scan over the threads). Returns the total number of row tiles.
+static_assert(2 * kThreads >= kMaxExperts, "two experts per thread in the tile prefix");
 __device__ int build_tile_prefix(const Gemm& g, int* off, int* pre, int* part)
 {
     const int t = threadIdx.x;
@@ -97,8 +119,10 @@ __device__ int build_tile_prefix(const Gemm& g, int* off, int* pre, int* part)
         off[i] = min(max(o, 0), g.tokens);
     }
     __syncthreads();
-    const int cnt = t < E ? (max(off[t + 1] - off[t], 0) + kBM - 1) / kBM : 0;
-    part[t] = cnt;
+    const int e0 = 2 * t, e1 = 2 * t + 1;
+    const int c0 = e0 < E ? (max(off[e0 + 1] - off[e0], 0) + kBM - 1) / kBM : 0;
+    const int c1 = e1 < E ? (max(off[e1 + 1] - off[e1], 0) + kBM - 1) / kBM : 0;
+    part[t] = c0 + c1;
     __syncthreads();
     for (int d = 1; d < kThreads; d <<= 1) {
         const int v = t >= d ? part[t - d] : 0;
@@ -106,19 +130,41 @@ __device__ int build_tile_prefix(const Gemm& g, int* off, int* pre, int* part)
         part[t] += v;
         __syncthreads();
     }
-    if (t < E)
-        pre[t + 1] = part[t];
+    if (e0 < E)
+        pre[e0 + 1] = part[t] - c1;
+    if (e1 < E)
+        pre[e1 + 1] = part[t];
     if (t == 0)
         pre[0] = 0;
     __syncthreads();
     return pre[E];
 }
 
+// Walk order: tiles are taken column-major within groups of kGroupRows row
+// tiles (row tile = group base + i % rows, column tile = i / rows for the
+// group's i-th tile). The 32 consecutive tiles one XCD runs together then
+// cover 8 row tiles x 4 column tiles and share their x and w slices in that
+// XCD's L2, where a row-major walk has each workgroup stream its own w
+// slice. A bijection of [0, row_tiles * nt). Measured on the 8-expert
+// problem: groups of 8 rows beat 4 and 16 by 3%, and 2 by 7%.
+constexpr int kGroupRows = 8;
+
+__device__ __forceinline__ void tile_coords(int tile, int row_tiles, int nt, int& mt, int& ct)
+{
+    const int group = tile / (kGroupRows * nt);
+    const int first = group * kGroupRows;
+    const int rows = min(kGroupRows, row_tiles - first);
+    const int i = tile - group * kGroupRows * nt;
+    mt = first + i % rows;
+    ct = i / rows;
+}
+
 __device__ __forceinline__ TileRef tile_ref(const Gemm& g, const int* off, const int* pre,
-                                            int tile)
+                                            int row_tiles, int tile)
 {
     const int nt = g.n / kBN;
-    const int mt = tile / nt;
+    int mt, ct;
+    tile_coords(tile, row_tiles, nt, mt, ct);
     int lo = 0, hi = g.experts;                 // largest e with pre[e] <= mt
     while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
@@ -131,29 +177,56 @@ __device__ __forceinline__ TileRef tile_ref(const Gemm& g, const int* off, const
     r.e = uniform(lo);
     r.row0 = uniform(off[lo] + (mt - pre[lo]) * kBM);
     r.rows = uniform(min(kBM, off[lo + 1] - r.row0));
-    r.n0 = uniform((tile - mt * nt) * kBN);
+    r.n0 = uniform(ct * kBN);
     return r;
 }
 
-// 256 x 64 slices of x (rows row0.., clamped to the tile's valid rows) and
-// w (rows n0..) at K offset k0: thread t loads 16-byte chunk t % 8 of rows
-// t / 8 + 64 j, j = 0..3, of each.
-struct Slice {
-    u32x4 a[4], b[4];
+// A tile's operand windows as buffer resources (base and size in SGPRs):
+// x rows row0 .. row0 + rows and w rows n0 .. n0 + 256 of expert e. A row
+// of x past a partial tile lies outside its window, and the hardware range
+// check returns zeros for it (those rows are computed, never stored). Each
+// lane keeps one 32-bit offset per operand: chunk t % 8 of row t / 8.
+// Windows are at most 256 rows of pitch < 2^22 elements: under 2^31 bytes.
+struct TileSrc {
+    __amdgpu_buffer_rsrc_t x, w;
+    int vx, vw;              // lane offsets (bytes)
+    int row_x, row_w;        // bytes between rows kLoadRows apart
 };
 
-__device__ __forceinline__ void load_slice(Slice& s, const Gemm& g, const TileRef& tr, int k0)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t window(const uint16_t* base, int bytes)
 {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), (short)0, bytes,
+                                             0x00020000);
+}
+
+__device__ __forceinline__ TileSrc tile_src(const Gemm& g, const TileRef& tr)
+{
+    TileSrc t;
+    t.x = window(g.x + (int64_t)tr.row0 * g.ld_x, tr.rows * (int)g.ld_x * 2);
+    t.w = window(g.w + (int64_t)tr.e * g.w_expert + (int64_t)tr.n0 * g.ld_w, kBN * (int)g.ld_w * 2);
     const int c = threadIdx.x & 7;
     const int r0 = threadIdx.x >> 3;
-    const uint16_t* wb = g.w + (int64_t)tr.e * g.w_expert + (int64_t)tr.n0 * g.ld_w + k0 + 8 * c;
-    const uint16_t* xb = g.x + k0 + 8 * c;
+    t.vx = r0 * (int)g.ld_x * 2 + 16 * c;
+    t.vw = r0 * (int)g.ld_w * 2 + 16 * c;
+    t.row_x = kLoadRows * (int)g.ld_x * 2;
+    t.row_w = kLoadRows * (int)g.ld_w * 2;
+    return t;
+}
+
+// 256 x 64 slices of x and w at K offset k0: thread t loads 16-byte chunk
+// t % 8 of rows t / 8 + 32 j, j = 0..7, of each.
+struct Slice {
+    u32x4 a[kSliceLoads], b[kSliceLoads];
+};
+
+__device__ __forceinline__ void load_slice(Slice& s, const TileSrc& src, int k0)
+{
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int r = r0 + 64 * j;
-        const int xr = tr.row0 + min(r, tr.rows - 1);
-        s.a[j] = *reinterpret_cast<const u32x4*>(xb + (int64_t)xr * g.ld_x);
-        s.b[j] = *reinterpret_cast<const u32x4*>(wb + (int64_t)r * g.ld_w);
+    for (int j = 0; j < kSliceLoads; ++j) {
+        s.a[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                               src.x, src.vx, j * src.row_x + 2 * k0, 0));
+        s.b[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                               src.w, src.vw, j * src.row_w + 2 * k0, 0));
     }
 }
 
@@ -162,80 +235,154 @@ __device__ __forceinline__ void store_slice(uint8_t* stage, const Slice& s)
     const int c = threadIdx.x & 7;
     const int r0 = threadIdx.x >> 3;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int r = r0 + 64 * j;
+    for (int j = 0; j < kSliceLoads; ++j) {
+        const int r = r0 + kLoadRows * j;
         *reinterpret_cast<u32x4*>(stage + chunk_at(r, c)) = s.a[j];
         *reinterpret_cast<u32x4*>(stage + kBM * kRowPitch + chunk_at(r, c)) = s.b[j];
     }
 }
 
-// acc[tm][tn] += the wave's 64 x 128 part of the staged slice (4 K steps of
-// 16): per step 2 A and 4 B fragments feed 8 MFMAs.
-__device__ __forceinline__ void mma_slice(f32x16 (&acc)[2][4], const uint8_t* stage, int wm,
-                                          int wn, int lane)
+// The wave's MFMA operands for one 16-deep K step kk of the staged slice:
+// 4 A fragments (rows 128 wm + 32 t + lane % 32) and 4 B fragments (columns
+// 128 wn + 32 t + lane % 32), each 8 K values starting at 8 (2 kk + lane / 32).
+struct Frags {
+    bf16x8 a[kTM], b[kTN];
+};
+
+__device__ __forceinline__ void read_frags(Frags& f, const uint8_t* stage, int kk, int wm, int wn,
+                                           int lane)
 {
+    const int c = 2 * kk + (lane >> 5);
 #pragma unroll
-    for (int kk = 0; kk < kBK / 16; ++kk) {
-        const int c = 2 * kk + (lane >> 5);
-        bf16x8 a[2], b[4];
+    for (int t = 0; t < kTM; ++t)
+        f.a[t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
+                                                stage + chunk_at(kWaveM * wm + 32 * t + (lane & 31), c)));
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
-            a[t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
-                                                   stage + chunk_at(64 * wm + 32 * t + (lane & 31), c)));
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-            b[t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
-                                                   stage + kBM * kRowPitch +
-                                                   chunk_at(128 * wn + 32 * t + (lane & 31), c)));
-#pragma unroll
-        for (int tm = 0; tm < 2; ++tm)
-#pragma unroll
-            for (int tn = 0; tn < 4; ++tn)
-                acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[tm], b[tn], acc[tm][tn], 0, 0, 0);
-    }
+    for (int t = 0; t < kTN; ++t)
+        f.b[t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
+                                                stage + kBM * kRowPitch +
+                                                chunk_at(kWaveN * wn + 32 * t + (lane & 31), c)));
 }
 
-// The K loop of one tile. Ends with a barrier after the last slice's reads.
-__device__ __forceinline__ void gemm_tile(const Gemm& g, const TileRef& tr, uint8_t* smem,
-                                          f32x16 (&acc)[2][4], int wm, int wn, int lane)
+// acc[tm][tn] += A fragment tm x B fragment tn: 16 MFMAs.
+__device__ __forceinline__ void mma_step(f32x16 (&acc)[kTM][kTN], const Frags& f)
 {
 #pragma unroll
-    for (int tm = 0; tm < 2; ++tm)
+    for (int tm = 0; tm < kTM; ++tm)
 #pragma unroll
-        for (int tn = 0; tn < 4; ++tn)
-            acc[tm][tn] = f32x16{};
-    const int kb_count = g.k / kBK;
-    Slice s;
-    load_slice(s, g, tr, 0);
-    store_slice(smem, s);
+        for (int tn = 0; tn < kTN; ++tn)
+            acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[tm], f.b[tn], acc[tm][tn], 0, 0, 0);
+}
+
+// Fixes the issue order of one pipeline phase for the scheduler: kPairs
+// times one MFMA then one instruction of kind kOther (0x100 LDS read, 0x200
+// LDS write), then the phase's remaining MFMAs. A fence closes the phase.
+template <int kOther, int kPairs>
+__device__ __forceinline__ void phase_order()
+{
+#pragma unroll
+    for (int i = 0; i < kPairs; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kOther, 1, 0);
+    }
+    if constexpr (kPairs < kTM * kTN)
+        __builtin_amdgcn_sched_group_barrier(0x008, kTM * kTN - kPairs, 0);
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// One pass of the K loop over the slice staged in stage kb % 2. With
+// kWrite it writes slice kb + 1 (in registers `wr`) to the other stage; with
+// kLoad it loads slice k_load into `ld` (two slices ahead: the loads have a
+// whole pass, about 2000 MFMA cycles, before their pass writes them). One
+// wave per SIMD has no other wave to hide its waits behind, so the pass is
+// software-pipelined by hand: the fragments of K step kk + 1 are read from
+// LDS while the MFMAs of step kk issue, and slice kb + 1 is written while
+// the last step's MFMAs issue. Two fragment sets suffice: a set is refilled
+// only after every MFMA reading it has issued. Ends with a barrier.
+template <bool kWrite, bool kLoad>
+__device__ __forceinline__ void k_pass(const TileSrc& src, uint8_t* smem, f32x16 (&acc)[kTM][kTN],
+                                       const Slice& wr, Slice& ld, int kb, int k_load, int wm,
+                                       int wn, int lane)
+{
+    if constexpr (kLoad)
+        load_slice(ld, src, k_load * kBK);
+    const uint8_t* st = smem + (kb & 1) * kStageBytes;
+    Frags f0, f1;
+    read_frags(f0, st, 0, wm, wn, lane);
+    __builtin_amdgcn_sched_barrier(0);
+    mma_step(acc, f0);
+    read_frags(f1, st, 1, wm, wn, lane);
+    phase_order<0x100, kTM + kTN>();
+    mma_step(acc, f1);
+    read_frags(f0, st, 2, wm, wn, lane);
+    phase_order<0x100, kTM + kTN>();
+    mma_step(acc, f0);
+    read_frags(f1, st, 3, wm, wn, lane);
+    phase_order<0x100, kTM + kTN>();
+    mma_step(acc, f1);
+    if constexpr (kWrite) {
+        store_slice(smem + ((kb + 1) & 1) * kStageBytes, wr);
+        static_assert(2 * kSliceLoads <= kTM * kTN, "one LDS write per MFMA");
+        phase_order<0x200, 2 * kSliceLoads>();
+    }
     __syncthreads();
-    for (int kb = 0; kb < kb_count; ++kb) {
-        const bool more = kb + 1 < kb_count;
-        if (more)
-            load_slice(s, g, tr, (kb + 1) * kBK);
-        mma_slice(acc, smem + (kb & 1) * kStageBytes, wm, wn, lane);
-        if (more)
-            store_slice(smem + ((kb + 1) & 1) * kStageBytes, s);
-        __syncthreads();
-    }
 }
 
-// The waves of row band p (wm == p) write their 64 x 128 accumulator parts
-// into the C buffer: row 32 tm + 8 (i / 4) + 4 (lane / 32) + i % 4, column
-// 128 wn + 32 tn + lane % 32 (the v_mfma_f32_32x32x16 result layout).
-__device__ __forceinline__ void stage_accumulators(float* c, const f32x16 (&acc)[2][4], int wn,
-                                                   int lane)
+// The K loop of one tile: slice 0 staged, slice 1 in registers, then passes
+// in pairs so that each register set keeps its registers (slice kb + 1 sits
+// in s1 for even kb, in s0 for odd kb). Prefetches past the last slice are
+// clamped to it (a repeated load of data already in L2, never used), which
+// keeps every pass free of branches. Ends with a barrier after the last
+// slice's reads.
+__device__ __forceinline__ void gemm_tile(const Gemm& g, const TileRef& tr, uint8_t* smem,
+                                          f32x16 (&acc)[kTM][kTN], int wm, int wn, int lane)
 {
 #pragma unroll
-    for (int tm = 0; tm < 2; ++tm)
+    for (int tm = 0; tm < kTM; ++tm)
 #pragma unroll
-        for (int tn = 0; tn < 4; ++tn)
+        for (int tn = 0; tn < kTN; ++tn)
+            acc[tm][tn] = f32x16{};
+    const int last = g.k / kBK - 1;
+    const TileSrc src = tile_src(g, tr);
+    Slice s0, s1;
+    load_slice(s0, src, 0);
+    store_slice(smem, s0);
+    load_slice(s1, src, min(1, last) * kBK);
+    __syncthreads();
+    int kb = 0;
+    for (; kb + 2 <= last; kb += 2) {
+        k_pass<true, true>(src, smem, acc, s1, s0, kb, kb + 2, wm, wn, lane);
+        k_pass<true, true>(src, smem, acc, s0, s1, kb + 1, min(kb + 3, last), wm, wn, lane);
+    }
+    if (kb < last) {   // kb = last - 1 (even): slice last is in s1
+        k_pass<true, false>(src, smem, acc, s1, s0, kb, 0, wm, wn, lane);
+        ++kb;
+    }
+    k_pass<false, false>(src, smem, acc, s0, s1, kb, 0, wm, wn, lane);   // touches neither set
+}
+
+// Epilogue pass p holds the tile rows of MFMA row tile p of every wave:
+// C buffer row r is tile row 128 (r / 32) + 32 p + r % 32. All 4 waves
+// write their tile p (no branch, and 64 accumulators per lane per pass):
+// row 32 wm + 8 (i / 4) + 4 (lane / 32) + i % 4, column 128 wn + 32 tn +
+// lane % 32 (the v_mfma_f32_32x32x16 result layout).
+__device__ __forceinline__ int pass_row(int pass, int r)
+{
+    return kWaveM * (r >> 5) + 32 * pass + (r & 31);
+}
+
+template <int kPass>
+__device__ __forceinline__ void stage_accumulators(float* c, const f32x16 (&acc)[kTM][kTN], int wm,
+                                                   int wn, int lane)
+{
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int row = 32 * tm + (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3);
-                const int col = 128 * wn + 32 * tn + (lane & 31);
-                c[row * kCPitch + col] = acc[tm][tn][i];
-            }
+    for (int tn = 0; tn < kTN; ++tn)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int row = 32 * wm + (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3);
+            const int col = kWaveN * wn + 32 * tn + (lane & 31);
+            c[row * kCPitch + col] = acc[kPass][tn][i];
+        }
 }
 
 // ---- SwiGLU of FP32 values -------------------------------------------------
@@ -280,13 +427,11 @@ struct Bf16Out {
 
 // Fused epilogue of one 64-row pass: 64 rows x 8 NVFP4 blocks (each block =
 // 32 interleaved accumulator columns [g x8, u x8, g x8, u x8] -> 16
-// outputs); thread t takes block t % 8 of row t / 8.
-__device__ __forceinline__ void epilogue(const Gemm& g, const TileRef& tr, int pass,
-                                         const float* c, const FusedOut& o,
-                                         const nvfp4::RowScale& rs)
+// outputs); thread t takes block t % 8 of rows t / 8 and t / 8 + 32.
+__device__ __forceinline__ void fused_block(const Gemm& g, const TileRef& tr, int pass,
+                                            const float* c, const FusedOut& o,
+                                            const nvfp4::RowScale& rs, int row, int bl)
 {
-    const int bl = threadIdx.x & 7;
-    const int row = threadIdx.x >> 3;
     const int inter = g.n / 2;
     const float* src = c + row * kCPitch + 32 * bl;
     float v[32];
@@ -306,7 +451,7 @@ __device__ __forceinline__ void epilogue(const Gemm& g, const TileRef& tr, int p
     }
     uint32_t sf;
     const uint2 q = nvfp4::quantize16(y, rs, sf);
-    const int trow = kPassRows * pass + row;
+    const int trow = pass_row(pass, row);
     if (trow < tr.rows) {
         const int64_t grow = tr.row0 + trow;
         const int64_t blk = grow * (inter / 16) + tr.n0 / 32 + bl;
@@ -321,21 +466,30 @@ __device__ __forceinline__ void epilogue(const Gemm& g, const TileRef& tr, int p
     }
 }
 
-// BF16 epilogue of one pass: thread t writes 16-byte chunks t + 512 j
-// (j = 0..3) of the 64 x 256 pass, chunk q = row q / 32, columns 8 (q % 32).
-__device__ __forceinline__ void epilogue(const Gemm&, const TileRef& tr, int pass, const float* c,
-                                         const Bf16Out& o, const nvfp4::RowScale&)
+__device__ __forceinline__ void epilogue(const Gemm& g, const TileRef& tr, int pass,
+                                         const float* c, const FusedOut& o,
+                                         const nvfp4::RowScale& rs, int tid)
 {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int q = threadIdx.x + kThreads * j;
+    for (int j = 0; j < kPassRows * 8 / kThreads; ++j)
+        fused_block(g, tr, pass, c, o, rs, (tid >> 3) + (kThreads / 8) * j, tid & 7);
+}
+
+// BF16 epilogue of one pass: thread t writes 16-byte chunks t + 256 j
+// (j = 0..7) of the 64 x 256 pass, chunk q = row q / 32, columns 8 (q % 32).
+__device__ __forceinline__ void epilogue(const Gemm&, const TileRef& tr, int pass, const float* c,
+                                         const Bf16Out& o, const nvfp4::RowScale&, int tid)
+{
+#pragma unroll
+    for (int j = 0; j < kPassRows * kBN / 8 / kThreads; ++j) {
+        const int q = tid + kThreads * j;
         const int row = q >> 5;
         const int col = 8 * (q & 31);
         const float4 f0 = *reinterpret_cast<const float4*>(c + row * kCPitch + col);
         const float4 f1 = *reinterpret_cast<const float4*>(c + row * kCPitch + col + 4);
         const u32x4 w = {pack_bf16x2(f0.x, f0.y), pack_bf16x2(f0.z, f0.w), pack_bf16x2(f1.x, f1.y),
                          pack_bf16x2(f1.z, f1.w)};
-        const int trow = kPassRows * pass + row;
+        const int trow = pass_row(pass, row);
         if (trow < tr.rows)
             *reinterpret_cast<u32x4*>(o.out + (int64_t)(tr.row0 + trow) * o.ld_out + tr.n0 + col) = w;
     }
@@ -348,10 +502,14 @@ __device__ __forceinline__ float expert_scale(const FusedOut& o, int e)
 __device__ __forceinline__ float expert_scale(const Bf16Out&, int) { return 1.0f; }
 
 // Persistent walk over the tiles. With a grid of a multiple of 8 workgroups
-// (one per CU, dealt round-robin to the 8 XCDs), XCD x takes the x-th eighth
-// of the tile list and its workgroups stride through it: concurrently
-// running workgroups of one XCD work on neighbouring tiles (the same row
-// tile, successive column tiles), which share their x rows in that XCD's L2.
+// (one per CU, dealt round-robin to the 8 XCDs), each round of gridDim.x
+// consecutive tiles of the walk order is split into 8 runs, run x going to
+// XCD x's workgroups: the workgroups of one XCD work on neighbouring tiles
+// (sharing x and w slices in that XCD's L2), and the 8 XCDs work on the same
+// row groups of the same expert at the same time (sharing them in the
+// Infinity Cache). Giving each XCD a contiguous eighth of the whole walk
+// instead put the XCDs on different experts, whose weights do not fit the
+// cache together: 9% slower.
 template <class Out>
 __global__ __launch_bounds__(kThreads) void moe_gemm_kernel(Gemm g, Out o)
 {
@@ -365,26 +523,31 @@ __global__ __launch_bounds__(kThreads) void moe_gemm_kernel(Gemm g, Out o)
     const int wave = uniform(threadIdx.x / kWave);
     const int wm = wave >> 1, wn = wave & 1;
     float* c = reinterpret_cast<float*>(smem);
-    int first = blockIdx.x, step = gridDim.x, end = tiles;
-    if (gridDim.x % kXcds == 0) {
-        const int per = (tiles + kXcds - 1) / kXcds;
-        const int xcd = blockIdx.x % kXcds;
-        first = xcd * per + blockIdx.x / kXcds;
-        step = gridDim.x / kXcds;
-        end = min(tiles, (xcd + 1) * per);
-    }
-    f32x16 acc[2][4];
-    for (int tile = first; tile < end; tile += step) {
-        const TileRef tr = tile_ref(g, off, pre, tile);
+    int first = blockIdx.x;
+    if (gridDim.x % kXcds == 0)
+        first = (blockIdx.x % kXcds) * (gridDim.x / kXcds) + blockIdx.x / kXcds;
+    f32x16 acc[kTM][kTN];
+    for (int tile = first; tile < tiles; tile += gridDim.x) {
+        const TileRef tr = tile_ref(g, off, pre, row_tiles, tile);
         gemm_tile(g, tr, smem, acc, wm, wn, lane);
         const nvfp4::RowScale rs = nvfp4::row_scale(expert_scale(o, tr.e));
-        for (int pass = 0; pass < kBM / kPassRows; ++pass) {
-            if (wm == pass)
-                stage_accumulators(c, acc, wn, lane);
+        // the thread index taken afresh per tile: the epilogue's addresses
+        // are then computed here, not hoisted out of the tile loop, where
+        // they would stay live through the K loop and crowd its registers
+        int tid = threadIdx.x;
+        asm volatile("" : "+v"(tid));
+        const int el = tid & (kWave - 1);
+        static_assert(kBM / kPassRows == kTM && kPassRows == 2 * 32, "one MFMA row tile per pass");
+        auto pass = [&](auto p) {
+            stage_accumulators<decltype(p)::value>(c, acc, wm, wn, el);
             __syncthreads();
-            epilogue(g, tr, pass, c, o, rs);
+            epilogue(g, tr, decltype(p)::value, c, o, rs, tid);
             __syncthreads();   // the next pass (or tile) overwrites the buffer
-        }
+        };
+        pass(Int<0>{});
+        pass(Int<1>{});
+        pass(Int<2>{});
+        pass(Int<3>{});
     }
 }
 
@@ -404,6 +567,9 @@ nvfp4_status_t make_gemm(const uint16_t* x, const uint16_t* w, int64_t tokens, i
     if (hidden % kBK != 0 || n % kBN != 0 || num_experts > kMaxExperts)
         return NVFP4_ERROR_UNSUPPORTED_SHAPE;
     if (tokens > INT32_MAX || hidden > INT32_MAX || n > INT32_MAX)
+        return NVFP4_ERROR_UNSUPPORTED_SHAPE;
+    // a tile's operand window (256 rows) is addressed with 32-bit offsets
+    if (ld_x >= kMaxPitch || ld_w >= kMaxPitch)
         return NVFP4_ERROR_UNSUPPORTED_SHAPE;
     const int experts = offsets != nullptr ? num_experts : 1;
     // byte extents of x and of the weight stack must be addressable with

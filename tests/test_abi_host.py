@@ -213,6 +213,9 @@ def test_gemm_validation(lib):
         assert f(lib, x=None) == INVALID
         assert f(lib, hidden=0, ld_x=0, ld_w=0) == SHAPE
         assert f(lib, tokens=2**31) == SHAPE
+        assert f(lib, ld_x=2**22) == SHAPE                         # 32-bit window offsets
+        assert f(lib, ld_w=2**22) == SHAPE
+        assert f(lib, ld_x=2**22 - 8, ld_w=2**22 - 8, x=None) == INVALID   # largest pitch passes
     assert gf(lib, inter=64) == SHAPE                              # 2 * inter % 256
     assert gf(lib, packed=None) == INVALID
     assert gf(lib, packed=A16 + 4) == MISALIGNED
@@ -237,9 +240,10 @@ def test_pitch_extent_overflow_is_rejected(lib):
     for fused in (False, True):
         assert gsc(lib, fused, ld=big) == INVALID
     for g in (gf, gb):
-        assert g(lib, ld_x=big) == INVALID
-        assert g(lib, ld_w=big) == INVALID
-        assert g(lib, offs=A16, ne=512, ld_w=2**63 // (2 * 512 * 256) + 8) == INVALID
+        # the grouped GEMM caps pitches below 2^22 first
+        assert g(lib, ld_x=big) == SHAPE
+        assert g(lib, ld_w=big) == SHAPE
+        assert g(lib, offs=A16, ne=512, ld_w=2**63 // (2 * 512 * 256) + 8) == SHAPE
     assert gb(lib, ld_out=big) == INVALID
     # one row has no extent beyond its own columns
     assert q(lib, rows=1, ld=big, x=None) == INVALID   # still reaches the NULL check

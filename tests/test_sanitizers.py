@@ -92,8 +92,8 @@ int main(void) {
     CHECK(moe_l1_gemm_bf16(A, A, 4, 64, 200, 64, 64, A, 1, A, 256, NULL) == NVFP4_ERROR_UNSUPPORTED_SHAPE);
     CHECK(moe_l1_gemm_swiglu_nvfp4(A, A, 4, 64, 128, 64, 64, A, 1, NULL, (uint8_t *)A + 4, A, NULL, NULL) == NVFP4_ERROR_MISALIGNED);
     CHECK(moe_l1_gemm_swiglu_nvfp4(A, A, 4, 64, 128, 64, 64, A, 1, NULL, A, NULL, NULL, NULL) == NVFP4_ERROR_INVALID_VALUE);
-    CHECK(moe_l1_gemm_bf16(A, A, 4, 64, 256, 64, INT64_MAX - 7, A, 1, A, 256, NULL) == NVFP4_ERROR_INVALID_VALUE);
-    CHECK(moe_l1_gemm_bf16(A, A, 4, 64, 256, INT64_MAX - 7, 64, NULL, 0, A, 256, NULL) == NVFP4_ERROR_INVALID_VALUE);
+    CHECK(moe_l1_gemm_bf16(A, A, 4, 64, 256, 64, INT64_MAX - 7, A, 1, A, 256, NULL) == NVFP4_ERROR_UNSUPPORTED_SHAPE);
+    CHECK(moe_l1_gemm_bf16(A, A, 4, 64, 256, INT64_MAX - 7, 64, NULL, 0, A, 256, NULL) == NVFP4_ERROR_UNSUPPORTED_SHAPE);
     CHECK(moe_l1_gemm_bf16(A, A, 4, 64, 256, 64, 64, NULL, 0, A, INT64_MAX - 7, NULL) == NVFP4_ERROR_INVALID_VALUE);
     CHECK(moe_l1_gemm_swiglu_nvfp4(A, A, 4, 64, INT64_MAX / 2 + 1, 64, 64, NULL, 0, NULL, A, A, NULL, NULL) == NVFP4_ERROR_INVALID_VALUE);
     CHECK(swiglu_bf16(A, 4, 32, 64, A, INT64_MAX - 7, NULL) == NVFP4_ERROR_INVALID_VALUE);
