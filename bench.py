@@ -271,16 +271,23 @@ def graph_ms(fn, launches=50, replays=20):
     return e0.elapsed_time(e1) / (launches * replays)
 
 
-def cpu_baseline(x):
+def cpu_baseline(x, gpu_packed=None, gpu_scales=None, gpu_value=None):
     """The CPU oracle on the same prefill input: all host threads over the
-    whole workload (median of 3), plus one thread over 16384 rows."""
+    whole workload (median of 3), plus one thread over 16384 rows. The
+    oracle's output of the last pass is compared byte for byte with the GPU's
+    output of the last timed launch (the fused path's acceptance exempts
+    codes whose scaled value lies within 1e-6 of a rounding boundary, so a
+    handful of differing code bytes is expected; scale bytes differ only
+    where an amax does)."""
+    import numpy as np
     import oracle
     n_elem = x.shape[0] * (x.shape[1] // 2)
     threads = oracle.num_threads()
     times = []
+    ref = None
     for _ in range(3):
         t = time.perf_counter()
-        oracle.swiglu_quantize(x)
+        ref = oracle.swiglu_quantize(x)
         times.append(time.perf_counter() - t)
     med = statistics.median(times)
     oracle.set_num_threads(1)
@@ -296,7 +303,7 @@ def cpu_baseline(x):
             model = next(l.split(":", 1)[1].strip() for l in f if l.startswith("model name"))
     except (OSError, StopIteration):
         pass
-    return {
+    out = {
         "value": round(n_elem * BYTES_PER_ELEM / med / 1e9, 3),
         "unit": "GB/s",
         "cores": threads,
@@ -304,7 +311,17 @@ def cpu_baseline(x):
         "sample": "full prefill workload 65536x6144 BF16, median of 3 passes on %d threads "
                   "(%.2f s each); 1 thread over 16384 rows: %.3f GB/s; host CPU: %s"
                   % (threads, med, one_elem * BYTES_PER_ELEM / one / 1e9, model),
+        "elements_per_s": round(n_elem / med, 1),
     }
+    if gpu_value is not None:
+        out["gpu_over_cpu"] = round(gpu_value / out["value"], 1)
+    if gpu_packed is not None:
+        gp = gpu_packed.cpu().numpy()
+        gsc = gpu_scales.cpu().numpy()
+        out["checked_against_gpu"] = {
+            "packed_bytes": int(gp.size), "packed_bytes_differ": int(np.count_nonzero(gp != ref[0])),
+            "scale_bytes": int(gsc.size), "scale_bytes_differ": int(np.count_nonzero(gsc != ref[1]))}
+    return out
 
 
 kern_ms_headline = []
@@ -583,7 +600,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle on host cores)", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(w.x)
+        cpu = cpu_baseline(w.x, packed, scales, value)
 
     line = {
         "metric": "fused SwiGLU+NVFP4 quantize HBM GB/s and % of MI355X peak, prefill shape",

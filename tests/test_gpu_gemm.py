@@ -71,9 +71,11 @@ def gs_rows_of(g, gs, rows=None):
     return r if rows is None else r[rows]
 
 
+# hidden / 64 K slices: 1, 2, 3, 4, 5, 8, 16 and 64 (the K loop runs its
+# slices in pairs, with separate tails for an odd and an even count)
 @pytest.mark.parametrize("tokens,hidden,inter,experts,seed", [
     (300, 256, 128, 5, 1), (1000, 512, 384, 9, 2), (257, 64, 128, 1, 3), (513, 1024, 256, 3, 4),
-    (256, 4096, 128, 2, 5)])
+    (256, 4096, 128, 2, 5), (130, 128, 128, 2, 6), (260, 192, 256, 2, 7), (511, 320, 128, 4, 8)])
 def test_gemm_exact_operands(M, tokens, hidden, inter, experts, seed):
     g = W.moe_gemm(seed, tokens, hidden, inter, experts, exact=True)
     acc = oracle.moe_l1_gemm(g.x, g.w1, g.offsets)
@@ -142,7 +144,7 @@ def check_random(g, r, rows, gs=None):
 
 
 @pytest.mark.parametrize("tokens,hidden,inter,experts,seed", [
-    (700, 1024, 256, 6, 11), (2048, 2048, 512, 16, 12)])
+    (700, 1024, 256, 6, 11), (2048, 2048, 512, 16, 12), (600, 448, 256, 3, 13)])
 def test_gemm_random_operands(M, tokens, hidden, inter, experts, seed):
     g = W.moe_gemm(seed, tokens, hidden, inter, experts)
     say("moe_l1_gemm random", tokens, hidden, inter, "experts", experts)
