@@ -184,13 +184,18 @@ __device__ __forceinline__ TileRef tile_ref(const Gemm& g, const int* off, const
 // A tile's operand windows as buffer resources (base and size in SGPRs):
 // x rows row0 .. row0 + rows and w rows n0 .. n0 + 256 of expert e. A row
 // of x past a partial tile lies outside its window, and the hardware range
-// check returns zeros for it (those rows are computed, never stored). Each
-// lane keeps one 32-bit offset per operand: chunk t % 8 of row t / 8.
-// Windows are at most 256 rows of pitch < 2^22 elements: under 2^31 bytes.
+// check returns zeros for it (those rows are computed, never stored). The
+// range check covers the VGPR offset (plus the instruction's immediate),
+// not the SGPR offset, so a lane keeps the whole row offset of each of its
+// 8 x rows in VGPRs, and the SGPR offset only carries the K position within
+// the row. Every w row lies inside its window: one VGPR offset (chunk t % 8
+// of row t / 8), with the row step in the SGPR offset. Windows are at most
+// 256 rows of pitch < 2^22 elements: under 2^31 bytes.
 struct TileSrc {
     __amdgpu_buffer_rsrc_t x, w;
-    int vx, vw;              // lane offsets (bytes)
-    int row_x, row_w;        // bytes between rows kLoadRows apart
+    int vx[kSliceLoads];     // lane offsets (bytes) of its x rows t / 8 + 32 j
+    int vw;                  // lane offset of its w row t / 8
+    int row_w;               // bytes between w rows kLoadRows apart
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t window(const uint16_t* base, int bytes)
@@ -206,9 +211,10 @@ __device__ __forceinline__ TileSrc tile_src(const Gemm& g, const TileRef& tr)
     t.w = window(g.w + (int64_t)tr.e * g.w_expert + (int64_t)tr.n0 * g.ld_w, kBN * (int)g.ld_w * 2);
     const int c = threadIdx.x & 7;
     const int r0 = threadIdx.x >> 3;
-    t.vx = r0 * (int)g.ld_x * 2 + 16 * c;
+#pragma unroll
+    for (int j = 0; j < kSliceLoads; ++j)
+        t.vx[j] = (r0 + kLoadRows * j) * (int)g.ld_x * 2 + 16 * c;
     t.vw = r0 * (int)g.ld_w * 2 + 16 * c;
-    t.row_x = kLoadRows * (int)g.ld_x * 2;
     t.row_w = kLoadRows * (int)g.ld_w * 2;
     return t;
 }
@@ -224,7 +230,7 @@ __device__ __forceinline__ void load_slice(Slice& s, const TileSrc& src, int k0)
 #pragma unroll
     for (int j = 0; j < kSliceLoads; ++j) {
         s.a[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                               src.x, src.vx, j * src.row_x + 2 * k0, 0));
+                                               src.x, src.vx[j], 2 * k0, 0));
         s.b[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
                                                src.w, src.vw, j * src.row_w + 2 * k0, 0));
     }
