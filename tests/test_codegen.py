@@ -12,6 +12,10 @@ cross-compiles the device code to assembly).
 * No scalar-memory writes or atomics anywhere in the device code: stores and
   atomics go through the vector memory path only.
 * No kernel uses scratch memory (no register spills), in either source.
+* The grouped GEMM's x slice loads are range-checked row by row: the buffer
+  range check covers the VGPR offset, not the SGPR offset, so the x loads
+  must use one VGPR offset per x row a lane loads (8), not one offset plus
+  a row step in the SGPR (which would let a partial tile read past x).
 """
 import os
 import re
@@ -101,3 +105,27 @@ def test_no_scratch_in_any_kernel(tmp_path):
         names = re.findall(r"Function Name: (\S+)", r.stderr)
         assert sizes and len(sizes) == len(names), src
         assert all(int(v) == 0 for v in sizes), list(zip(names, sizes))
+
+
+@pytest.fixture(scope="module")
+def gemm_isa(tmp_path_factory):
+    from moe_swiglu_epilogue_amd import build as B
+    out = tmp_path_factory.mktemp("isa") / "moe_gemm.s"
+    subprocess.run([B.HIPCC, *B.FLAGS, "-I", os.path.join(ROOT, "include"), "--cuda-device-only",
+                    "-S", B.GEMM_SRC, "-o", str(out)], check=True, capture_output=True)
+    return out.read_text()
+
+
+def test_gemm_x_rows_are_range_checked(gemm_isa):
+    ks = {n: b for n, b in _kernels(gemm_isa).items() if "moe_gemm_kernel" in n}
+    assert len(ks) == 2, sorted(ks)
+    for name, body in ks.items():
+        voffsets = {}
+        for l in body:
+            m = re.match(r"buffer_load_dwordx4 v\[\d+:\d+\], (v\d+), (s\[\d+:\d+\]), \S+ offen", l)
+            if m:
+                voffsets.setdefault(m.group(2), set()).add(m.group(1))
+        # the x resource (in whichever SGPRs it sits) is loaded through 8
+        # distinct VGPR offsets, one per row a lane loads; w through one
+        counts = sorted(len(v) for v in voffsets.values())
+        assert 8 in counts and set(counts) <= {1, 8}, (name, counts)
