@@ -23,11 +23,12 @@
 // computes 256 x 256 output tiles; wave (wm, wn) owns rows 128 wm .. +128
 // and columns 128 wn .. +128 as 4 x 4 MFMA tiles of 32 x 32, whose 256
 // accumulator registers per lane sit in the SIMD's accumulation registers.
-// The K loop stages 256 x 64 slices of x and w in LDS (double-buffered, rows
-// padded against bank conflicts); the slices arrive by buffer loads two
-// slices ahead, through two register sets, and each pass is
-// software-pipelined by hand (fragment reads for the next K step and the LDS
-// writes of the next slice interleaved with the MFMAs).
+// The K loop stages 256 x 64 slices of x and w in LDS (double-buffered,
+// 16-byte chunks XOR-swizzled against bank conflicts). The slices arrive by
+// buffer loads straight into LDS (buffer_load_dwordx4 ... lds, 16 bytes per
+// lane on gfx950) one slice ahead, so no register holds them on the way,
+// and each pass is software-pipelined by hand (the fragment reads for the
+// next K step interleaved with the MFMAs).
 //
 // What bounds it: a 256 x 256 tile does 128 FLOP per byte of operand slices,
 // so the matrix-core peak would need about 19 TB/s of operands from L2. With
@@ -54,12 +55,12 @@ constexpr int kBM = 256, kBN = 256, kBK = 64;
 constexpr int kThreads = 256;                             // 4 waves: 2 x 2 wave tiles of 128 x 128
 constexpr int kWaveM = 128, kWaveN = 128;
 constexpr int kTM = kWaveM / 32, kTN = kWaveN / 32;       // 4 x 4 MFMA tiles per wave
-constexpr int kLoadRows = kThreads / 8;                   // rows one slice load instruction covers
-constexpr int kSliceLoads = kBM / kLoadRows;              // 16-byte chunks of x (and of w) per thread
 constexpr int kMaxExperts = 512;
-constexpr int kRowBytes = kBK * 2;                        // 128 data bytes per staged row
-constexpr int kRowPitch = kRowBytes + 16;                 // one 16-byte pad per row
-constexpr int kStageBytes = (kBM + kBN) * kRowPitch;      // 73,728 B: x slice then w slice
+constexpr int kRowBytes = kBK * 2;                        // 128 bytes per staged row
+constexpr int kRegionBytes = kBM * kRowBytes;             // 32 KB: one operand's slice
+constexpr int kStageBytes = 2 * kRegionBytes;             // x slice, then w slice
+constexpr int kDmaRows = kWave * 16 / kRowBytes;          // staged rows one LDS-DMA load fills (8)
+constexpr int kDmaLoads = kBM / (kThreads / kWave) / kDmaRows;   // per wave and operand (8)
 constexpr int kPassRows = 64;                             // epilogue rows per pass
 constexpr int kCPitch = kBN + 4;                          // floats per LDS row of the C buffer
 constexpr int kCBytes = kPassRows * kCPitch * 4;          // 66,560 B
@@ -82,12 +83,13 @@ struct Int {
     static constexpr int value = v;
 };
 
-// Byte offset of 16-byte chunk c (0..7) of staged row r. Rows are padded to
-// 144 bytes, so the 16 rows whose chunks one LDS cycle serves (a wave reads
-// 32 rows at one chunk position) start in 16 different 4-bank groups (no
-// bank conflicts), and a lane's chunk for each K step is its row base plus
-// an immediate offset.
-__device__ __forceinline__ int chunk_at(int r, int c) { return r * kRowPitch + (c << 4); }
+// Staged rows are 128 bytes (8 chunks of 16) with no padding: an LDS-DMA
+// load writes 1 KB contiguously. Logical chunk c of row r sits in slot
+// c ^ swz(r). One LDS cycle serves 16 lanes of a 16-byte read; a fragment
+// read has those lanes on 16 consecutive rows at one logical chunk, and
+// (r % 2, c ^ swz(r)) then takes 16 different values: 16 different 4-bank
+// groups of the 64 banks, no conflicts.
+__device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
 
 struct Gemm {
     const uint16_t* x;
@@ -192,59 +194,68 @@ __device__ __forceinline__ TileRef tile_ref(const Gemm& g, const int* off, const
 // of row t / 8), with the row step in the SGPR offset. Windows are at most
 // 256 rows of pitch < 2^22 elements: under 2^31 bytes.
 struct TileSrc {
-    __amdgpu_buffer_rsrc_t x, w;
-    int vx[kSliceLoads];     // lane offsets (bytes) of its x rows t / 8 + 32 j
-    int vw;                  // lane offset of its w row t / 8
-    int row_w;               // bytes between w rows kLoadRows apart
+    u32x4 x, w;              // buffer descriptors (SGPRs)
+    int vx[kDmaLoads];       // x row offsets of this lane for load instruction j
+    int vw[2];               // w offsets (row within the 8-row group) for even / odd j
+    int row_w;               // bytes of one w row
 };
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t window(const uint16_t* base, int bytes)
+// A raw buffer descriptor over [base, base + bytes): base address, stride 0,
+// the size for the range check, and the same format word as
+// __builtin_amdgcn_make_buffer_rsrc takes. Wave-uniform, kept in SGPRs.
+__device__ __forceinline__ u32x4 window(const uint16_t* base, int bytes)
 {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), (short)0, bytes,
-                                             0x00020000);
+    const uint64_t a = (uint64_t)(uintptr_t)base;
+    return u32x4{(uint32_t)uniform((int)(uint32_t)a), (uint32_t)uniform((int)(uint32_t)(a >> 32)),
+                 (uint32_t)uniform(bytes), 0x00020000u};
 }
 
-__device__ __forceinline__ TileSrc tile_src(const Gemm& g, const TileRef& tr)
+// Load instruction j of wave w fills staged rows 64 w + 8 j .. +8 (1 KB of
+// LDS, lane l at byte 16 l): lane l loads row 64 w + 8 j + l / 8, logical
+// chunk (l % 8) ^ swz(row) = (l % 8) ^ (4 (j % 2) + l / 16).
+__device__ __forceinline__ TileSrc tile_src(const Gemm& g, const TileRef& tr, int wave)
 {
     TileSrc t;
     t.x = window(g.x + (int64_t)tr.row0 * g.ld_x, tr.rows * (int)g.ld_x * 2);
     t.w = window(g.w + (int64_t)tr.e * g.w_expert + (int64_t)tr.n0 * g.ld_w, kBN * (int)g.ld_w * 2);
-    const int c = threadIdx.x & 7;
-    const int r0 = threadIdx.x >> 3;
+    const int l = threadIdx.x & (kWave - 1);
 #pragma unroll
-    for (int j = 0; j < kSliceLoads; ++j)
-        t.vx[j] = (r0 + kLoadRows * j) * (int)g.ld_x * 2 + 16 * c;
-    t.vw = r0 * (int)g.ld_w * 2 + 16 * c;
-    t.row_w = kLoadRows * (int)g.ld_w * 2;
+    for (int j = 0; j < kDmaLoads; ++j) {
+        const int c = (l & 7) ^ (4 * (j & 1) + (l >> 4));
+        t.vx[j] = (64 * wave + 8 * j + (l >> 3)) * (int)g.ld_x * 2 + 16 * c;
+        if (j < 2)
+            t.vw[j] = (l >> 3) * (int)g.ld_w * 2 + 16 * c;
+    }
+    t.row_w = (int)g.ld_w * 2;
     return t;
 }
 
-// 256 x 64 slices of x and w at K offset k0: thread t loads 16-byte chunk
-// t % 8 of rows t / 8 + 32 j, j = 0..7, of each.
-struct Slice {
-    u32x4 a[kSliceLoads], b[kSliceLoads];
-};
-
-__device__ __forceinline__ void load_slice(Slice& s, const TileSrc& src, int k0)
+__device__ __forceinline__ uint32_t lds_addr(const uint8_t* p)
 {
-#pragma unroll
-    for (int j = 0; j < kSliceLoads; ++j) {
-        s.a[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                               src.x, src.vx[j], 2 * k0, 0));
-        s.b[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                               src.w, src.vw, j * src.row_w + 2 * k0, 0));
-    }
+    return (uint32_t)uniform((int)(uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p);
 }
 
-__device__ __forceinline__ void store_slice(uint8_t* stage, const Slice& s)
+// 16 bytes per lane from the buffer straight into LDS at lds + 16 lane. By
+// inline assembly: the compiler would otherwise wait for every such load
+// before any later LDS read, since it cannot tell that they fill the other
+// stage. The caller waits (vmcnt(0)) before the stage is read.
+__device__ __forceinline__ void load_lds16(const u32x4& rsrc, uint32_t lds, int voff, int soff)
 {
-    const int c = threadIdx.x & 7;
-    const int r0 = threadIdx.x >> 3;
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :: "s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "memory");
+}
+
+// Wave w's share of a 256 x 64 slice at K offset k0: staged rows 64 w ..
+// +64 of x and of w, 8 loads each.
+static_assert(kDmaRows == 8 && kDmaLoads == 8, "the swizzle and offsets assume 8 x 8 rows");
+__device__ __forceinline__ void load_slice(const TileSrc& src, uint8_t* stage, int k0, int wave)
+{
 #pragma unroll
-    for (int j = 0; j < kSliceLoads; ++j) {
-        const int r = r0 + kLoadRows * j;
-        *reinterpret_cast<u32x4*>(stage + chunk_at(r, c)) = s.a[j];
-        *reinterpret_cast<u32x4*>(stage + kBM * kRowPitch + chunk_at(r, c)) = s.b[j];
+    for (int j = 0; j < kDmaLoads; ++j) {
+        const int row = 64 * wave + 8 * j;
+        load_lds16(src.x, lds_addr(stage + row * kRowBytes), src.vx[j], uniform(2 * k0));
+        load_lds16(src.w, lds_addr(stage + kRegionBytes + row * kRowBytes), src.vw[j & 1],
+                   uniform(row * src.row_w + 2 * k0));
     }
 }
 
@@ -258,16 +269,16 @@ struct Frags {
 __device__ __forceinline__ void read_frags(Frags& f, const uint8_t* stage, int kk, int wm, int wn,
                                            int lane)
 {
-    const int c = 2 * kk + (lane >> 5);
+    // rows 32 t + lane % 32 (+ a multiple of 128): swz depends on the lane only
+    const int off = (lane & 31) * kRowBytes + (((2 * kk + (lane >> 5)) ^ swz(lane & 31)) << 4);
 #pragma unroll
     for (int t = 0; t < kTM; ++t)
         f.a[t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
-                                                stage + chunk_at(kWaveM * wm + 32 * t + (lane & 31), c)));
+                                                stage + (kWaveM * wm + 32 * t) * kRowBytes + off));
 #pragma unroll
     for (int t = 0; t < kTN; ++t)
         f.b[t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
-                                                stage + kBM * kRowPitch +
-                                                chunk_at(kWaveN * wn + 32 * t + (lane & 31), c)));
+                                                stage + kRegionBytes + (kWaveN * wn + 32 * t) * kRowBytes + off));
 }
 
 // acc[tm][tn] += A fragment tm x B fragment tn: 16 MFMAs.
@@ -296,22 +307,21 @@ __device__ __forceinline__ void phase_order()
     __builtin_amdgcn_sched_barrier(0);
 }
 
-// One pass of the K loop over the slice staged in stage kb % 2. With
-// kWrite it writes slice kb + 1 (in registers `wr`) to the other stage; with
-// kLoad it loads slice k_load into `ld` (two slices ahead: the loads have a
-// whole pass, about 2000 MFMA cycles, before their pass writes them). One
-// wave per SIMD has no other wave to hide its waits behind, so the pass is
-// software-pipelined by hand: the fragments of K step kk + 1 are read from
-// LDS while the MFMAs of step kk issue, and slice kb + 1 is written while
-// the last step's MFMAs issue. Two fragment sets suffice: a set is refilled
-// only after every MFMA reading it has issued. Ends with a barrier.
-template <bool kWrite, bool kLoad>
+// One pass of the K loop over the slice staged in stage kb % 2; with kLoad
+// it first starts the loads of slice kb + 1 into the other stage (read last
+// in the previous pass, which ended with a barrier) and waits for them at
+// the end. One wave per SIMD has no other wave to hide its waits behind, so
+// the pass is software-pipelined by hand: the fragments of K step kk + 1
+// are read from LDS while the MFMAs of step kk issue. Two fragment sets
+// suffice: a set is refilled only after every MFMA reading it has issued.
+// Ends with a barrier (after which every wave's loads of slice kb + 1 are in
+// LDS).
+template <bool kLoad>
 __device__ __forceinline__ void k_pass(const TileSrc& src, uint8_t* smem, f32x16 (&acc)[kTM][kTN],
-                                       const Slice& wr, Slice& ld, int kb, int k_load, int wm,
-                                       int wn, int lane)
+                                       int kb, int wave, int wm, int wn, int lane)
 {
     if constexpr (kLoad)
-        load_slice(ld, src, k_load * kBK);
+        load_slice(src, smem + ((kb + 1) & 1) * kStageBytes, (kb + 1) * kBK, wave);
     const uint8_t* st = smem + (kb & 1) * kStageBytes;
     Frags f0, f1;
     read_frags(f0, st, 0, wm, wn, lane);
@@ -326,22 +336,15 @@ __device__ __forceinline__ void k_pass(const TileSrc& src, uint8_t* smem, f32x16
     read_frags(f1, st, 3, wm, wn, lane);
     phase_order<0x100, kTM + kTN>();
     mma_step(acc, f1);
-    if constexpr (kWrite) {
-        store_slice(smem + ((kb + 1) & 1) * kStageBytes, wr);
-        static_assert(2 * kSliceLoads <= kTM * kTN, "one LDS write per MFMA");
-        phase_order<0x200, 2 * kSliceLoads>();
-    }
+    if constexpr (kLoad)
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
 }
 
-// The K loop of one tile: slice 0 staged, slice 1 in registers, then passes
-// in pairs so that each register set keeps its registers (slice kb + 1 sits
-// in s1 for even kb, in s0 for odd kb). Prefetches past the last slice are
-// clamped to it (a repeated load of data already in L2, never used), which
-// keeps every pass free of branches. Ends with a barrier after the last
-// slice's reads.
+// The K loop of one tile. Ends with a barrier after the last slice's reads.
 __device__ __forceinline__ void gemm_tile(const Gemm& g, const TileRef& tr, uint8_t* smem,
-                                          f32x16 (&acc)[kTM][kTN], int wm, int wn, int lane)
+                                          f32x16 (&acc)[kTM][kTN], int wave, int wm, int wn,
+                                          int lane)
 {
 #pragma unroll
     for (int tm = 0; tm < kTM; ++tm)
@@ -349,22 +352,13 @@ __device__ __forceinline__ void gemm_tile(const Gemm& g, const TileRef& tr, uint
         for (int tn = 0; tn < kTN; ++tn)
             acc[tm][tn] = f32x16{};
     const int last = g.k / kBK - 1;
-    const TileSrc src = tile_src(g, tr);
-    Slice s0, s1;
-    load_slice(s0, src, 0);
-    store_slice(smem, s0);
-    load_slice(s1, src, min(1, last) * kBK);
+    const TileSrc src = tile_src(g, tr, wave);
+    load_slice(src, smem, 0, wave);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    int kb = 0;
-    for (; kb + 2 <= last; kb += 2) {
-        k_pass<true, true>(src, smem, acc, s1, s0, kb, kb + 2, wm, wn, lane);
-        k_pass<true, true>(src, smem, acc, s0, s1, kb + 1, min(kb + 3, last), wm, wn, lane);
-    }
-    if (kb < last) {   // kb = last - 1 (even): slice last is in s1
-        k_pass<true, false>(src, smem, acc, s1, s0, kb, 0, wm, wn, lane);
-        ++kb;
-    }
-    k_pass<false, false>(src, smem, acc, s0, s1, kb, 0, wm, wn, lane);   // touches neither set
+    for (int kb = 0; kb < last; ++kb)
+        k_pass<true>(src, smem, acc, kb, wave, wm, wn, lane);
+    k_pass<false>(src, smem, acc, last, wave, wm, wn, lane);
 }
 
 // Epilogue pass p holds the tile rows of MFMA row tile p of every wave:
@@ -535,7 +529,7 @@ __global__ __launch_bounds__(kThreads) void moe_gemm_kernel(Gemm g, Out o)
     f32x16 acc[kTM][kTN];
     for (int tile = first; tile < tiles; tile += gridDim.x) {
         const TileRef tr = tile_ref(g, off, pre, row_tiles, tile);
-        gemm_tile(g, tr, smem, acc, wm, wn, lane);
+        gemm_tile(g, tr, smem, acc, wave, wm, wn, lane);
         const nvfp4::RowScale rs = nvfp4::row_scale(expert_scale(o, tr.e));
         // the thread index taken afresh per tile: the epilogue's addresses
         // are then computed here, not hoisted out of the tile loop, where

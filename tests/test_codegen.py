@@ -16,6 +16,10 @@ cross-compiles the device code to assembly).
   range check covers the VGPR offset, not the SGPR offset, so the x loads
   must use one VGPR offset per x row a lane loads (8), not one offset plus
   a row step in the SGPR (which would let a partial tile read past x).
+* The GEMM's LDS-DMA loads are written as inline assembly that sets M0 (the
+  LDS address) itself, so M0 must have no other use in those kernels: every
+  M0 write is immediately followed by an LDS-DMA load and every such load
+  immediately follows one.
 """
 import os
 import re
@@ -122,10 +126,27 @@ def test_gemm_x_rows_are_range_checked(gemm_isa):
     for name, body in ks.items():
         voffsets = {}
         for l in body:
-            m = re.match(r"buffer_load_dwordx4 v\[\d+:\d+\], (v\d+), (s\[\d+:\d+\]), \S+ offen", l)
+            m = re.match(r"buffer_load_dwordx4 (?:v\[\d+:\d+\], )?(v\d+), (s\[\d+:\d+\]), \S+ offen", l)
             if m:
                 voffsets.setdefault(m.group(2), set()).add(m.group(1))
         # the x resource (in whichever SGPRs it sits) is loaded through 8
-        # distinct VGPR offsets, one per row a lane loads; w through one
+        # distinct VGPR offsets, one per row a lane loads; w through at most 2
+        # (its row step is in the SGPR offset: every w row is inside its window)
         counts = sorted(len(v) for v in voffsets.values())
-        assert 8 in counts and set(counts) <= {1, 8}, (name, counts)
+        assert 8 in counts and set(counts) <= {1, 2, 8}, (name, counts)
+
+
+def test_gemm_m0_only_feeds_lds_dma(gemm_isa):
+    for name, body in _kernels(gemm_isa).items():
+        if "moe_gemm_kernel" not in name:
+            continue
+        code = [l for l in body if not l.startswith(";")]
+        dma = 0
+        for k, l in enumerate(code):
+            if re.search(r"\bm0\b", l):
+                assert l.startswith("s_mov_b32 m0,"), (name, l)
+                assert code[k + 1].startswith("buffer_load_dwordx4") and code[k + 1].endswith(" lds"), (name, code[k + 1])
+            if l.startswith("buffer_load_dwordx4") and l.endswith(" lds"):
+                assert code[k - 1].startswith("s_mov_b32 m0,"), (name, code[k - 1])
+                dma += 1
+        assert dma >= 16, (name, dma)
