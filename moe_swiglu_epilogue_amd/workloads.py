@@ -279,6 +279,31 @@ def moe_gemm(seed: int = 6, tokens: int = 32768, hidden: int = 7168, inter: int 
 
 
 # ---- small edge-case generators ----------------------------------------------
+@dataclass
+class KvWorkload:
+    x: np.ndarray            # BF16 bits [tokens][heads * head_dim]
+    slots: np.ndarray        # int64 [tokens]: cache row of each token, -1 for padding
+    num_slots: int
+    heads: int
+    head_dim: int
+
+
+def kv_cache(seed: int = 7, tokens: int = 65536, heads: int = 8, head_dim: int = 128,
+             num_slots: int = 131072, pad_fraction: float = 0.01) -> KvWorkload:
+    """Keys (or values) of `tokens` new tokens for a paged NVFP4 KV cache. Each
+    head's values are N(0, 1) times a per-head lognormal(0, 1) scale (heads
+    differ in range). The tokens take distinct slots drawn at random from the
+    cache's `num_slots`, in random order; a `pad_fraction` of them are
+    padding (slot -1)."""
+    rng = np.random.default_rng(seed)
+    scale = rng.lognormal(0.0, 1.0, heads).astype(np.float32)
+    x = rng.standard_normal((tokens, heads, head_dim), dtype=np.float32) * scale[None, :, None]
+    slots = rng.choice(num_slots, size=tokens, replace=False).astype(np.int64)
+    slots[rng.random(tokens) < pad_fraction] = -1
+    return KvWorkload(to_bf16_bits(x.reshape(tokens, heads * head_dim)), slots, num_slots, heads,
+                      head_dim)
+
+
 def random_plain(rows: int, cols: int, seed: int, scale: float = 1.0) -> np.ndarray:
     rng = np.random.default_rng(seed)
     return to_bf16_bits(rng.standard_normal((rows, cols)) * scale)

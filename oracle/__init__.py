@@ -276,6 +276,40 @@ def dequantize(packed: np.ndarray, scales: np.ndarray, gs_rows=None) -> np.ndarr
     return out
 
 
+def quantize_paged(x: np.ndarray, slots, packed_cache: np.ndarray, scales_cache: np.ndarray,
+                   gs: float | None = None):
+    """Paged KV-cache write ("2026-05-28_STATUS.md": KV cache infra with a
+    paged cache, FP4 quantize in the compressor; "Priority 7: NVFP4-2 FP4 KV
+    pipeline"). Row r of the BF16 input is quantized exactly as
+    quantize_bf16 does (one global scale for all rows) and its bytes replace
+    cache row slots[r]; a slot outside [0, num_slots) skips the row. The
+    caches are updated in place and returned. Rows are visited one by one so
+    that the slot rule reads as written (no NumPy fancy indexing, whose
+    negative indices would wrap)."""
+    packed, scales = quantize_bf16(x, None if gs is None else np.full(x.shape[0], gs, np.float32))
+    num_slots = packed_cache.shape[0]
+    for r in range(x.shape[0]):
+        slot = int(slots[r])
+        if 0 <= slot < num_slots:
+            packed_cache[slot, :] = packed[r]
+            scales_cache[slot, :] = scales[r]
+    return packed_cache, scales_cache
+
+
+def dequantize_paged(packed_cache: np.ndarray, scales_cache: np.ndarray, slots,
+                     gs: float | None = None) -> np.ndarray:
+    """Paged KV-cache read: row r is the dequantize of cache row slots[r], or
+    zeros for a slot outside [0, num_slots)."""
+    num_slots, half = packed_cache.shape
+    out = np.zeros((len(slots), 2 * half), np.float32)
+    for r in range(len(slots)):
+        slot = int(slots[r])
+        if 0 <= slot < num_slots:
+            out[r] = dequantize(packed_cache[slot:slot + 1], scales_cache[slot:slot + 1],
+                                None if gs is None else np.full(1, gs, np.float32))[0]
+    return out
+
+
 def group_amax(y: np.ndarray, offsets: np.ndarray) -> np.ndarray:
     a = np.ascontiguousarray(y, dtype=np.float32)
     o = np.ascontiguousarray(offsets, dtype=np.int32)

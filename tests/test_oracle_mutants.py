@@ -138,3 +138,48 @@ def test_pins_catch_gemm_mutant(name, monkeypatch):
     monkeypatch.setattr(oracle, "moe_l1_gemm", GEMM_MUTANTS[name])
     with pytest.raises(AssertionError):
         P.pin_moe_l1_gemm()
+
+
+# the paged KV-cache write and read, mutated in the plausible ways: the row
+# index used as the slot, a negative slot allowed to wrap (NumPy indexing),
+# the read ignoring the slots, skipped rows not zeroed
+def _paged_row_as_slot(x, slots, pc, sc, gs=None):
+    return _REAL_QP(x, np.arange(len(slots)), pc, sc, gs)
+
+
+def _paged_wrap(x, slots, pc, sc, gs=None):
+    p, s = oracle.quantize_bf16(x, None if gs is None else np.full(x.shape[0], gs, np.float32))
+    for r, slot in enumerate(slots):
+        if slot < pc.shape[0]:
+            pc[int(slot)] = p[r]
+            sc[int(slot)] = s[r]
+    return pc, sc
+
+
+def _paged_read_identity(pc, sc, slots, gs=None):
+    return _REAL_DP(pc, sc, np.arange(len(slots)), gs)
+
+
+def _paged_read_garbage(pc, sc, slots, gs=None):
+    out = _REAL_DP(pc, sc, slots, gs)
+    bad = [r for r, slot in enumerate(slots) if not 0 <= slot < pc.shape[0]]
+    out[bad] = 1.0
+    return out
+
+
+_REAL_QP = oracle.quantize_paged
+_REAL_DP = oracle.dequantize_paged
+PAGED_MUTANTS = {
+    "paged_row_as_slot": ("quantize_paged", _paged_row_as_slot),
+    "paged_negative_wraps": ("quantize_paged", _paged_wrap),
+    "paged_read_ignores_slots": ("dequantize_paged", _paged_read_identity),
+    "paged_read_skipped_not_zero": ("dequantize_paged", _paged_read_garbage),
+}
+
+
+@pytest.mark.parametrize("name", sorted(PAGED_MUTANTS))
+def test_pins_catch_paged_mutant(name, monkeypatch):
+    attr, fn = PAGED_MUTANTS[name]
+    monkeypatch.setattr(oracle, attr, fn)
+    with pytest.raises((AssertionError, IndexError)):
+        P.pin_paged_kv()

@@ -362,11 +362,60 @@ def pin_moe_l1_gemm():
     assert np.allclose(one, xf @ wf[1].T, rtol=0, atol=1e-12)
 
 
+def pin_paged_kv():
+    """The paged KV-cache write and read against what the slot rule fixes:
+    identity slots reduce to quantize_bf16 of the rows; permuting rows and
+    slots together gives the same cache; rows whose slot is outside
+    [0, num_slots) (-1, num_slots, far beyond, a large negative) leave a
+    poisoned cache row untouched, as do slots no row names; the read returns
+    dequantize of each named row and zeros for skipped slots; a global scale
+    goes through as a per-row scale of quantize_bf16."""
+    rng = np.random.default_rng(91)
+    rows, cols, num_slots = 9, 64, 16
+    x = W.to_bf16_bits(rng.standard_normal((rows, cols)) * 3.0)
+    p_ref, s_ref = oracle.quantize_bf16(x)
+    pc = np.full((rows, cols // 2), 0xA5, np.uint8)
+    sc = np.full((rows, cols // 16), 0x5A, np.uint8)
+    oracle.quantize_paged(x, np.arange(rows), pc, sc)
+    assert np.array_equal(pc, p_ref) and np.array_equal(sc, s_ref)
+    slots = np.array([5, -1, 0, 15, 16, 3, 1000, -7, 9], np.int64)
+    pc = np.full((num_slots, cols // 2), 0xA5, np.uint8)
+    sc = np.full((num_slots, cols // 16), 0x5A, np.uint8)
+    oracle.quantize_paged(x, slots, pc, sc)
+    named = {5: 0, 0: 2, 15: 3, 3: 5, 9: 8}
+    for slot in range(num_slots):
+        if slot in named:
+            assert np.array_equal(pc[slot], p_ref[named[slot]]), slot
+            assert np.array_equal(sc[slot], s_ref[named[slot]]), slot
+        else:
+            assert (pc[slot] == 0xA5).all() and (sc[slot] == 0x5A).all(), slot
+    perm = rng.permutation(rows)
+    pc2 = np.full_like(pc, 0xA5)
+    sc2 = np.full_like(sc, 0x5A)
+    oracle.quantize_paged(x[perm], slots[perm], pc2, sc2)
+    assert np.array_equal(pc2, pc) and np.array_equal(sc2, sc)
+    out = oracle.dequantize_paged(pc, sc, slots)
+    deq = oracle.dequantize(p_ref, s_ref)
+    for r, slot in enumerate(slots):
+        if 0 <= slot < num_slots:
+            assert np.array_equal(out[r], deq[r]), r
+        else:
+            assert (out[r] == 0).all() and not np.signbit(out[r]).any(), r
+    g = np.float32(0.37)
+    pg, sg = oracle.quantize_bf16(x, np.full(rows, g, np.float32))
+    pc3 = np.zeros((rows, cols // 2), np.uint8)
+    sc3 = np.zeros((rows, cols // 16), np.uint8)
+    oracle.quantize_paged(x, np.arange(rows)[::-1].copy(), pc3, sc3, gs=float(g))
+    assert np.array_equal(pc3, pg[::-1]) and np.array_equal(sc3, sg[::-1])
+    assert np.array_equal(oracle.dequantize_paged(pc3, sc3, np.arange(rows)[::-1].copy(), gs=float(g)),
+                          oracle.dequantize(pg, sg, np.full(rows, g, np.float32)))
+
+
 ALL_PINS = [pin_page_facts, pin_fp8_decode_vs_torch, pin_fp8_saturation,
             pin_fp8_roundtrip, pin_e2m1_format, pin_e2m1_table, pin_swiglu_vs_torch,
             pin_swiglu_closed_forms, pin_quantize_vs_twin, pin_dequant_closed_form,
             pin_group_amax, pin_expert_global_scale, pin_bf16_vs_torch, pin_bf16_ties,
-            pin_swiglu_bf16_vs_torch, pin_swiglu_f32, pin_moe_l1_gemm]
+            pin_swiglu_bf16_vs_torch, pin_swiglu_f32, pin_moe_l1_gemm, pin_paged_kv]
 
 
 # ---- tests --------------------------------------------------------------------
