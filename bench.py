@@ -14,7 +14,8 @@ quantize, the dequantize and the global-scale pre-pass on the same tensor;
 the two-pass ablation (compact BF16 SwiGLU, then the standalone quantize);
 in-repo read / copy kernels over the same input as HBM ceilings; the ragged
 256-expert workload (pre-pass, quantize with per-expert scales, dequantize);
-the decode-shaped workload over 8 rotating buffer sets; the two small
+the decode-shaped workload over 8 rotating buffer sets; the paged KV-cache
+write and read (65536 tokens x 8 heads x 128, 131072 slots); the two small
 cache-resident shapes (standalone 128 x 256, fused 512 x 4096) as launch
 rates; the MoE L1 grouped GEMM with the fused epilogue against the unfused
 flow and hipBLASLt.
@@ -47,7 +48,7 @@ PMC_SUMMARY = os.path.join(ROOT, "profiles", "fused_quantize_kernel_prefill_pmc.
 CALIB_READ_BLOCKS = (1024, 1536, 8192, 49152)
 CALIB_COPY_BLOCKS = (512, 8192, 49152)
 SECONDARY = ("nvfp4_quantize", "nvfp4_dequantize", "global_scale", "two_pass", "calib_read",
-             "calib_copy", "ragged", "decode", "small", "gemm")
+             "calib_copy", "ragged", "decode", "small", "kv", "gemm")
 PEAK_BF16_TFLOPS = 2500.0           # MI355X dense BF16 matrix peak
 
 
@@ -482,6 +483,31 @@ def secondary_figures(M, W, x, packed, scales, args, dev):
             lambda: M.swiglu_nvfp4_quantize(xf, packed=pf, scales=sf),
             w.rows * w.out_cols * BYTES_PER_ELEM, w.rows * w.out_cols, [w.rows, 2 * w.out_cols])
         del xs, ps, ss, xf, pf, sf
+    if "kv" in want:
+        # paged KV-cache write and read: 65536 tokens x 8 heads x 128 into a
+        # 131072-slot NVFP4 cache (1% padding tokens, slot -1). Bytes: the
+        # BF16 input of every token plus the codes and scales of the tokens
+        # written; the read moves the cache bytes of the valid slots plus
+        # the FP32 output of every row
+        w = W.kv_cache()
+        cols = w.heads * w.head_dim
+        valid = int(((w.slots >= 0) & (w.slots < w.num_slots)).sum())
+        xk = torch.from_numpy(w.x.view(np.int16)).to(dev).view(torch.bfloat16)
+        sk = torch.from_numpy(w.slots).to(dev)
+        pk = torch.zeros((w.num_slots, cols // 2), dtype=torch.uint8, device=dev)
+        sck = torch.zeros((w.num_slots, cols // 16), dtype=torch.uint8, device=dev)
+        n = w.x.shape[0]
+        kv = {"shape": {"tokens": n, "heads": w.heads, "head_dim": w.head_dim,
+                        "num_slots": w.num_slots, "valid_tokens": valid}}
+        kv["write"] = measure("paged KV write nvfp4_quantize_paged",
+                              lambda: M.nvfp4_quantize_paged(xk, sk, pk, sck),
+                              n * cols * 2 + valid * cols * 0.5625, n * cols, st, ms)
+        outk = torch.empty((n, cols), dtype=torch.float32, device=dev)
+        kv["read"] = measure("paged KV read nvfp4_dequantize_paged",
+                             lambda: M.nvfp4_dequantize_paged(pk, sck, sk, out=outk),
+                             valid * cols * 0.5625 + n * cols * 4, n * cols, st, ms)
+        sec["kv_cache_paged"] = kv
+        del xk, sk, pk, sck, outk
     if "gemm" in want:
         sec["moe_l1_gemm"] = gemm_figures(M, W, args)
     return sec

@@ -55,7 +55,8 @@
  *   synchronizes, and enqueues its kernels on `stream` (NULL = the default
  *   stream): one kernel per call, three for the global-scale calls. Inputs
  *   and outputs must not overlap. Every byte of the output regions
- *   described above is written.
+ *   described above is written (the paged cache write excepted: it writes
+ *   only the cache rows its slots name).
  *
  * Preconditions checked on the host, before any HIP call (so they work on a
  * machine without a GPU) - a failing check returns without launching:
@@ -232,6 +233,49 @@ nvfp4_status_t moe_l1_gemm_bf16(const uint16_t *x, const uint16_t *w1,
                                 const int32_t *expert_offsets,
                                 int32_t num_experts, uint16_t *out,
                                 int64_t ld_out, hipStream_t stream);
+
+/*
+ * Paged KV-cache write: the same block quantization as nvfp4_quantize, for a
+ * second producer, the keys or values of new tokens going into an NVFP4
+ * paged cache. Pages: "2026-05-28_STATUS.md" (table "What's working": KV
+ * cache infra with a paged cache; the compressor's flush_write kernels with
+ * FP8/FP4 quantize; table "What's BLOCKED": "Priority 7: NVFP4-2 FP4 KV
+ * pipeline"). The pages give no cache layout; the one here is the plain
+ * reading: one cache row per token slot.
+ *   x             [rows][ld_x] BF16: row r is one token's keys (or values),
+ *                 all heads, cols = heads * head_dim, cols % 16 == 0 (a block
+ *                 never crosses a head when head_dim % 16 == 0).
+ *   gs            NULL (1.0) or gs[0], one global scale for the call.
+ *   slot_mapping  [rows] int64, device: row r goes to cache row
+ *                 slot_mapping[r]. A slot outside [0, num_slots) (such as -1
+ *                 for a padding token) is skipped: nothing is written for
+ *                 that row. Slots must be distinct (two rows with one slot
+ *                 leave that slot's bytes unspecified, still in bounds).
+ *   packed_cache  [num_slots][cols/2], scales_cache [num_slots][cols/16],
+ *                 contiguous; only the rows named by valid slots are
+ *                 written, every other cache byte keeps its value.
+ * num_slots < 2^31. rows == 0, cols == 0 or num_slots == 0 is a no-op. x as
+ * for nvfp4_quantize (16-byte base and pitch); packed_cache 8-byte and
+ * slot_mapping 8-byte aligned. One kernel.
+ */
+nvfp4_status_t nvfp4_quantize_paged(const uint16_t *x, int64_t rows, int64_t cols,
+                                    int64_t ld_x, const float *gs,
+                                    const int64_t *slot_mapping, int64_t num_slots,
+                                    uint8_t *packed_cache, uint8_t *scales_cache,
+                                    hipStream_t stream);
+
+/*
+ * Paged KV-cache read: out[r][c] = the nvfp4_dequantize value of cache row
+ * slots[r] (the FP4 KV consumer side; same pages as nvfp4_quantize_paged).
+ * A slot outside [0, num_slots) gives a row of zeros. gs: NULL (1.0) or
+ * gs[0]. out [rows][cols] FP32 contiguous, 16-byte aligned; slots [rows]
+ * int64, 8-byte aligned; the caches may be NULL when num_slots == 0.
+ * rows == 0 or cols == 0 is a no-op. One kernel.
+ */
+nvfp4_status_t nvfp4_dequantize_paged(const uint8_t *packed_cache,
+                                      const uint8_t *scales_cache, int64_t num_slots,
+                                      const int64_t *slots, int64_t rows, int64_t cols,
+                                      const float *gs, float *out, hipStream_t stream);
 
 /* Static English text for a status code (never NULL). */
 const char *nvfp4_status_string(nvfp4_status_t status);

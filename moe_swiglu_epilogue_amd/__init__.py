@@ -11,8 +11,8 @@ import importlib
 
 __all__ = ["nvfp4_quantize", "swiglu_nvfp4_quantize", "nvfp4_dequantize",
            "nvfp4_global_scale", "swiglu_nvfp4_global_scale", "swiglu_bf16",
-           "moe_l1_gemm_swiglu_nvfp4", "moe_l1_gemm_bf16",
-           "Nvfp4Error", "library_path"]
+           "moe_l1_gemm_swiglu_nvfp4", "moe_l1_gemm_bf16", "nvfp4_quantize_paged",
+           "nvfp4_dequantize_paged", "Nvfp4Error", "library_path"]
 
 
 def __getattr__(name):

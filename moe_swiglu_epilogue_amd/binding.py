@@ -21,7 +21,8 @@ STATUS = {0: "NVFP4_SUCCESS", 1: "NVFP4_ERROR_INVALID_VALUE",
 
 EXPORTS = ("nvfp4_quantize", "swiglu_nvfp4_quantize", "nvfp4_dequantize",
            "nvfp4_global_scale", "swiglu_nvfp4_global_scale", "swiglu_bf16",
-           "moe_l1_gemm_swiglu_nvfp4", "moe_l1_gemm_bf16", "nvfp4_status_string")
+           "moe_l1_gemm_swiglu_nvfp4", "moe_l1_gemm_bf16", "nvfp4_quantize_paged",
+           "nvfp4_dequantize_paged", "nvfp4_status_string")
 
 _LIB = None
 _vp = C.c_void_p
@@ -66,6 +67,10 @@ def _lib():
         L.moe_l1_gemm_bf16.argtypes = [_vp, _vp, _i64, _i64, _i64, _i64, _i64, _vp, _i32, _vp,
                                        _i64, _vp]
         L.moe_l1_gemm_bf16.restype = C.c_int
+        L.nvfp4_quantize_paged.argtypes = [_vp, _i64, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _vp]
+        L.nvfp4_quantize_paged.restype = C.c_int
+        L.nvfp4_dequantize_paged.argtypes = [_vp, _vp, _i64, _vp, _i64, _i64, _vp, _vp, _vp]
+        L.nvfp4_dequantize_paged.restype = C.c_int
         L.nvfp4_status_string.argtypes = [C.c_int]
         L.nvfp4_status_string.restype = C.c_char_p
         _LIB = L
@@ -323,4 +328,57 @@ def moe_l1_gemm_bf16(x: torch.Tensor, w1: torch.Tensor,
     _call(_lib().moe_l1_gemm_bf16, "moe_l1_gemm_bf16", _ptr(x), _ptr(w), tokens, hidden, n,
           _pitch(x), w.stride(1), _ptr(expert_offsets), e, _ptr(out), _pitch(out),
           _stream(stream))
+    return out
+
+
+def _slots(t: torch.Tensor, rows: int, device, name: str) -> torch.Tensor:
+    if t.dtype != torch.int64 or t.device != device or not t.is_contiguous():
+        raise TypeError("%s must be a contiguous int64 tensor on the input's device" % name)
+    if t.numel() != rows:
+        raise ValueError("%s must hold one slot per row" % name)
+    return t
+
+
+def _cache(packed_cache, scales_cache, cols):
+    for t, name in ((packed_cache, "packed_cache"), (scales_cache, "scales_cache")):
+        if t.dtype != torch.uint8 or not t.is_cuda or t.dim() != 2 or not t.is_contiguous():
+            raise TypeError("%s must be a contiguous 2-D uint8 GPU tensor" % name)
+    n = packed_cache.shape[0]
+    if (tuple(packed_cache.shape) != (n, cols // 2)
+            or tuple(scales_cache.shape) != (n, cols // 16)):
+        raise ValueError("caches must be [num_slots, cols/2] and [num_slots, cols/16]")
+    return n
+
+
+def nvfp4_quantize_paged(x: torch.Tensor, slot_mapping: torch.Tensor, packed_cache: torch.Tensor,
+                         scales_cache: torch.Tensor, gs: torch.Tensor | None = None, *,
+                         stream=None):
+    """BF16 [rows, cols] -> NVFP4 rows written into cache rows slot_mapping[r]
+    of packed_cache [num_slots, cols/2] and scales_cache [num_slots, cols/16]
+    (in place; slots outside [0, num_slots) are skipped)."""
+    x = _bf16_matrix(x, "x")
+    rows, cols = x.shape
+    _experts(gs, None, x.device)
+    slot_mapping = _slots(slot_mapping, rows, x.device, "slot_mapping")
+    n = _cache(packed_cache, scales_cache, cols)
+    _call(_lib().nvfp4_quantize_paged, "nvfp4_quantize_paged", _ptr(x), rows, cols, _pitch(x),
+          _ptr(gs), _ptr(slot_mapping), n, _ptr(packed_cache), _ptr(scales_cache),
+          _stream(stream))
+    return packed_cache, scales_cache
+
+
+def nvfp4_dequantize_paged(packed_cache: torch.Tensor, scales_cache: torch.Tensor,
+                           slots: torch.Tensor, gs: torch.Tensor | None = None, *,
+                           out: torch.Tensor | None = None, stream=None):
+    """Cache rows slots[r] -> FP32 [rows, cols] (zeros for slots outside
+    [0, num_slots))."""
+    cols = packed_cache.shape[1] * 2 if packed_cache.dim() == 2 else 0
+    n = _cache(packed_cache, scales_cache, cols)
+    device = packed_cache.device
+    _experts(gs, None, device)
+    rows = slots.numel()
+    slots = _slots(slots, rows, device, "slots")
+    out = _out(out, (rows, cols), torch.float32, device, "out")
+    _call(_lib().nvfp4_dequantize_paged, "nvfp4_dequantize_paged", _ptr(packed_cache),
+          _ptr(scales_cache), n, _ptr(slots), rows, cols, _ptr(gs), _ptr(out), _stream(stream))
     return out

@@ -138,16 +138,21 @@ constexpr int kOutStorePolicy = 17;     // output stores: sc0 sc1 (system scope;
 // that tile's bytes of its kind, so the other lanes' stores (and, in a
 // partial tile, the lanes past the data) fall out of range and are dropped.
 // Narrow path: 8-byte and 1-byte lane stores straight from registers.
+// With keep == false (a paged write whose slot is skipped) nothing is
+// stored: the wide path's windows are empty, so the hardware drops every
+// store without a branch.
 template <bool kWide>
 __device__ __forceinline__ void store_tile_outputs(uint8_t* lds_bytes, uint2 q, uint32_t sf,
                                                    const Tile& t, int b, int lane,
                                                    const Geometry& geo, uint8_t* packed,
-                                                   uint8_t* scales)
+                                                   uint8_t* scales, bool keep = true)
 {
     const int64_t tb = (int64_t)t.row * geo.bpr + t.blk0;   // first block of the tile
     if constexpr (!kWide) {
-        *reinterpret_cast<uint2*>(packed + (tb + b) * 8) = q;
-        scales[tb + b] = (uint8_t)sf;
+        if (keep) {
+            *reinterpret_cast<uint2*>(packed + (tb + b) * 8) = q;
+            scales[tb + b] = (uint8_t)sf;
+        }
     } else {
         wave_lds_sync();
         reinterpret_cast<u32x2*>(lds_bytes)[b] = u32x2{q.x, q.y};
@@ -156,9 +161,9 @@ __device__ __forceinline__ void store_tile_outputs(uint8_t* lds_bytes, uint2 q, 
         const u32x4 d = reinterpret_cast<const u32x4*>(lds_bytes)[lane];
         const bool scale_lane = lane >= kWave / 2;
         const int off = (lane & (kWave / 2 - 1)) * 16;
-        __builtin_amdgcn_raw_buffer_store_b128(d, buffer_over(packed + tb * 8, t.nblk * 8),
+        __builtin_amdgcn_raw_buffer_store_b128(d, buffer_over(packed + tb * 8, keep ? t.nblk * 8 : 0),
                                                scale_lane ? kOffRange : off, 0, kOutStorePolicy);
-        __builtin_amdgcn_raw_buffer_store_b128(d, buffer_over(scales + tb, t.nblk),
+        __builtin_amdgcn_raw_buffer_store_b128(d, buffer_over(scales + tb, keep ? t.nblk : 0),
                                                scale_lane ? off : kOffRange, 0, kOutStorePolicy);
     }
 }
@@ -418,6 +423,40 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
     return __builtin_bit_cast(uint32_t, b);
 }
 
+// ---------------------------------------------------------------------------
+// Paged KV-cache write: the standalone quantize of a row of BF16 values
+// (keys or values of one token, all heads), stored in cache row
+// slots[row] instead of row `row`. A slot outside [0, num_slots) (a padding
+// token's -1) is skipped. The slot is wave-uniform (one row per tile): one
+// scalar load per tile.
+// ---------------------------------------------------------------------------
+template <bool kWide>
+__global__ __launch_bounds__(PlainBlock::kWaves * kWave) void quantize_paged_kernel(
+    const uint16_t* __restrict__ in, int64_t ld_in, Geometry geo, const float* __restrict__ gs,
+    const int64_t* __restrict__ slots, int64_t num_slots, uint8_t* __restrict__ packed,
+    uint8_t* __restrict__ scales)
+{
+    constexpr int kWaves = PlainBlock::kWaves;
+    __shared__ u32x4 stage[kWaves][kStageSlots(PlainBlock::P)];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = uniform(threadIdx.x / kWave);
+    const int tile = blockIdx.x * kWaves + wave;
+    if (tile >= geo.tiles)
+        return;
+    const nvfp4::RowScale rs = nvfp4::row_scale(gs != nullptr ? gs[0] : 1.0f);
+    walk_tiles<PlainBlock>(in, ld_in, geo, tile, gridDim.x * kWaves, lane, stage[wave], nullptr,
+                           [&](int, const Tile& t, int b, const float (&y)[16]) {
+        const int64_t slot = slots[t.row];
+        const bool keep = slot >= 0 && slot < num_slots;
+        Tile o = t;
+        o.row = keep ? (int)slot : 0;
+        uint32_t sf;
+        const uint2 q = nvfp4::quantize16(y, rs, sf);
+        store_tile_outputs<kWide>(reinterpret_cast<uint8_t*>(stage[wave]), q, sf, o, b, lane, geo,
+                                  packed, scales, keep);
+    });
+}
+
 __global__ __launch_bounds__(FusedBlock::kWaves * kWave) void swiglu_bf16_kernel(
     const uint16_t* __restrict__ in, int64_t ld_in, Geometry geo, uint16_t* __restrict__ out,
     int64_t ld_out)
@@ -564,10 +603,13 @@ __global__ void global_scale_kernel(const uint32_t* acc, float* gs, int n)
 // computes its block, the wave transposes the tile through LDS and writes it
 // with coalesced stores.
 // ---------------------------------------------------------------------------
+// kPaged: output row r reads cache row slots[r] (a paged KV-cache read); a
+// slot outside [0, num_slots) gives a row of zeros.
+template <bool kPaged>
 __global__ __launch_bounds__(kThreads) void nvfp4_dequantize_kernel(
     const uint8_t* __restrict__ packed, const uint8_t* __restrict__ scales, Geometry geo,
     const float* __restrict__ gs, const int32_t* __restrict__ offsets, int num_experts,
-    float* __restrict__ out)
+    float* __restrict__ out, const int64_t* __restrict__ slots, int64_t num_slots)
 {
     constexpr int P = 4;
     __shared__ f32x4 stage[kWavesPerBlock][kStageSlots(P)];
@@ -580,13 +622,26 @@ __global__ __launch_bounds__(kThreads) void nvfp4_dequantize_kernel(
         const Tile t = tile_at(tile, geo);
         const int nwords = t.nblk * P;
         const float g_s = nvfp4::row_global_scale(gs, offsets, num_experts, t.row);
-        const int64_t ib = (int64_t)t.row * geo.bpr + t.blk0 + lane;
+        int64_t src_row = t.row;
+        bool valid = true;
+        if constexpr (kPaged) {
+            const int64_t slot = slots[t.row];
+            valid = slot >= 0 && slot < num_slots;
+            src_row = valid ? slot : 0;
+        }
+        const int64_t ib = src_row * geo.bpr + t.blk0 + lane;
         wave_lds_sync();
         if (lane < t.nblk) {
-            const u32x2 pv = ld_stream(reinterpret_cast<const u32x2*>(packed) + ib);
-            const uint32_t sf = __builtin_nontemporal_load(scales + ib);
             float v[16];
-            nvfp4::dequantize16(make_uint2(pv.x, pv.y), sf, g_s, v);
+            if (valid) {
+                const u32x2 pv = ld_stream(reinterpret_cast<const u32x2*>(packed) + ib);
+                const uint32_t sf = __builtin_nontemporal_load(scales + ib);
+                nvfp4::dequantize16(make_uint2(pv.x, pv.y), sf, g_s, v);
+            } else {
+#pragma unroll
+                for (int k = 0; k < 16; ++k)
+                    v[k] = 0.0f;
+            }
 #pragma unroll
             for (int k = 0; k < P; ++k)
                 lds[lds_slot(lane * P + k)] = f32x4{v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]};
@@ -799,8 +854,9 @@ nvfp4_status_t nvfp4_dequantize(const uint8_t* packed, const uint8_t* scales, in
     Geometry g;
     if ((st = make_geometry(rows, cols, g)) != NVFP4_SUCCESS)
         return st;
-    hipLaunchKernelGGL(nvfp4_dequantize_kernel, grid_for(g), dim3(kThreads), 0, stream,
-                       packed, scales, g, gs, expert_offsets, (int)num_experts, out);
+    hipLaunchKernelGGL(nvfp4_dequantize_kernel<false>, grid_for(g), dim3(kThreads), 0, stream,
+                       packed, scales, g, gs, expert_offsets, (int)num_experts, out,
+                       (const int64_t*)nullptr, (int64_t)0);
     return launched();
 }
 
@@ -881,6 +937,62 @@ nvfp4_status_t swiglu_bf16(const uint16_t* gate_up, int64_t rows, int64_t inter,
         return st;
     hipLaunchKernelGGL(swiglu_bf16_kernel, persistent_grid_for<FusedBlock>(g),
                        dim3(FusedBlock::kWaves * kWave), 0, stream, gate_up, ld_in, g, out, ld_out);
+    return launched();
+}
+
+nvfp4_status_t nvfp4_quantize_paged(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
+                                    const float* gs, const int64_t* slot_mapping,
+                                    int64_t num_slots, uint8_t* packed_cache,
+                                    uint8_t* scales_cache, hipStream_t stream)
+{
+    if (rows < 0 || cols < 0 || ld_x < cols || !extent_ok(rows, ld_x) || num_slots < 0)
+        return NVFP4_ERROR_INVALID_VALUE;
+    if (cols % 16 != 0 || num_slots > INT32_MAX)
+        return NVFP4_ERROR_UNSUPPORTED_SHAPE;
+    if (rows == 0 || cols == 0 || num_slots == 0)
+        return NVFP4_SUCCESS;   // nothing to write (every slot is out of range)
+    if (!x || !slot_mapping || !packed_cache || !scales_cache)
+        return NVFP4_ERROR_INVALID_VALUE;
+    if (!aligned(x, 16) || ld_x % 8 != 0 || !aligned(packed_cache, 8) ||
+        !aligned(slot_mapping, 8))
+        return NVFP4_ERROR_MISALIGNED;
+    Geometry g;
+    nvfp4_status_t st = make_geometry(rows, cols, g);
+    if (st != NVFP4_SUCCESS)
+        return st;
+    const dim3 grid = persistent_grid_for<PlainBlock>(g);
+    const dim3 block(PlainBlock::kWaves * kWave);
+    if (wide_stores(g, packed_cache, scales_cache))
+        hipLaunchKernelGGL(quantize_paged_kernel<true>, grid, block, 0, stream, x, ld_x, g, gs,
+                           slot_mapping, num_slots, packed_cache, scales_cache);
+    else
+        hipLaunchKernelGGL(quantize_paged_kernel<false>, grid, block, 0, stream, x, ld_x, g, gs,
+                           slot_mapping, num_slots, packed_cache, scales_cache);
+    return launched();
+}
+
+nvfp4_status_t nvfp4_dequantize_paged(const uint8_t* packed_cache, const uint8_t* scales_cache,
+                                      int64_t num_slots, const int64_t* slots, int64_t rows,
+                                      int64_t cols, const float* gs, float* out,
+                                      hipStream_t stream)
+{
+    if (rows < 0 || cols < 0 || num_slots < 0)
+        return NVFP4_ERROR_INVALID_VALUE;
+    if (cols % 16 != 0 || num_slots > INT32_MAX)
+        return NVFP4_ERROR_UNSUPPORTED_SHAPE;
+    if (rows == 0 || cols == 0)
+        return NVFP4_SUCCESS;
+    if (!slots || !out || (num_slots > 0 && (!packed_cache || !scales_cache)))
+        return NVFP4_ERROR_INVALID_VALUE;
+    if (!aligned(packed_cache, 8) || !aligned(out, 16) || !aligned(slots, 8))
+        return NVFP4_ERROR_MISALIGNED;
+    Geometry g;
+    nvfp4_status_t st = make_geometry(rows, cols, g);
+    if (st != NVFP4_SUCCESS)
+        return st;
+    hipLaunchKernelGGL(nvfp4_dequantize_kernel<true>, grid_for(g), dim3(kThreads), 0, stream,
+                       packed_cache, scales_cache, g, gs, (const int32_t*)nullptr, 0, out, slots,
+                       num_slots);
     return launched();
 }
 

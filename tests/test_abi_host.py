@@ -41,6 +41,7 @@ def test_header_declares_the_entry_points():
                                   "nvfp4_dequantize", "nvfp4_global_scale",
                                   "swiglu_nvfp4_global_scale", "swiglu_bf16",
                                   "moe_l1_gemm_swiglu_nvfp4", "moe_l1_gemm_bf16",
+                                  "nvfp4_quantize_paged", "nvfp4_dequantize_paged",
                                   "nvfp4_status_string"])
 
 
@@ -227,6 +228,46 @@ def test_gemm_validation(lib):
     assert gb(lib, tokens=0, x=None, w=None, out=None) == OK
 
 
+def qp(lib, x=A16, rows=4, cols=32, ld=32, gs=None, slots=A16, ns=8, packed=A16, scales=A16):
+    return lib.nvfp4_quantize_paged(x, rows, cols, ld, gs, slots, ns, packed, scales, None)
+
+
+def dp(lib, packed=A16, scales=A16, ns=8, slots=A16, rows=4, cols=32, gs=None, out=A16):
+    return lib.nvfp4_dequantize_paged(packed, scales, ns, slots, rows, cols, gs, out, None)
+
+
+def test_paged_validation(lib):
+    assert qp(lib, rows=-1) == INVALID
+    assert qp(lib, ns=-1) == INVALID
+    assert qp(lib, ld=16) == INVALID
+    assert qp(lib, cols=24, ld=24) == SHAPE
+    assert qp(lib, ns=2**31) == SHAPE
+    assert qp(lib, x=None) == INVALID
+    assert qp(lib, slots=None) == INVALID
+    assert qp(lib, packed=None) == INVALID
+    assert qp(lib, scales=None) == INVALID
+    assert qp(lib, x=A16 + 2) == MISALIGNED
+    assert qp(lib, ld=36) == MISALIGNED
+    assert qp(lib, packed=A16 + 4) == MISALIGNED
+    assert qp(lib, slots=A16 + 4) == MISALIGNED
+    assert qp(lib, rows=2**31, cols=16, ld=16) == SHAPE
+    # nothing to write succeeds without launching (NULL pointers are fine)
+    assert qp(lib, x=None, rows=0, slots=None, packed=None, scales=None) == OK
+    assert qp(lib, x=None, slots=None, ns=0, packed=None, scales=None) == OK
+    assert dp(lib, rows=-1) == INVALID
+    assert dp(lib, ns=-1) == INVALID
+    assert dp(lib, cols=24) == SHAPE
+    assert dp(lib, ns=2**31) == SHAPE
+    assert dp(lib, slots=None) == INVALID
+    assert dp(lib, out=None) == INVALID
+    assert dp(lib, packed=None) == INVALID
+    assert dp(lib, out=A16 + 8) == MISALIGNED
+    assert dp(lib, slots=A16 + 4) == MISALIGNED
+    assert dp(lib, rows=0, slots=None, out=None, packed=None, scales=None) == OK
+    # an empty cache may be NULL (every row reads as zeros)
+    assert dp(lib, ns=0, packed=None, scales=None, rows=0) == OK
+
+
 def test_pitch_extent_overflow_is_rejected(lib):
     """A row pitch whose byte extent rows * ld * 2 leaves int64 cannot
     describe a real buffer: every entry point says INVALID and computes
@@ -264,3 +305,8 @@ def test_binding_rejects_host_tensors():
         M.swiglu_nvfp4_global_scale(torch.zeros(4, 64, dtype=torch.bfloat16))
     with pytest.raises(TypeError):
         M.swiglu_bf16(torch.zeros(4, 64, dtype=torch.bfloat16))
+    cache_p, cache_s = torch.zeros(8, 16, dtype=torch.uint8), torch.zeros(8, 2, dtype=torch.uint8)
+    with pytest.raises(TypeError):
+        M.nvfp4_quantize_paged(x, torch.zeros(4, dtype=torch.int64), cache_p, cache_s)
+    with pytest.raises(TypeError):
+        M.nvfp4_dequantize_paged(cache_p, cache_s, torch.zeros(4, dtype=torch.int64))

@@ -1,7 +1,7 @@
 """Code generation checks on the gfx950 ISA of the library (CPU only: hipcc
 cross-compiles the device code to assembly).
 
-* The pipelined store loops (quantize, compact SwiGLU) must never wait for
+* The pipelined store loops (quantize, paged write, compact SwiGLU) must never wait for
   their own output stores:
   on gfx9 the vmcnt counter covers stores as well as loads, so the loop
   that holds a wide-store quantize kernel's output stores (found from its
@@ -72,8 +72,9 @@ def loop_waits_for_stores(isa):
     """Names of the pipelined store kernels (wide-store quantize, compact
     SwiGLU) whose store loop has a vmcnt(0)."""
     ks = {n: body for n, body in _kernels(isa).items()
-          if ("quantize_tiles_kernel" in n and "Lb1E" in n) or "swiglu_bf16_kernel" in n}
-    assert len(ks) == 3, sorted(ks)
+          if (("quantize_tiles_kernel" in n or "quantize_paged_kernel" in n) and "Lb1E" in n)
+          or "swiglu_bf16_kernel" in n}
+    assert len(ks) == 4, sorted(ks)
     bad = []
     for name, body in ks.items():
         loops = store_loops(body)
