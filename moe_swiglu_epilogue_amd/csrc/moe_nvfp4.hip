@@ -215,7 +215,9 @@ struct PlainBlock {
     }
 };
 
-// A wave's walk over its tiles (first `tile`, then every `stride`-th):
+// A wave's walk over its tiles (first `tile`, then every `stride`-th; the
+// caller has tile < geo.tiles, and runs `setup` itself on waves without a
+// tile so that every wave reaches its barrier once):
 // keeps one tile in flight and calls op(tile, t, b, y) with each lane's block b of
 // tile t and its 16 values y. Loop invariant: tile t is staged in LDS and no
 // loads are in flight. Each pass issues the loads of the next tile first,
@@ -223,15 +225,18 @@ struct PlainBlock {
 // store (its stores are the only memory operations younger than those
 // loads, so the wait before staging does not wait for them) and may use the
 // wave's LDS area between the two LDS syncs of the pass.
-template <class Block, class Op>
+template <class Block, class Setup, class Op>
 __device__ __forceinline__ void walk_tiles(const uint16_t* in, int64_t ld_in, const Geometry& geo,
                                            int tile, int stride, int lane, u32x4* lds,
-                                           const uint8_t* sig, Op&& op)
+                                           const uint8_t* sig, Setup&& setup, Op&& op)
 {
     constexpr int P = Block::P;
     Tile t = tile_at(tile, geo);
     u32x4 v[P];
     load_tile<P>(v, in, ld_in, t, lane);
+    // the workgroup's one-time set-up (LDS tables, ending in a barrier) runs
+    // while the first tile's loads are in flight
+    setup();
     stage_tile<P>(lds, v, lane);
     // Keeps the prologue's staging out of the loop: were the compiler to
     // merge it with the loop's own staging at the loop head, the merged
@@ -368,20 +373,24 @@ __global__ __launch_bounds__(Block::kWaves * kWave) void quantize_tiles_kernel(
     const int tile = blockIdx.x * kWaves + wave;
     const int stride = gridDim.x * kWaves;
     const bool lds_experts = offsets != nullptr && num_experts <= kLdsExperts;
-    fill_sigma_table<Block>(sig);
-    if (lds_experts)
-        fill_expert_table<kWaves * kWave>(tab, offsets, gs, num_experts);
-    if (Block::kSigmaTable || lds_experts)
-        __syncthreads();
-    if (tile >= geo.tiles)
+    auto setup = [&]() {
+        fill_sigma_table<Block>(sig);
+        if (lds_experts)
+            fill_expert_table<kWaves * kWave>(tab, offsets, gs, num_experts);
+        if (Block::kSigmaTable || lds_experts)
+            __syncthreads();
+    };
+    if (tile >= geo.tiles) {
+        setup();
         return;
+    }
     // Without experts the global scale (and its reciprocal) is the same for
     // every row: computed once here instead of per tile.
     nvfp4::RowScale rs = nvfp4::row_scale(gs != nullptr ? gs[0] : 1.0f);
     ExpertBatch batch;
     int n = 0;   // tiles done by this wave
     walk_tiles<Block>(in, ld_in, geo, tile, stride, lane, lds,
-                      reinterpret_cast<const uint8_t*>(sig),
+                      reinterpret_cast<const uint8_t*>(sig), setup,
                       [&](int tile_index, const Tile& t, int b, const float (&y)[16]) {
         if (lds_experts) {
             const int j = n & (kWave - 1);
@@ -445,7 +454,7 @@ __global__ __launch_bounds__(PlainBlock::kWaves * kWave) void quantize_paged_ker
         return;
     const nvfp4::RowScale rs = nvfp4::row_scale(gs != nullptr ? gs[0] : 1.0f);
     walk_tiles<PlainBlock>(in, ld_in, geo, tile, gridDim.x * kWaves, lane, stage[wave], nullptr,
-                           [&](int, const Tile& t, int b, const float (&y)[16]) {
+                           [] {}, [&](int, const Tile& t, int b, const float (&y)[16]) {
         const int64_t slot = slots[t.row];
         const bool keep = slot >= 0 && slot < num_slots;
         Tile o = t;
@@ -469,12 +478,16 @@ __global__ __launch_bounds__(FusedBlock::kWaves * kWave) void swiglu_bf16_kernel
     const int wave = uniform(threadIdx.x / kWave);
     u32x4* lds = stage[wave];
     const int tile = blockIdx.x * kWaves + wave;
-    fill_sigma_table<Block>(sig);
-    __syncthreads();
-    if (tile >= geo.tiles)
+    auto setup = [&]() {
+        fill_sigma_table<Block>(sig);
+        __syncthreads();
+    };
+    if (tile >= geo.tiles) {
+        setup();
         return;
+    }
     walk_tiles<Block>(in, ld_in, geo, tile, gridDim.x * kWaves, lane, lds,
-                      reinterpret_cast<const uint8_t*>(sig),
+                      reinterpret_cast<const uint8_t*>(sig), setup,
                       [&](int, const Tile& t, int b, const float (&y)[16]) {
         u32x4 w[2];
 #pragma unroll
@@ -538,12 +551,16 @@ __global__ __launch_bounds__(Block::kWaves * kWave) void amax_tiles_kernel(
     const int wave = uniform(threadIdx.x / kWave);
     const int tile = blockIdx.x * kWaves + wave;
     const int stride = gridDim.x * kWaves;
-    fill_sigma_table<Block>(sig);
-    for (int i = threadIdx.x; i < groups; i += kWaves * kWave)
-        part[i] = 0u;
-    if (offsets != nullptr)
-        fill_expert_table<kWaves * kWave>(tab, offsets, nullptr, groups);
-    __syncthreads();
+    auto setup = [&]() {
+        fill_sigma_table<Block>(sig);
+        for (int i = threadIdx.x; i < groups; i += kWaves * kWave)
+            part[i] = 0u;
+        if (offsets != nullptr)
+            fill_expert_table<kWaves * kWave>(tab, offsets, nullptr, groups);
+        __syncthreads();
+    };
+    if (tile >= geo.tiles)
+        setup();
     if (tile < geo.tiles) {
         // Each lane keeps a running max over the wave's consecutive tiles of
         // one expert; the wave reduces it and folds it into the workgroup's
@@ -558,7 +575,7 @@ __global__ __launch_bounds__(Block::kWaves * kWave) void amax_tiles_kernel(
                 atomicMax(&part[cur], __float_as_uint(m));
         };
         walk_tiles<Block>(in, ld_in, geo, tile, stride, lane, stage[wave],
-                          reinterpret_cast<const uint8_t*>(sig),
+                          reinterpret_cast<const uint8_t*>(sig), setup,
                           [&](int tile_index, const Tile&, int, const float (&y)[16]) {
             int e = 0;
             if (offsets != nullptr) {
