@@ -3,16 +3,18 @@
 //
 // Kernels: the fused SwiGLU + NVFP4 quantize and the standalone quantize
 // (quantize_tiles_kernel), the dequantize, the global-scale pre-pass
-// (amax_tiles_kernel and two small helpers) and the compact BF16 SwiGLU pass.
-// The grouped GEMM with the fused epilogue is in moe_gemm.hip.
+// (amax_tiles_kernel and two small helpers), the compact BF16 SwiGLU pass,
+// and the paged KV-cache write (quantize_paged_kernel) and read (the
+// dequantize with a slot indirection). The grouped GEMM with the fused
+// epilogue is in moe_gemm.hip.
 //
 // Work decomposition: one lane owns one NVFP4 block of 16 output values; one
 // wave64 owns a "tile" of 64 consecutive blocks of one row, so the row index
 // and its base addresses are wave-uniform (scalar registers). Tiles are
 // numbered row-major and handed to waves with a grid-stride loop: the
-// quantize, pre-pass and compact kernels walk them with a persistent grid
-// sized per kernel (workgroup waves and workgroups per CU measured on
-// MI355X), the dequantize with one tile per wave.
+// quantize, paged-write, pre-pass and compact kernels walk them with a
+// persistent grid sized per kernel (workgroup waves and workgroups per CU
+// measured on MI355X), the dequantize with one tile per wave.
 //
 // Method: "nvfp4-megamoe-kernel" log, "NVFP4-1.1_APPROACH_PART_2.md"
 // (fused-epilogue design: SiLU(gate) and SwiGLU in FP32 registers, every two
