@@ -9,13 +9,19 @@ for bit, over the BF16 value space:
   (random signs): about 2 million element quotients across 127 scales.
 
 Both runs use a power-of-two global scale (the v_rcp_f32 path of the element
-quotient) and a general one (the IEEE-division path)."""
+quotient) and a general one (the IEEE-division path).
+
+The fused path gets the same treatment for its SwiGLU: every finite BF16 gate
+value (both signs, zero and subnormals included: every entry of the kernel's
+sigmoid table and both clamped ends) times up values 1, -1, 0.5 and -0.75,
+each y checked against the oracle with the fused acceptance rules."""
 import numpy as np
 import pytest
 import torch
 
 import oracle
 import parity as P
+from moe_swiglu_epilogue_amd import workloads as W
 
 pytestmark = pytest.mark.gpu
 
@@ -59,3 +65,35 @@ def test_standalone_quantize_over_bf16_space(gs):
     P.assert_bytes_equal("scales", s.cpu().numpy(), rs)
     P.assert_bytes_equal("packed", p.cpu().numpy(), rp)
     say("bit-exact: %d elements, %d distinct scale bytes" % (x.size, np.unique(rs).size))
+
+
+def gate_sweep_input(inter=2048):
+    gates = np.concatenate([np.arange(0, 0x7F80), np.arange(0x8000, 0xFF80)]).astype(np.uint16)
+    ups = np.array([0x3F80, 0xBF80, 0x3F00, 0xBF40], np.uint16)        # 1, -1, 0.5, -0.75
+    g = np.tile(gates, ups.size)
+    u = np.repeat(ups, gates.size)
+    n = -(-g.size // inter) * inter
+    g = np.concatenate([g, np.zeros(n - g.size, np.uint16)]).reshape(-1, inter)
+    u = np.concatenate([u, np.full(n - u.size, 0x3F80, np.uint16)]).reshape(-1, inter)
+    return W.interleave(g, u)
+
+
+def test_fused_swiglu_over_every_bf16_gate():
+    import moe_swiglu_epilogue_amd as M
+    x = gate_sweep_input()
+    say("fused quantize over every finite BF16 gate:", x.shape)
+    xt = torch.from_numpy(x.view(np.int16)).cuda().view(torch.bfloat16)
+    p, s, y = M.swiglu_nvfp4_quantize(xt, swiglu_out=True)
+    torch.cuda.synchronize()
+    p, s, y = p.cpu().numpy(), s.cpu().numpy(), y.cpu().numpy()
+    rp, rs, ry, rbsf, rv = oracle.swiglu_quantize(x, diag=True)
+    rep = P.fused_report(p, s, y, rp, rs, ry, rbsf, rv)
+    say("every-gate sweep:", rep)
+    # every y within the SwiGLU tolerance; the GPU's bytes are exactly the
+    # quantize of its own y; every byte that differs from the oracle's lies
+    # at a rounding boundary (a directed sweep, so the exempt count is
+    # reported, not capped by the random-workload fraction)
+    assert rep.swiglu_bad == 0, rep
+    assert rep.requant_mismatch == 0, rep
+    assert rep.scale_mismatch == rep.scale_exempt, rep
+    assert rep.code_mismatch == rep.code_exempt, rep
