@@ -97,7 +97,9 @@ class FusedReport:
 def check_swiglu(y_gpu: np.ndarray, y_ref: np.ndarray) -> int:
     yg = np.asarray(y_gpu, np.float64)
     yr = np.asarray(y_ref, np.float64)
-    close = np.abs(yg - yr) <= SWIGLU_RTOL * np.abs(yr)
+    # a zero y must also carry the reference's sign (it is the code's sign
+    # bit); for nonzero y the relative bound already implies the same sign
+    close = (np.abs(yg - yr) <= SWIGLU_RTOL * np.abs(yr)) & (np.signbit(yg) == np.signbit(yr))
     tiny = (np.abs(yr) < SWIGLU_ABS_FLOOR) & (np.signbit(yg) == np.signbit(yr))
     return int(np.count_nonzero(~(close | tiny)))
 
