@@ -273,7 +273,10 @@ def _weights(w1: torch.Tensor, x: torch.Tensor):
         raise TypeError("w1 must be bfloat16 on the activations' device")
     if w1.dim() == 2:
         w1 = w1.unsqueeze(0)
-    if w1.dim() != 3 or w1.stride(2) != 1 or w1.stride(0) != w1.shape[1] * w1.stride(1):
+    # the expert stride only matters between experts (a size-1 dimension may
+    # carry any stride, such as the 0 of a NumPy newaxis)
+    if (w1.dim() != 3 or w1.stride(2) != 1
+            or (w1.shape[0] > 1 and w1.stride(0) != w1.shape[1] * w1.stride(1))):
         raise ValueError("w1 must be [E, n, hidden] with unit column stride and packed experts")
     return w1
 

@@ -389,18 +389,22 @@ __device__ __forceinline__ void stage_accumulators(float* c, const f32x16 (&acc)
 // silu(g) u = g u / (1 + e^-g), e^-g = 2^(-g log2 e). log2 e = kL2eHi + kL2eLo
 // (kL2eHi = RN(log2 e)); the product -g kL2eHi is split into its rounded
 // value p and exact error (fma), so 2^(-g log2 e) = 2^p 2^t with
-// t = perr - g kL2eLo, |t| < 2e-5 for |g| < 100, and 2^t = 1 + t ln 2 to
+// t = perr - g kL2eLo, |t| < 2e-5 for |g| <= 128, and 2^t = 1 + t ln 2 to
 // better than 1e-10. v_exp_f32 and v_rcp_f32 are about 1 ulp each: about
-// 4 ulp in all. g < -88.7 overflows 2^p and gives y = +-0 (the exact |y|
-// is below 1e-30 while |u| < 1e6).
+// 4 ulp in all. The sigmoid's argument is clamped to [-128, 128], where it
+// has already saturated in FP32 (1 above; below, 2^p overflows, 1/(1 + inf)
+// is 0 and y is a zero with the sign of g u): unclamped, -g log2 e overflows
+// for |g| > 2.3e38 and the split turns into 0 * inf (NaN) or a zero of the
+// wrong sign.
 __device__ __forceinline__ float swiglu_f32(float g, float u)
 {
     const float kL2eHi = 0x1.715476p+0f;
     const float kL2eLo = 0x1.4ae0bep-26f;
     const float kLn2 = 0x1.62e430p-1f;
-    const float p = -g * kL2eHi;
-    const float perr = __builtin_fmaf(-g, kL2eHi, -p);
-    const float t = __builtin_fmaf(-g, kL2eLo, perr);
+    const float gc = __builtin_fminf(__builtin_fmaxf(g, -128.0f), 128.0f);
+    const float p = -gc * kL2eHi;
+    const float perr = __builtin_fmaf(-gc, kL2eHi, -p);
+    const float t = __builtin_fmaf(-gc, kL2eLo, perr);
     const float e0 = __builtin_amdgcn_exp2f(p);
     // e0 (1 + t ln 2), not e0 + e0 t ln 2: when 2^p overflows the factor is
     // positive and inf stays inf (inf - inf would be NaN)

@@ -92,8 +92,8 @@ def test_gemm_exact_operands(M, tokens, hidden, inter, experts, seed):
     say("fused GEMM exact", rep)
     if rep.swiglu_bad:
         yg, yr = r["y"].astype(np.float64), ry.astype(np.float64)
-        bad = np.argwhere(~((np.abs(yg - yr) <= 2e-6 * np.abs(yr)) |
-                            ((np.abs(yr) < 1e-30) & (np.signbit(yg) == np.signbit(yr)))))
+        bad = np.argwhere(~(((np.abs(yg - yr) <= 2e-6 * np.abs(yr)) | (np.abs(yr) < 1e-30))
+                            & (np.signbit(yg) == np.signbit(yr))))
         for t, j in bad[:8]:
             col = 16 * (j // 8) + j % 8
             say("swiglu outlier: g %r u %r gpu %r ref %r rel %.3g" % (
@@ -192,3 +192,52 @@ def test_gemm_prefill_shape_sampled(M):
     codes, scl, worst = check_random(g, r, rows)
     say("prefill-shaped sampled rows %d: code mismatch %.2e, scale mismatch %.2e; worst err/tol %.3f"
         % (rows.size, codes, scl, worst))
+
+
+def test_gemm_epilogue_over_every_bf16_gate(M):
+    """The fused epilogue's FP32 SwiGLU (exp2 and reciprocal, not the table of
+    the standalone kernel) over every finite BF16 gate value times up values
+    1, -1, 0.5 and -0.75. One-hot activations make the GEMM deliver chosen
+    accumulators exactly: x[t][k] = (k == t), so acc[t][n] = w1[n][t]."""
+    inter, rows = 4096, 64
+    gates = np.concatenate([np.arange(0, 0x7F80), np.arange(0x8000, 0xFF80)]).astype(np.uint16)
+    ups = np.array([0x3F80, 0xBF80, 0x3F00, 0xBF40], np.uint16)
+    g = np.tile(gates, ups.size)
+    u = np.repeat(ups, gates.size)
+    n = rows * inter
+    g = np.concatenate([g, np.zeros(n - g.size, np.uint16)]).reshape(rows, inter)
+    u = np.concatenate([u, np.full(n - u.size, 0x3F80, np.uint16)]).reshape(rows, inter)
+    acc_bits = W.interleave(g, u)                                   # [rows][2I]
+    x = np.where(np.eye(rows, dtype=bool), np.uint16(0x3F80), np.uint16(0))
+    w1 = np.ascontiguousarray(acc_bits.T)[None]                     # [1][2I][rows]
+    off = np.array([0, rows], np.int32)
+    wl = W.GemmWorkload(x, w1, off, inter)
+    acc = oracle.moe_l1_gemm(x, w1, off)
+    acc32 = acc.astype(np.float32)
+    # each accumulator is its chosen value, except that a -0 gate sums with
+    # +0 products to +0 (IEEE), on the GPU as in the oracle
+    got = (acc32.view(np.uint32) >> 16).astype(np.uint16)
+    assert np.array_equal(got[acc_bits != 0x8000], acc_bits[acc_bits != 0x8000])
+    assert (got[acc_bits == 0x8000] == 0).all()
+    say("moe_l1_gemm every BF16 gate through the epilogue:", x.shape, w1.shape)
+    r = run(M, wl)
+    P.assert_bytes_equal("bf16 GEMM", r["bf16"], oracle.f32_to_bf16(acc32))
+    ry = oracle.swiglu_f32(acc32)
+    rp, rs, rbsf, rv = oracle.quantize_f32(ry, None, diag=True)
+    rep = P.fused_report(r["p"], r["s"], r["y"], rp, rs, ry, rbsf, rv)
+    say("every-gate epilogue:", rep)
+    if rep.swiglu_bad:
+        yg, yr = r["y"].astype(np.float64), ry.astype(np.float64)
+        bad = np.argwhere(~(((np.abs(yg - yr) <= 2e-6 * np.abs(yr)) | (np.abs(yr) < 1e-30))
+                            & (np.signbit(yg) == np.signbit(yr))))
+        for t, j in bad[:: max(1, len(bad) // 24)][:24]:
+            col = 16 * (j // 8) + j % 8
+            say("outlier: g %r (0x%04x) u %r gpu %r ref %r" % (
+                float(acc32[t, col]), int(acc_bits[t, col]), float(acc32[t, col + 8]),
+                float(yg[t, j]), float(yr[t, j])))
+        gbad = np.array([acc32[t, 16 * (j // 8) + j % 8] for t, j in bad])
+        say("outlier gates: min %r max %r" % (float(gbad.min()), float(gbad.max())))
+    assert rep.swiglu_bad == 0, rep
+    assert rep.requant_mismatch == 0, rep
+    assert rep.scale_mismatch == rep.scale_exempt, rep
+    assert rep.code_mismatch == rep.code_exempt, rep
