@@ -97,3 +97,20 @@ def test_fused_swiglu_over_every_bf16_gate():
     assert rep.requant_mismatch == 0, rep
     assert rep.scale_mismatch == rep.scale_exempt, rep
     assert rep.code_mismatch == rep.code_exempt, rep
+
+
+def test_compact_swiglu_over_every_bf16_gate():
+    """The compact BF16 SwiGLU pass (same sigmoid table, then round to BF16)
+    over the same sweep: every output equals the oracle's BF16 rounding of
+    its SwiGLU, except within the SwiGLU tolerance of a BF16 midpoint (and
+    zeros below the tiny floor with matching sign)."""
+    import moe_swiglu_epilogue_amd as M
+    x = gate_sweep_input()
+    say("compact swiglu over every finite BF16 gate:", x.shape)
+    xt = torch.from_numpy(x.view(np.int16)).cuda().view(torch.bfloat16)
+    out = M.swiglu_bf16(xt)
+    torch.cuda.synchronize()
+    got = out.view(torch.int16).cpu().numpy().view(np.uint16)
+    rep = P.bf16_report(got, oracle.swiglu_bf16(x), oracle.swiglu(x))
+    say("every-gate compact:", rep)
+    assert rep.mismatch == rep.exempt + rep.tiny, rep
