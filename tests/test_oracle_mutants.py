@@ -98,6 +98,8 @@ PY_MUTANTS = {
     "gs_reciprocal_multiply": lambda a: np.where(
         a > 0, np.asarray(a, np.float32) * (np.float32(1.0) / np.float32(2688.0)),
         np.float32(1.0)).astype(np.float32),
+    "gs_no_clamp": lambda a: np.where(a > 0, np.asarray(a, np.float32) / np.float32(2688.0),
+                                      np.float32(1.0)).astype(np.float32),
 }
 
 

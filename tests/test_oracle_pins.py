@@ -260,7 +260,8 @@ def pin_expert_global_scale():
     """gs = RN32(amax / (6 * 448)): exact powers of two, 1.0 for an all-zero
     expert, the nearest binary32 to the exact rational quotient, and the
     defining property that the expert's largest block gets scale byte 0x7e
-    (the FP8 maximum 448)."""
+    (the FP8 maximum 448); clamped to [2^-100, 2^100] beyond that range
+    (scale byte below 0x7e under the lower bound, saturated above)."""
     from fractions import Fraction as F
     ks = np.arange(-20, 21)
     amax = (2688.0 * 2.0 ** ks).astype(np.float32)
@@ -279,6 +280,17 @@ def pin_expert_global_scale():
         x[5] = -ai
         _, sf, _, _ = oracle.quantize_block(x, float(gi))
         assert sf == 0x7E, (ai, gi, hex(sf))
+    # the clamp to [2^-100, 2^100]: exactly at both bounds, and beyond them
+    lo, hi = np.float32(2.0 ** -100), np.float32(2.0 ** 100)
+    edge = np.array([2688.0 * 2.0 ** -100, 2688.0 * 2.0 ** -101, 2688.0 * 2.0 ** -120, 1e-40,
+                     2688.0 * 2.0 ** 100, 2688.0 * 2.0 ** 101, 3.0e38], np.float32)
+    want = np.array([lo, lo, lo, lo, hi, hi, hi], np.float32)
+    assert np.array_equal(oracle.expert_global_scale(edge), want), oracle.expert_global_scale(edge)
+    for ai, gi, top in ((edge[2], lo, False), (edge[6], hi, True)):
+        x = np.zeros(16, np.float32)
+        x[3] = ai
+        _, sf, _, _ = oracle.quantize_block(x, float(gi))
+        assert (sf == 0x7E) if top else (sf < 0x7E), (ai, hex(sf))
 
 
 def pin_bf16_vs_torch(step: int = 997, chunk: int = 1 << 24):
