@@ -143,7 +143,10 @@ nvfp4_status_t nvfp4_dequantize(const uint8_t *packed, const uint8_t *scales,
  * quantizer will see, amax_e, and the FP32 global scale
  *     gs[e] = RN(amax_e / (6 * 448))        (1.0 when amax_e == 0 or the
  *                                            expert has no rows),
- * which puts the expert's largest block scale on the FP8 maximum 448.
+ * which puts the expert's largest block scale on the FP8 maximum 448,
+ * clamped to [2^-100, 2^100], the global scales the quantize calls accept
+ * (an expert with amax below 2688 * 2^-100 keeps block scales under 448; one
+ * above 2688 * 2^100 saturates them).
  * Page: "NVFP4-1.1_APPROACH_PART_2.md" (the fused kernel's l2_global_scale
  * parameter, the decode-direction global scale in the FP8 scale rule), with
  * the per-expert amax / (6 * 448) recipe of the ragged grouped MoE workload.

@@ -607,13 +607,15 @@ __global__ __launch_bounds__(Block::kWaves * kWave) void amax_tiles_kernel(
     }
 }
 
-// gs[e] = RN(amax[e] / 2688) (IEEE division), 1.0 for an empty or all-zero
-// expert; acc holds the amax bits and may be the gs array itself.
+// gs[e] = RN(amax[e] / 2688) (IEEE division) clamped to [2^-100, 2^100], the
+// global scales the quantizers are defined for; 1.0 for an empty or all-zero
+// expert. acc holds the amax bits and may be the gs array itself.
 __global__ void global_scale_kernel(const uint32_t* acc, float* gs, int n)
 {
+    const float lo = 0x1p-100f, hi = 0x1p+100f;
     for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) {
         const float a = __uint_as_float(acc[i]);
-        gs[i] = a > 0.0f ? a / kFp4Fp8Max : 1.0f;
+        gs[i] = a > 0.0f ? __builtin_fminf(__builtin_fmaxf(a / kFp4Fp8Max, lo), hi) : 1.0f;
     }
 }
 

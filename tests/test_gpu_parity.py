@@ -312,6 +312,31 @@ def test_global_scale_empty_and_zero(M):
         assert am[2] > 0 and gs[2] == np.float32(am[2]) / np.float32(2688.0)
 
 
+def test_global_scale_clamped_range(M):
+    """Experts with tiny (~1e-30) and huge (~1e36) values get global scales
+    clamped to 2^-100 and 2^100, bit-exact against the oracle, and the
+    quantize with those scales stays bit-exact."""
+    rng = np.random.default_rng(61)
+    rows, cols = 48, 256
+    x = rng.standard_normal((rows, cols))
+    x[:16] *= 1e-30
+    x[16:32] *= 1e36
+    xb = W.to_bf16_bits(x)
+    off = np.array([0, 16, 32, 48], np.int32)
+    say("global scale clamp: experts of magnitude 1e-30, 1e36, 1")
+    gs, am = M.nvfp4_global_scale(dev_bf16(xb), dev(off), amax=True)
+    gs, am = host(gs), host(am)
+    ref_am = oracle.group_amax(W.bf16_bits_to_f32(xb), off)
+    ref_gs = oracle.expert_global_scale(ref_am)
+    assert np.array_equal(am.view(np.uint32), ref_am.view(np.uint32))
+    assert np.array_equal(gs.view(np.uint32), ref_gs.view(np.uint32))
+    assert gs[0] == np.float32(2.0 ** -100) and gs[1] == np.float32(2.0 ** 100)
+    p, s = M.nvfp4_quantize(dev_bf16(xb), dev(gs), dev(off))
+    rp, rs = oracle.quantize_bf16(xb, oracle.rows_global_scale(gs, off, rows))
+    P.assert_bytes_equal("scales", host(s), rs)
+    P.assert_bytes_equal("packed", host(p), rp)
+
+
 # ---- compact SwiGLU pass (two-pass variant) -------------------------------------------
 def bf16_check(M, x, what, ld_out=None, quantize_cols=None):
     rows, inter = x.shape[0], x.shape[1] // 2
