@@ -281,14 +281,16 @@ __device__ __forceinline__ void read_frags(Frags& f, const uint8_t* stage, int k
                                                 stage + kRegionBytes + (kWaveN * wn + 32 * t) * kRowBytes + off));
 }
 
-// acc[tm][tn] += A fragment tm x B fragment tn: 16 MFMAs.
+// acc[tm][tn] += A fragment tm x B fragment tn for the kCount MFMA tiles
+// kFirst .. kFirst + kCount - 1 (tile i = row tile i / kTN, column tile
+// i % kTN); the whole step is 16 MFMAs.
+template <int kFirst = 0, int kCount = kTM * kTN>
 __device__ __forceinline__ void mma_step(f32x16 (&acc)[kTM][kTN], const Frags& f)
 {
 #pragma unroll
-    for (int tm = 0; tm < kTM; ++tm)
-#pragma unroll
-        for (int tn = 0; tn < kTN; ++tn)
-            acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[tm], f.b[tn], acc[tm][tn], 0, 0, 0);
+    for (int i = kFirst; i < kFirst + kCount; ++i)
+        acc[i / kTN][i % kTN] =
+            __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i / kTN], f.b[i % kTN], acc[i / kTN][i % kTN], 0, 0, 0);
 }
 
 // Fixes the issue order of one pipeline phase for the scheduler: kPairs
@@ -307,25 +309,23 @@ __device__ __forceinline__ void phase_order()
     __builtin_amdgcn_sched_barrier(0);
 }
 
-// One pass of the K loop over the slice staged in stage kb % 2; with kLoad
-// it first starts the loads of slice kb + 1 into the other stage (read last
-// in the previous pass, which ended with a barrier) and waits for them at
-// the end. One wave per SIMD has no other wave to hide its waits behind, so
-// the pass is software-pipelined by hand: the fragments of K step kk + 1
-// are read from LDS while the MFMAs of step kk issue. Two fragment sets
-// suffice: a set is refilled only after every MFMA reading it has issued.
-// Ends with a barrier (after which every wave's loads of slice kb + 1 are in
-// LDS).
-template <bool kLoad>
-__device__ __forceinline__ void k_pass(const TileSrc& src, uint8_t* smem, f32x16 (&acc)[kTM][kTN],
-                                       int kb, int wave, int wm, int wn, int lane)
+// MFMAs of K step 3 that a pass leaves for after the next barrier.
+constexpr int kHeld = 16;
+constexpr int kStep = kTM * kTN;
+
+// The MFMAs of slice kb staged in stage kb % 2, software-pipelined by hand:
+// one wave per SIMD has no other wave to hide its waits behind, so the
+// fragments of K step kk + 1 are read from LDS while the MFMAs of step kk
+// issue. Two fragment sets suffice: a set is refilled only after every MFMA
+// reading it has issued. On entry f0 holds (or is being read with) step 0.
+// The pass stops kHeld MFMAs short of the end of step 3; f1 keeps that
+// step's fragments for them, and the caller issues them after the next
+// barrier, where they cover the latency of the next slice's first fragment
+// reads and the issue of its loads (otherwise the matrix core idles
+// through both).
+__device__ __forceinline__ void k_pass(const uint8_t* st, f32x16 (&acc)[kTM][kTN], Frags& f0,
+                                       Frags& f1, int wm, int wn, int lane)
 {
-    if constexpr (kLoad)
-        load_slice(src, smem + ((kb + 1) & 1) * kStageBytes, (kb + 1) * kBK, wave);
-    const uint8_t* st = smem + (kb & 1) * kStageBytes;
-    Frags f0, f1;
-    read_frags(f0, st, 0, wm, wn, lane);
-    __builtin_amdgcn_sched_barrier(0);
     mma_step(acc, f0);
     read_frags(f1, st, 1, wm, wn, lane);
     phase_order<0x100, kTM + kTN>();
@@ -335,13 +335,45 @@ __device__ __forceinline__ void k_pass(const TileSrc& src, uint8_t* smem, f32x16
     mma_step(acc, f0);
     read_frags(f1, st, 3, wm, wn, lane);
     phase_order<0x100, kTM + kTN>();
-    mma_step(acc, f1);
-    if constexpr (kLoad)
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
+    mma_step<0, kStep - kHeld>(acc, f1);
+    __builtin_amdgcn_sched_barrier(0);
 }
 
-// The K loop of one tile. Ends with a barrier after the last slice's reads.
+// The held MFMAs of K step 3 of the previous slice (fragments in f1), with
+// the next slice's loads (k0) issued between them: load n of the wave is
+// its x (n even) or w (n odd) load of rows 64 w + 8 (n / 2) .. +8, so the
+// matrix core is not idle while they issue.
+__device__ __forceinline__ void mma_held_loading(f32x16 (&acc)[kTM][kTN], const Frags& f1,
+                                                 const TileSrc& src, uint8_t* stage, int k0,
+                                                 int wave)
+{
+    constexpr int kPer = 2 * kDmaLoads / kHeld;           // loads after each held MFMA
+    static_assert(kPer * kHeld == 2 * kDmaLoads, "the loads spread evenly over the held MFMAs");
+#pragma unroll
+    for (int j = 0; j < kHeld; ++j) {
+        const int i = kStep - kHeld + j;
+        acc[i / kTN][i % kTN] =
+            __builtin_amdgcn_mfma_f32_32x32x16_bf16(f1.a[i / kTN], f1.b[i % kTN], acc[i / kTN][i % kTN], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int q = 0; q < kPer; ++q) {
+            const int n = kPer * j + q;
+            const int row = 64 * wave + 8 * (n >> 1);
+            if ((n & 1) == 0)
+                load_lds16(src.x, lds_addr(stage + row * kRowBytes), src.vx[n >> 1], uniform(2 * k0));
+            else
+                load_lds16(src.w, lds_addr(stage + kRegionBytes + row * kRowBytes), src.vw[(n >> 1) & 1],
+                           uniform(row * src.row_w + 2 * k0));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// The K loop of one tile. Slice kb + 1 is loaded straight into the other
+// stage while slice kb is computed; each wave waits for its own loads
+// (vmcnt(0)) and the barrier that follows makes every wave's loads visible
+// and ends all reads of the stage the next loads overwrite. Ends with a
+// barrier after the last slice's reads.
 __device__ __forceinline__ void gemm_tile(const Gemm& g, const TileRef& tr, uint8_t* smem,
                                           f32x16 (&acc)[kTM][kTN], int wave, int wm, int wn,
                                           int lane)
@@ -356,9 +388,34 @@ __device__ __forceinline__ void gemm_tile(const Gemm& g, const TileRef& tr, uint
     load_slice(src, smem, 0, wave);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    for (int kb = 0; kb < last; ++kb)
-        k_pass<true>(src, smem, acc, kb, wave, wm, wn, lane);
-    k_pass<false>(src, smem, acc, last, wave, wm, wn, lane);
+    Frags f0, f1;
+    read_frags(f0, smem, 0, wm, wn, lane);
+    if (last > 0)
+        load_slice(src, smem + kStageBytes, kBK, wave);
+    __builtin_amdgcn_sched_barrier(0);
+    k_pass(smem, acc, f0, f1, wm, wn, lane);
+    // slices 1 .. last - 1, each loading the next
+    for (int kb = 1; kb < last; ++kb) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        const uint8_t* st = smem + (kb & 1) * kStageBytes;
+        read_frags(f0, st, 0, wm, wn, lane);
+        __builtin_amdgcn_sched_barrier(0);
+        mma_held_loading(acc, f1, src, smem + ((kb + 1) & 1) * kStageBytes, (kb + 1) * kBK, wave);
+        k_pass(st, acc, f0, f1, wm, wn, lane);
+    }
+    if (last > 0) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        const uint8_t* st = smem + (last & 1) * kStageBytes;
+        read_frags(f0, st, 0, wm, wn, lane);
+        __builtin_amdgcn_sched_barrier(0);
+        mma_step<kStep - kHeld, kHeld>(acc, f1);
+        __builtin_amdgcn_sched_barrier(0);
+        k_pass(st, acc, f0, f1, wm, wn, lane);
+    }
+    mma_step<kStep - kHeld, kHeld>(acc, f1);
+    __syncthreads();
 }
 
 // Epilogue pass p holds the tile rows of MFMA row tile p of every wave:
