@@ -71,8 +71,11 @@ def gs_rows_of(g, gs, rows=None):
     return r if rows is None else r[rows]
 
 
-# hidden / 64 K slices: 1, 2, 3, 4, 5, 8, 16 and 64 (the K loop runs its
-# slices in pairs, with separate tails for an odd and an even count)
+# hidden / 64 K slices: 1, 2, 3, 4, 5, 8, 16 and 64. The K loop has a first
+# slice, a middle loop (slices 1 .. n - 2, each loading the next) and a last
+# slice, with the last K step's MFMAs of each slice issued after the next
+# barrier: one slice runs the first alone, two the first and the last, three
+# or more all three parts.
 @pytest.mark.parametrize("tokens,hidden,inter,experts,seed", [
     (300, 256, 128, 5, 1), (1000, 512, 384, 9, 2), (257, 64, 128, 1, 3), (513, 1024, 256, 3, 4),
     (256, 4096, 128, 2, 5), (130, 128, 128, 2, 6), (260, 192, 256, 2, 7), (511, 320, 128, 4, 8)])
