@@ -72,7 +72,11 @@ def test_standalone_e2m1_convert_all_half_steps(M):
 
 @pytest.mark.parametrize("rows,cols,ld,seed", [
     (1, 16, 16, 1), (3, 48, 48, 2), (7, 1600, 1600, 3), (64, 4096, 4104, 4),
-    (257, 1040, 1048, 5), (1000, 256, 256, 6)])
+    (257, 1040, 1048, 5), (1000, 256, 256, 6),
+    # 16-byte stores, tiles walked in pairs: an odd tile count (the last
+    # tile closes its pair alone) with pairs that straddle a row break
+    # (144 blocks = 64 + 64 + 16 per row), and 80-block rows with a pitch
+    (5, 2304, 2304, 7), (9, 1280, 1296, 11), (1, 3072, 3072, 12)])
 def test_standalone_shapes_bit_exact(M, rows, cols, ld, seed):
     rng = np.random.default_rng(seed)
     full = W.random_plain(rows, ld, seed, scale=10.0 ** rng.uniform(-3, 3))
@@ -90,6 +94,21 @@ def test_standalone_experts_bit_exact(M):
     x = W.random_plain(rows, cols, 8, scale=3.0)
     off = W.random_offsets(rows, E, seed=9, empty=6)
     gs = (10.0 ** np.random.default_rng(10).uniform(-3, 0, E)).astype(np.float32)
+    say("nvfp4_quantize experts", rows, cols, E)
+    p, s = M.nvfp4_quantize(dev_bf16(x), gs_tensor(gs), dev(off))
+    rp, rs = oracle.quantize_bf16(x, oracle.rows_global_scale(gs, off, rows))
+    P.assert_bytes_equal("scales", host(s), rs)
+    P.assert_bytes_equal("packed", host(p), rp)
+
+
+def test_standalone_experts_long_walk_bit_exact(M):
+    """65536 x 4096 with 64 experts: 262144 tiles, so every wave of the
+    persistent grid walks more than 64 tiles (in pairs) and refills its
+    per-lane expert lookahead more than once."""
+    rows, cols, E = 65536, 4096, 64
+    x = W.random_plain(rows, cols, 13, scale=2.0)
+    off = W.random_offsets(rows, E, seed=14, empty=5)
+    gs = (10.0 ** np.random.default_rng(15).uniform(-3, 1, E)).astype(np.float32)
     say("nvfp4_quantize experts", rows, cols, E)
     p, s = M.nvfp4_quantize(dev_bf16(x), gs_tensor(gs), dev(off))
     rp, rs = oracle.quantize_bf16(x, oracle.rows_global_scale(gs, off, rows))
