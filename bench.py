@@ -411,11 +411,11 @@ def secondary_figures(M, W, x, packed, scales, args, dev):
         rr, ri = w.rows, w.out_cols
         xr = torch.from_numpy(w.x.view(np.int16)).to(dev).view(torch.bfloat16)
         offr = torch.from_numpy(w.offsets).to(dev)
+        ragged = {"shape": [rr, 2 * ri], "experts": 256, "input_sha256": W.sha256(w.x)}
         del w
         gsr = torch.empty(256, dtype=torch.float32, device=dev)
         pr = torch.empty((rr, ri // 2), dtype=torch.uint8, device=dev)
         sr = torch.empty((rr, ri // 16), dtype=torch.uint8, device=dev)
-        ragged = {"shape": [rr, 2 * ri], "experts": 256}
         ragged["global_scale"] = measure(
             "ragged swiglu_nvfp4_global_scale",
             lambda: M.swiglu_nvfp4_global_scale(xr, offr, gs=gsr), rr * ri * 4.0, rr * ri, st, ms)
@@ -438,6 +438,7 @@ def secondary_figures(M, W, x, packed, scales, args, dev):
         w = W.decode()
         dr, di = w.rows, w.out_cols
         base = torch.from_numpy(w.x.view(np.int16)).to(dev).view(torch.bfloat16)
+        decode_sha = W.sha256(w.x)
         del w
         sets = [(base.clone(), torch.empty((dr, di // 2), dtype=torch.uint8, device=dev),
                  torch.empty((dr, di // 16), dtype=torch.uint8, device=dev)) for _ in range(8)]
@@ -450,7 +451,8 @@ def secondary_figures(M, W, x, packed, scales, args, dev):
             M.swiglu_nvfp4_quantize(xi, packed=pi, scales=si)
         sec["decode_shaped"] = measure(
             "decode-shaped swiglu_nvfp4_quantize", rotating, dr * di * BYTES_PER_ELEM, dr * di,
-            max(st, 80), ms, {"shape": [dr, 2 * di], "note": "8 rotating input/output sets"})
+            max(st, 80), ms, {"shape": [dr, 2 * di], "note": "8 rotating input/output sets",
+                              "input_sha256": decode_sha})
         del sets
     if "small" in want:
         # the two small shapes: 128 x 256 standalone (84 KB moved) and
@@ -461,11 +463,11 @@ def secondary_figures(M, W, x, packed, scales, args, dev):
         xs = torch.from_numpy(w.x.view(np.int16)).to(dev).view(torch.bfloat16)
         ps = torch.empty((w.rows, w.out_cols // 2), dtype=torch.uint8, device=dev)
         ss = torch.empty((w.rows, w.out_cols // 16), dtype=torch.uint8, device=dev)
-        def small(name, fn, nbytes, elems, shape):
+        def small(name, fn, nbytes, elems, shape, sha):
             r = measure(name, fn, nbytes, elems, max(st, 200), ms,
                         {"shape": shape, "note": "cache-resident, launch-bound; ms is the eager "
                          "launch rate through the Python binding, graph_ms the device time per "
-                         "launch inside a HIP graph of 50 launches"})
+                         "launch inside a HIP graph of 50 launches", "input_sha256": sha})
             gm = graph_ms(fn)
             r["graph_ms"] = round(gm, 5)
             r["graph_elements_per_s"] = round(elems / gm * 1e3, 1)
@@ -473,7 +475,8 @@ def secondary_figures(M, W, x, packed, scales, args, dev):
             return r
         sec["small_standalone"] = small(
             "standalone 128x256 nvfp4_quantize", lambda: M.nvfp4_quantize(xs, packed=ps, scales=ss),
-            w.rows * w.out_cols * 2.5625, w.rows * w.out_cols, [w.rows, w.out_cols])
+            w.rows * w.out_cols * 2.5625, w.rows * w.out_cols, [w.rows, w.out_cols],
+            W.sha256(w.x))
         w = W.fused_small()
         xf = torch.from_numpy(w.x.view(np.int16)).to(dev).view(torch.bfloat16)
         pf = torch.empty((w.rows, w.out_cols // 2), dtype=torch.uint8, device=dev)
@@ -481,7 +484,8 @@ def secondary_figures(M, W, x, packed, scales, args, dev):
         sec["small_fused"] = small(
             "fused 512x4096 swiglu_nvfp4_quantize",
             lambda: M.swiglu_nvfp4_quantize(xf, packed=pf, scales=sf),
-            w.rows * w.out_cols * BYTES_PER_ELEM, w.rows * w.out_cols, [w.rows, 2 * w.out_cols])
+            w.rows * w.out_cols * BYTES_PER_ELEM, w.rows * w.out_cols, [w.rows, 2 * w.out_cols],
+            W.sha256(w.x))
         del xs, ps, ss, xf, pf, sf
     if "kv" in want:
         # paged KV-cache write and read: 65536 tokens x 8 heads x 128 into a
