@@ -399,16 +399,35 @@ struct ExpertBatch {
     }
 };
 
-// Fills the workgroup's sigmoid table (fused input only). Every wave of the
-// workgroup takes part, so all of them reach the barrier.
+// sigma(g) = 1 / (1 + e^-g), correctly rounded to binary32 (bit patterns),
+// for the table's gates: positive magnitudes m = 0 .. kSigSpan - 1, then the
+// negative ones (generated by gen_sigma_table.py with 60-digit arithmetic).
+__device__ const uint32_t kSigmaBits[] __attribute__((aligned(16))) = {
+#include "sigma_table.inc"
+};
+static_assert(sizeof(kSigmaBits) == 2 * nvfp4::kSigSpan * 4, "one entry per gate");
+
+// Fills the workgroup's sigmoid table in LDS (fused input only) from
+// kSigmaBits: 32 KB, four 16-byte loads per thread, served by L2 after the
+// first workgroups. Every wave of the workgroup takes part, so all of them
+// reach the barrier.
 template <class Block>
 __device__ __forceinline__ void fill_sigma_table(float* sig)
 {
     if constexpr (Block::kSigmaTable) {
-        for (int i = threadIdx.x; i < 2 * nvfp4::kSigSpan; i += Block::kWaves * kWave) {
-            const int m = i & (nvfp4::kSigSpan - 1);
-            const bool neg = i >= nvfp4::kSigSpan;
-            sig[m + (neg ? nvfp4::kSigNeg : 0)] = nvfp4::sigma_entry(m, neg);
+        constexpr int kThreadsPerBlock = Block::kWaves * kWave;
+        constexpr int kWords = 2 * nvfp4::kSigSpan / 4;   // 16-byte words
+        static_assert(kWords % kThreadsPerBlock == 0, "whole words per thread");
+        const u32x4* src = reinterpret_cast<const u32x4*>(kSigmaBits);
+        u32x4 v[kWords / kThreadsPerBlock];
+#pragma unroll
+        for (int k = 0; k < kWords / kThreadsPerBlock; ++k)
+            v[k] = src[k * kThreadsPerBlock + threadIdx.x];
+#pragma unroll
+        for (int k = 0; k < kWords / kThreadsPerBlock; ++k) {
+            const int f = (k * kThreadsPerBlock + (int)threadIdx.x) * 4;   // first entry
+            const int at = f < nvfp4::kSigSpan ? f : f - nvfp4::kSigSpan + nvfp4::kSigNeg;
+            *reinterpret_cast<u32x4*>(sig + at) = v[k];
         }
     }
 }
@@ -424,7 +443,7 @@ __global__ __launch_bounds__(Block::kWaves * kWave) void quantize_tiles_kernel(
     constexpr int G = kWide ? Block::kScaleGroup : 1;
     __shared__ u32x4 stage[kWaves][kStageSlots(Block::P)];
     __shared__ u32x4 win[kWaves][4 * G];
-    __shared__ float sig[Block::kSigmaTable ? nvfp4::kSigFloats : 1];
+    __shared__ __attribute__((aligned(16))) float sig[Block::kSigmaTable ? nvfp4::kSigFloats : 1];
     __shared__ ExpertTable tab;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = uniform(threadIdx.x / kWave);
@@ -539,7 +558,7 @@ __global__ __launch_bounds__(FusedBlock::kWaves * kWave) void swiglu_bf16_kernel
     using Block = FusedBlock;
     constexpr int kWaves = Block::kWaves;
     __shared__ u32x4 stage[kWaves][kStageSlots(Block::P)];
-    __shared__ float sig[nvfp4::kSigFloats];
+    __shared__ __attribute__((aligned(16))) float sig[nvfp4::kSigFloats];
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = uniform(threadIdx.x / kWave);
     u32x4* lds = stage[wave];
@@ -610,7 +629,7 @@ __global__ __launch_bounds__(Block::kWaves * kWave) void amax_tiles_kernel(
     constexpr int kWaves = Block::kWaves;
     static_assert(kMaxScaleGroups <= kLdsExperts, "experts of a global-scale call fit in LDS");
     __shared__ u32x4 stage[kWaves][kStageSlots(Block::P)];
-    __shared__ float sig[Block::kSigmaTable ? nvfp4::kSigFloats : 1];
+    __shared__ __attribute__((aligned(16))) float sig[Block::kSigmaTable ? nvfp4::kSigFloats : 1];
     __shared__ uint32_t part[kMaxScaleGroups];
     __shared__ ExpertTable tab;
     const int lane = threadIdx.x & (kWave - 1);

@@ -49,29 +49,15 @@ __device__ __forceinline__ float swiglu_bf16(float g, float u)
 // stands (the floats in between are unused). Magnitudes below the range read
 // the first entry (sigma rounds to 1/2 there: |sigma - 1/2| < 2^-26),
 // magnitudes above it the last (sigma is 1, or below the FP32 range for
-// negative g). Entries are computed once per workgroup with sigma_entry(); a
-// lookup then replaces exp and rcp per element.
+// negative g). The entries are sigma correctly rounded to binary32, computed
+// at build time (gen_sigma_table.py) and copied into LDS once per
+// workgroup; a lookup then replaces exp and rcp per element.
 constexpr uint32_t kSigLo = 103u << 7;
 constexpr uint32_t kSigHi = (134u << 7) | 127u;
 constexpr int kSigSpan = (int)(kSigHi - kSigLo + 1);   // 4096
 constexpr int kSigNeg = 8192;
 constexpr int kSigFloats = kSigNeg + kSigSpan;         // 12288 (48 KB, 16 KB unused)
 static_assert(kSigNeg * 4 == 0x8000 && kSigSpan * 4 <= 0x8000, "sign bit is the offset");
-
-// sigma(g) for magnitude index m (g's 15 magnitude bits less kSigLo) and
-// sign neg: the exp2 argument -g * kLog2eHi is exact for a BF16 gate, its
-// tail is folded in by one fma, and the final reciprocal is a correctly
-// rounded division (about 2 ulp overall).
-__device__ __forceinline__ float sigma_entry(int m, bool neg)
-{
-    const float kLog2eHi = 0x1.7154p+0f;          // log2 e to 16 bits
-    const float kLog2eLoLn2 = 0x1.480fb6p-18f;    // (log2 e - kLog2eHi) ln 2
-    const float a = __uint_as_float((kSigLo + (uint32_t)m) << 16);
-    const float g = neg ? -a : a;
-    const float e = __builtin_amdgcn_exp2f(-g * kLog2eHi);
-    const float c = __builtin_fmaf(-g, kLog2eLoLn2, 1.0f);
-    return 1.0f / __builtin_fmaf(e, c, 1.0f);
-}
 
 // Byte offsets of the table entries for the two BF16 gates of w, in the
 // matching halves of the result. Both halves are done at once in packed

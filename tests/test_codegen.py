@@ -42,10 +42,11 @@ def isa(tmp_path_factory):
 
 def _kernels(text):
     lines = text.split("\n")
+    funcs = set(re.findall(r"\.type\s+(_Z\w+),@function", text))   # not data symbols
     out = {}
     for k, l in enumerate(lines):
         m = re.match(r"^(_Z\w+):", l)
-        if m:
+        if m and m.group(1) in funcs:
             end = next(j for j in range(k, len(lines)) if lines[j].strip().startswith(".Lfunc_end"))
             out[m.group(1)] = [x.strip() for x in lines[k + 1:end]
                                if x.startswith("\t") or re.match(r"^\.LBB\w+:", x)]
