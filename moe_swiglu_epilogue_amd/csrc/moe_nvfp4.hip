@@ -222,7 +222,7 @@ struct FusedBlock {
     // the prefill shape, 12 or 16 waves per CU are 4-6% slower and 4 waves
     // per CU 25% slower.
     static constexpr int kWaves = 8;
-    static constexpr int kBlocksPerCU = 1;   // 48 KB sigma table + 8 x 4.25 KB staging
+    static constexpr int kBlocksPerCU = 1;   // 64 KB sigma table + 8 x 4.25 KB staging
     static constexpr bool kSigmaTable = true;
     // Consecutive tiles per wave with wide stores (their scale bytes leave
     // as one piece). Measured on the prefill shape: 2 and 4 are 1.5-1.7%
@@ -241,10 +241,10 @@ struct FusedBlock {
             // keep o whole: one shift-or builds it, then one mask and one
             // shift split it (the compiler would otherwise rebuild each half)
             asm("" : "+v"(o));
-            const float s0 = *reinterpret_cast<const float*>(sig + (o & 0xffffu));
-            const float s1 = *reinterpret_cast<const float*>(sig + (o >> 16));
-            y[2 * i] = (nvfp4::bf16_lo(gw[i]) * nvfp4::bf16_lo(uw[i])) * s0;
-            y[2 * i + 1] = (nvfp4::bf16_hi(gw[i]) * nvfp4::bf16_hi(uw[i])) * s1;
+            const float2 s0 = *reinterpret_cast<const float2*>(sig + (o & 0xffffu));
+            const float2 s1 = *reinterpret_cast<const float2*>(sig + (o >> 16));
+            y[2 * i] = nvfp4::times_sigma(nvfp4::bf16_lo(gw[i]) * nvfp4::bf16_lo(uw[i]), s0);
+            y[2 * i + 1] = nvfp4::times_sigma(nvfp4::bf16_hi(gw[i]) * nvfp4::bf16_hi(uw[i]), s1);
         }
     }
 };
@@ -399,16 +399,17 @@ struct ExpertBatch {
     }
 };
 
-// sigma(g) = 1 / (1 + e^-g), correctly rounded to binary32 (bit patterns),
-// for the table's gates: positive magnitudes m = 0 .. kSigSpan - 1, then the
-// negative ones (generated by gen_sigma_table.py with 60-digit arithmetic).
+// sigma(g) = 1 / (1 + e^-g) as binary32 pairs {RZ(sigma), RN(sigma - hi)}
+// (bit patterns) for the table's gates: positive magnitudes m = 0 ..
+// kSigSpan - 1, then the negative ones (generated by gen_sigma_table.py with
+// 150-digit arithmetic). The LDS table is a plain copy of it.
 __device__ const uint32_t kSigmaBits[] __attribute__((aligned(16))) = {
 #include "sigma_table.inc"
 };
-static_assert(sizeof(kSigmaBits) == 2 * nvfp4::kSigSpan * 4, "one entry per gate");
+static_assert(sizeof(kSigmaBits) == nvfp4::kSigFloats * 4, "one pair per gate");
 
 // Fills the workgroup's sigmoid table in LDS (fused input only) from
-// kSigmaBits: 32 KB, four 16-byte loads per thread, served by L2 after the
+// kSigmaBits: 64 KB, eight 16-byte loads per thread, served by L2 after the
 // first workgroups. Every wave of the workgroup takes part, so all of them
 // reach the barrier.
 template <class Block>
@@ -416,19 +417,17 @@ __device__ __forceinline__ void fill_sigma_table(float* sig)
 {
     if constexpr (Block::kSigmaTable) {
         constexpr int kThreadsPerBlock = Block::kWaves * kWave;
-        constexpr int kWords = 2 * nvfp4::kSigSpan / 4;   // 16-byte words
+        constexpr int kWords = nvfp4::kSigFloats / 4;   // 16-byte words
         static_assert(kWords % kThreadsPerBlock == 0, "whole words per thread");
         const u32x4* src = reinterpret_cast<const u32x4*>(kSigmaBits);
+        u32x4* dst = reinterpret_cast<u32x4*>(sig);
         u32x4 v[kWords / kThreadsPerBlock];
 #pragma unroll
         for (int k = 0; k < kWords / kThreadsPerBlock; ++k)
             v[k] = src[k * kThreadsPerBlock + threadIdx.x];
 #pragma unroll
-        for (int k = 0; k < kWords / kThreadsPerBlock; ++k) {
-            const int f = (k * kThreadsPerBlock + (int)threadIdx.x) * 4;   // first entry
-            const int at = f < nvfp4::kSigSpan ? f : f - nvfp4::kSigSpan + nvfp4::kSigNeg;
-            *reinterpret_cast<u32x4*>(sig + at) = v[k];
-        }
+        for (int k = 0; k < kWords / kThreadsPerBlock; ++k)
+            dst[k * kThreadsPerBlock + threadIdx.x] = v[k];
     }
 }
 

@@ -43,27 +43,26 @@ __device__ __forceinline__ float swiglu_bf16(float g, float u)
 // A BF16 gate has 65536 values; sigma(g) = 1 / (1 + e^-g) only varies in FP32
 // for 2^-24 <= |g| < 256. The table holds sigma for every BF16 magnitude in
 // that range (exponent field 103..134, all 128 mantissas: kSigSpan values)
-// and both signs. Positive gates use floats [0, kSigSpan), negative ones
-// [kSigNeg, kSigNeg + kSigSpan): kSigNeg * 4 = 32768 is bit 15 of a BF16
-// half-word, so the sign bit serves as the sign's byte offset where it
-// stands (the floats in between are unused). Magnitudes below the range read
-// the first entry (sigma rounds to 1/2 there: |sigma - 1/2| < 2^-26),
-// magnitudes above it the last (sigma is 1, or below the FP32 range for
-// negative g). The entries are sigma correctly rounded to binary32, computed
-// at build time (gen_sigma_table.py) and copied into LDS once per
-// workgroup; a lookup then replaces exp and rcp per element.
+// and both signs, each entry a pair of floats hi = sigma rounded toward zero,
+// lo = RN(sigma - hi) >= 0 (8 bytes; hi + lo carries sigma to about 2^-47). Positive
+// gates use entries [0, kSigSpan), negative ones [kSigSpan, 2 kSigSpan):
+// kSigSpan * 8 = 32768 is bit 15 of a BF16 half-word, so the sign bit serves
+// as the sign's byte offset where it stands. Magnitudes below the range read
+// the first entry (sigma = 1/2 +- 2^-26 +- ... there), magnitudes above it the
+// last (sigma is 1 to within 2^-367, or below 2^-367 for negative g). The
+// entries are computed at build time (gen_sigma_table.py) and copied into
+// LDS once per workgroup; a lookup then replaces exp and rcp per element.
 constexpr uint32_t kSigLo = 103u << 7;
 constexpr uint32_t kSigHi = (134u << 7) | 127u;
 constexpr int kSigSpan = (int)(kSigHi - kSigLo + 1);   // 4096
-constexpr int kSigNeg = 8192;
-constexpr int kSigFloats = kSigNeg + kSigSpan;         // 12288 (48 KB, 16 KB unused)
-static_assert(kSigNeg * 4 == 0x8000 && kSigSpan * 4 <= 0x8000, "sign bit is the offset");
+constexpr int kSigFloats = 4 * kSigSpan;                // 16384 (64 KB)
+static_assert(kSigSpan * 8 == 0x8000, "sign bit is the offset of the negative half");
 
 // Byte offsets of the table entries for the two BF16 gates of w, in the
 // matching halves of the result. Both halves are done at once in packed
 // 16-bit arithmetic: magnitude bits less kSigLo saturating at 0
-// (v_pk_sub_u16 with clamp), capped at kSigSpan - 1 (v_pk_min_u16), times 4
-// (at most 14 bits, so one 32-bit shift cannot carry across halves), and the
+// (v_pk_sub_u16 with clamp), capped at kSigSpan - 1 (v_pk_min_u16), times 8
+// (at most 15 bits, so one 32-bit shift cannot carry across halves), and the
 // sign bits kept in place.
 __device__ __forceinline__ uint32_t sigma_offsets(uint32_t w)
 {
@@ -72,7 +71,19 @@ __device__ __forceinline__ uint32_t sigma_offsets(uint32_t w)
     const u16x2 top = {(unsigned short)(kSigSpan - 1), (unsigned short)(kSigSpan - 1)};
     u16x2 m = __builtin_bit_cast(u16x2, w & 0x7fff7fffu);
     m = __builtin_elementwise_min(__builtin_elementwise_sub_sat(m, lo), top);
-    return (__builtin_bit_cast(uint32_t, m) << 2) | (w & 0x80008000u);
+    return (__builtin_bit_cast(uint32_t, m) << 3) | (w & 0x80008000u);
+}
+
+// (g u) sigma for a table entry {hi, lo}: g u is exact in FP32 for BF16 g and
+// u (8 significant bits each); fma adds (g u) hi and RN((g u) lo) exactly and
+// rounds once, so the result is RN((g u) sigma) unless (g u) sigma lies
+// within about 2^-46 (relative) of a rounding midpoint. hi and lo are both
+// >= 0, so both terms carry the sign of g u: g u = -0 gives -0, and a g u
+// that overflowed to +-inf gives +-inf (a negative lo would add -0 to -0
+// as +0, or make inf - inf).
+__device__ __forceinline__ float times_sigma(float gu, float2 s)
+{
+    return __builtin_fmaf(gu, s.x, gu * s.y);
 }
 
 // ---- FP8 E4M3 ("fn") encode of a non-negative block scale -------------------

@@ -1,10 +1,12 @@
 """The sigmoid table of the fused SwiGLU kernels (csrc/sigma_table.inc): it is
-what its generator writes, and its values are sigma(g) = 1 / (1 + e^-g)
-correctly rounded to binary32, checked against float64 arithmetic and
-against the function's exact properties. CPU only."""
+what its generator writes, and each entry is the pair hi = RZ(sigma) (toward
+zero), lo = RN(sigma - hi) >= 0 of binary32 values for sigma(g) = 1 / (1 + e^-g),
+checked against float64 arithmetic, against the exact Taylor series of the
+sigmoid near 0 and against its exact properties. CPU only."""
 import importlib.util
 import os
 import struct
+from fractions import Fraction
 
 import numpy as np
 
@@ -21,18 +23,47 @@ def _gen():
 
 
 def _table():
+    """(hi, lo) float32 arrays of 8192 entries: g > 0, then g < 0."""
     bits = []
     with open(os.path.join(CSRC, "sigma_table.inc")) as f:
         for line in f:
             if line.startswith("0x"):
                 bits += [int(t.rstrip("u,"), 16) for t in line.split()]
-    return np.array(bits, np.uint32)
+    t = np.array(bits, np.uint32).view(np.float32)
+    assert t.size == 2 * 8192
+    return t[0::2], t[1::2]
 
 
 def _gates():
     a = ((((103 << 7) + np.arange(4096)).astype(np.uint32)) << 16).view(np.float32)
     a = a.astype(np.float64)
     return np.concatenate([a, -a])
+
+
+def _nearest_binary32(q):
+    """The binary32 nearest to the rational q, and the distance from q to the
+    nearest binary32 rounding midpoint."""
+    if q < 0:
+        b, m = _nearest_binary32(-q)
+        return -b, m
+    c = np.float32(float(q))
+    cands = [c, np.nextafter(c, np.float32(np.inf)), np.nextafter(c, np.float32(0))]
+    best = min(cands, key=lambda x: abs(Fraction(float(x)) - q))
+    mids = [(Fraction(float(best)) + Fraction(float(n))) / 2
+            for n in (np.nextafter(best, np.float32(np.inf)), np.nextafter(best, np.float32(0)))]
+    return best, min(abs(q - m) for m in mids)
+
+
+def _truncate_binary32(q):
+    """The largest binary32 not above the rational q >= 0, and the distance
+    from q to the nearest binary32 value."""
+    c = np.float32(float(q))
+    while Fraction(float(c)) > q:
+        c = np.nextafter(c, np.float32(0))
+    while Fraction(float(np.nextafter(c, np.float32(np.inf)))) <= q:
+        c = np.nextafter(c, np.float32(np.inf))
+    up = np.nextafter(c, np.float32(np.inf))
+    return c, min(q - Fraction(float(c)), Fraction(float(up)) - q)
 
 
 def test_committed_table_is_the_generators_output():
@@ -42,73 +73,44 @@ def test_committed_table_is_the_generators_output():
 
 
 def test_table_against_float64():
-    """Within 1 ulp of the float64 sigmoid everywhere, and equal to its
-    rounding wherever the float64 value lies clear of a binary32 midpoint
-    (float64's own error is below 1e-15 relative)."""
-    t = _table()
-    assert t.size == 8192
+    """hi is the float64 sigmoid truncated to binary32 wherever the float64
+    value lies clear of a binary32 value (float64's own error is below 1e-15
+    relative), and within 1 ulp of it everywhere; hi + lo agrees with the
+    float64 value to within 2^-47."""
+    hi, lo = _table()
     g = _gates()
     with np.errstate(over="ignore"):
         s64 = 1.0 / (1.0 + np.exp(-g))
-    ref = s64.astype(np.float32)
-    tf = t.view(np.float32)
-    d = t.view(np.int32).astype(np.int64) - ref.view(np.int32).astype(np.int64)
+    near = s64.astype(np.float32)
+    below = np.where(near.astype(np.float64) <= s64, near, np.nextafter(near, np.float32(0)))
+    above = np.nextafter(below, np.float32(np.inf))
+    d = hi.view(np.int32).astype(np.int64) - below.view(np.int32).astype(np.int64)
     assert np.abs(d).max() <= 1
-    # distance of the float64 value from the nearest binary32 midpoint
-    lo = np.where(ref.astype(np.float64) <= s64, ref, np.nextafter(ref, np.float32(0)))
-    hi = np.nextafter(lo, np.float32(np.inf))
-    mid = (lo.astype(np.float64) + hi.astype(np.float64)) / 2
-    clear = np.abs(s64 - mid) > 1e-14 * s64
-    # the rest (256) are small gates, where sigma = 1/2 + g/4 - g^3/48 + ...
-    # sits next to a midpoint by construction; the 1-ulp bound covers them
-    assert clear.sum() >= 7900
-    assert np.array_equal(tf[clear], ref[clear])
-
-
-def test_table_exact_properties():
-    tf = _table().view(np.float32).astype(np.float64)
-    pos, neg = tf[:4096], tf[4096:]
-    # the smallest magnitude, 2^-24: sigma = 1/2 +- 2^-26 rounds to 1/2 on both sides
-    assert pos[0] == 0.5 and neg[0] == 0.5
-    # monotone: increasing in g
-    assert np.all(np.diff(pos) >= 0) and np.all(np.diff(neg) <= 0)
-    assert np.all(pos >= 0.5) and np.all(neg <= 0.5) and np.all(neg >= 0)
-    # sigma(g) + sigma(-g) = 1, up to the two roundings
-    ulp = np.spacing(pos.astype(np.float32)).astype(np.float64)
-    assert np.all(np.abs(pos + neg - 1.0) <= ulp)
-    # the largest magnitudes: sigma(+255) rounds to 1, sigma(-255) (about 1.8e-111) to 0
-    assert pos[-1] == 1.0 and neg[-1] == 0.0
-    # subnormal binary32 results for g in (-103.3, -87.3), zero below
-    g = _gates()[4096:]
-    sub = neg[(neg > 0) & (neg < 2.0 ** -126)]
-    assert sub.size > 0
-    assert np.all(neg[g < -104.0] == 0.0)
-    # sigma(1) = 1 / (1 + 1/e): 0.7310585786300049 -> binary32 0x3f3b26a8
-    one = (127 - 103) * 128
-    assert struct.pack("<f", np.float32(pos[one])) == struct.pack("<I", 0x3f3b26a8)
-
-
-def _nearest_binary32(q):
-    """The binary32 nearest to the rational q (> 0), and the distance from q
-    to the nearest binary32 midpoint."""
-    from fractions import Fraction
-    c = np.float32(float(q))
-    cands = [c, np.nextafter(c, np.float32(np.inf)), np.nextafter(c, np.float32(0))]
-    best = min(cands, key=lambda x: abs(Fraction(float(x)) - q))
-    mids = [(Fraction(float(best)) + Fraction(float(n))) / 2
-            for n in (np.nextafter(best, np.float32(np.inf)), np.nextafter(best, np.float32(0)))]
-    return best, min(abs(q - m) for m in mids)
+    clear = (np.minimum(s64 - below.astype(np.float64), above.astype(np.float64) - s64)
+             > 1e-14 * s64)
+    # the rest are small gates, where sigma = 1/2 + g/4 - g^3/48 + ... sits
+    # next to a binary32 value by construction (the series test pins them),
+    # and gates above about 33, where sigma is within 1e-14 of 1 (pinned below)
+    assert clear.sum() >= 7100
+    assert np.array_equal(hi[clear], below[clear])
+    # the pair: |hi + lo - sigma| <= 2^-48 sigma (lo rounded to 24 bits, lo
+    # below 2^-23 sigma) plus float64's error, plus one binary32 subnormal
+    # step where lo (for sigma below about 1e-29) reaches the bottom of the range
+    pair = hi.astype(np.float64) + lo.astype(np.float64)
+    assert np.all(np.abs(pair - s64) <= 2.0 ** -47 * s64 + 2.0 ** -149)
+    # lo is the remainder: non-negative and below one ulp of hi
+    assert np.all(lo >= 0) and not np.any(np.signbit(lo))
+    assert np.all(lo.astype(np.float64) <= np.spacing(hi).astype(np.float64))
 
 
 def test_small_gates_exact_by_series():
     """For |g| <= 2^-6, sigma(g) = 1/2 + tanh(g/2)/2 = 1/2 + g/4 - g^3/48
     + g^5/480 - 17 g^7/80640 + 31 g^9/1451520 - ..., an alternating series
     whose remainder is below 2.2e-6 |g|^11. Summed exactly in rationals, it
-    fixes the correctly rounded binary32 of every such entry (including the
-    ones next to a midpoint, where float64 cannot decide), independently of
-    the generator's decimal arithmetic."""
-    from fractions import Fraction
-    t = _table().view(np.float32)
+    fixes both halves of every such entry (including the hi values next to a
+    midpoint, where float64 cannot decide), independently of the
+    generator's decimal arithmetic."""
+    hi, lo = _table()
     g = _gates()
     coef = [(1, Fraction(1, 4)), (3, Fraction(-1, 48)), (5, Fraction(1, 480)),
             (7, Fraction(-17, 80640)), (9, Fraction(31, 1451520))]
@@ -117,8 +119,56 @@ def test_small_gates_exact_by_series():
         x = Fraction(float(g[i]))
         q = Fraction(1, 2) + sum(c * x ** k for k, c in coef)
         bound = Fraction(22, 10 ** 7) * abs(x) ** 11
-        best, margin = _nearest_binary32(q)
-        assert margin > bound, i                      # the series decides the rounding
-        assert t[i] == best, (i, float(g[i]), t[i], best)
+        want_hi, margin = _truncate_binary32(q)
+        assert margin > bound, i                      # the series decides the truncation
+        assert hi[i] == want_hi, (i, float(g[i]), hi[i], want_hi)
+        want_lo, margin = _nearest_binary32(q - Fraction(float(want_hi)))
+        assert margin > bound, i
+        assert lo[i] == want_lo, (i, float(g[i]), lo[i], want_lo)
         checked += 1
     assert checked == 2 * (18 * 128 + 1)   # exponents 103..120 and 2^-6, both signs
+
+
+def test_table_exact_properties():
+    hi, lo = _table()
+    h = hi.astype(np.float64)
+    pos, neg = h[:4096], h[4096:]
+    # the smallest magnitude, 2^-24: sigma = 1/2 +- 2^-26 + O(2^-75) truncates
+    # to 1/2 and to 1/2 - 2^-25, and lo carries the 2^-26 on both sides
+    assert pos[0] == 0.5 and neg[0] == 0.5 - 2.0 ** -25
+    assert lo[0] == np.float32(2.0 ** -26) and lo[4096] == np.float32(2.0 ** -26)
+    # monotone: increasing in g
+    assert np.all(np.diff(pos) >= 0) and np.all(np.diff(neg) <= 0)
+    assert np.all(pos >= 0.5) and np.all(neg < 0.5) and np.all(neg >= 0)
+    # sigma(g) + sigma(-g) = 1: to the pairs' accuracy, in exact arithmetic
+    for i in range(0, 4096, 37):
+        s = (Fraction(float(hi[i])) + Fraction(float(lo[i])) + Fraction(float(hi[4096 + i]))
+             + Fraction(float(lo[4096 + i])))
+        assert abs(s - 1) <= Fraction(1, 2 ** 46), i
+    # the largest magnitudes: sigma(+255) = 1 - 1.8e-111 is 1 - 2^-24 plus lo =
+    # 2^-24; sigma(-255) (about 1.8e-111) is 0 in both halves
+    assert pos[-1] == 1.0 - 2.0 ** -24 and lo[4095] == np.float32(2.0 ** -24)
+    assert neg[-1] == 0.0 and lo[8191] == 0.0
+    # subnormal binary32 hi for g in (-103.3, -87.3), zero below
+    g = _gates()[4096:]
+    assert np.any((neg > 0) & (neg < 2.0 ** -126))
+    assert np.all(neg[g < -104.0] == 0.0)
+    # sigma(1) = 1 / (1 + 1/e) = 0.7310585786300049, between the binary32
+    # values 0x3f3b26a7 and 0x3f3b26a8: truncated, 0x3f3b26a7
+    one = (127 - 103) * 128
+    assert struct.pack("<f", np.float32(pos[one])) == struct.pack("<I", 0x3f3b26a7)
+
+
+def test_large_gates():
+    """For g >= 18, 1 - sigma(g) = e^-g / (1 + e^-g) < 2^-25, so sigma
+    truncates to 1 - 2^-24 and lo = RN(2^-24 - e^-g / (1 + e^-g)), which
+    float64 fixes (its error is below 1e-23 absolute, far inside lo's
+    rounding steps of at least 2^-48 here); above g = 40, lo = 2^-24."""
+    hi, lo = _table()
+    g = _gates()[:4096]
+    big = g >= 18.0
+    assert np.all(hi[:4096][big] == np.float32(1.0 - 2.0 ** -24))
+    t = np.exp(-g[big])
+    want = (2.0 ** -24 - t / (1.0 + t)).astype(np.float32)
+    assert np.array_equal(lo[:4096][big], want)
+    assert np.all(lo[:4096][g > 40.0] == np.float32(2.0 ** -24))
