@@ -115,7 +115,11 @@ nvfp4_status_t nvfp4_quantize(const uint16_t *x, int64_t rows, int64_t cols,
  * (pitch ld_in), computes y = silu(gate) * up in FP32 and writes
  * packed[rows][inter/2], scales[rows][inter/16] and, when swiglu_out is not
  * NULL, the FP32 y values [rows][inter] (a debug output: the quantized bytes
- * are the same with or without it).
+ * are the same with or without it). Each y is the binary32 rounding of the
+ * exact gate * up * sigmoid(gate), except where that value lies within about
+ * 2^-46 (relative) of a rounding midpoint, where it may be the neighbouring
+ * binary32 value, and except for |gate| < 2^-24, where sigmoid(+-2^-24)
+ * stands for sigmoid(gate) (less than 2^-26 away).
  */
 nvfp4_status_t swiglu_nvfp4_quantize(const uint16_t *gate_up, int64_t rows,
                                      int64_t inter, int64_t ld_in,
