@@ -12,7 +12,9 @@ Prints ONE JSON line with the throughput (HBM GB/s over the algorithmic bytes,
 oracle's throughput on the host cores, and secondary figures: the standalone
 quantize, the dequantize and the global-scale pre-pass on the same tensor;
 the two-pass ablation (compact BF16 SwiGLU, then the standalone quantize);
-in-repo read / copy kernels over the same input as HBM ceilings; the ragged
+in-repo read / copy kernels over the same input as HBM ceilings, and a kernel
+that moves the fused kernel's exact traffic mix (4 KB read, 576 B written
+per wave tile) without its compute; the ragged
 256-expert workload (pre-pass, quantize with per-expert scales, dequantize);
 the decode-shaped workload over 8 rotating buffer sets; the paged KV-cache
 write and read (65536 tokens x 8 heads x 128, 131072 slots); the two small
@@ -47,8 +49,11 @@ PMC_SUMMARY = os.path.join(ROOT, "profiles", "fused_quantize_kernel_prefill_pmc.
 # persistent grid of 6 workgroups per CU, the copy with one 4 KB tile per wave)
 CALIB_READ_BLOCKS = (1024, 1536, 8192, 49152)
 CALIB_COPY_BLOCKS = (512, 8192, 49152)
+# unused dynamic LDS per 256-thread workgroup of the traffic-mix kernel (caps
+# the waves per CU: all that fit, 16, 12)
+CALIB_MIX_LDS = (0, 40960, 53248)
 SECONDARY = ("nvfp4_quantize", "nvfp4_dequantize", "global_scale", "two_pass", "calib_read",
-             "calib_copy", "ragged", "decode", "small", "kv", "gemm")
+             "calib_copy", "calib_mix", "ragged", "decode", "small", "kv", "gemm")
 PEAK_BF16_TFLOPS = 2500.0           # MI355X dense BF16 matrix peak
 
 
@@ -58,7 +63,7 @@ def load_calib():
     if not os.path.exists(build.CALIB_LIB):
         raise RuntimeError("libnvfp4_calib.so is not built; run python -m moe_swiglu_epilogue_amd.build")
     lib = C.CDLL(build.CALIB_LIB)
-    for fn in (lib.nvfp4_calib_copy, lib.nvfp4_calib_read):
+    for fn in (lib.nvfp4_calib_copy, lib.nvfp4_calib_read, lib.nvfp4_calib_mix):
         fn.argtypes = [C.c_void_p, C.c_void_p, C.c_int64, C.c_int32, C.c_void_p]
         fn.restype = C.c_int
     return lib
@@ -378,7 +383,7 @@ def secondary_figures(M, W, x, packed, scales, args, dev):
     # in-repo calibration kernels over the same 805 MB input: HBM ceilings
     nbytes = x.numel() * 2
     stream = torch.cuda.current_stream().cuda_stream
-    if "calib_read" in want or "calib_copy" in want:
+    if "calib_read" in want or "calib_copy" in want or "calib_mix" in want:
         calib = load_calib()
     if "calib_read" in want:
         scratch = torch.empty(max(CALIB_READ_BLOCKS) * 16, dtype=torch.uint8, device=dev)
@@ -402,6 +407,18 @@ def secondary_figures(M, W, x, packed, scales, args, dev):
             best = r if best is None or r["GB_s"] > best["GB_s"] else best
         sec["calib_copy_ceiling"] = best
         del dst
+    if "calib_mix" in want:
+        # the fused kernel's own mix: 576 bytes written per 4 KB read, no compute
+        mix_out = torch.empty(nbytes // 4096 * 576, dtype=torch.uint8, device=dev)
+        best = None
+        for lds in CALIB_MIX_LDS:
+            r = measure("calib traffic-mix ceiling, %d B LDS per workgroup" % lds,
+                        lambda: checked(calib.nvfp4_calib_mix(
+                            x.data_ptr(), mix_out.data_ptr(), nbytes, lds, stream)),
+                        nbytes + mix_out.numel(), nbytes // 2, st, ms, {"lds_bytes": lds})
+            best = r if best is None or r["GB_s"] > best["GB_s"] else best
+        sec["calib_mix_ceiling"] = best
+        del mix_out
 
     if "ragged" in want:
         # ragged grouped MoE: 256 experts (Zipf 1.1), 131072 x 4096, per-expert
@@ -626,6 +643,9 @@ def main():
         if "calib_copy_ceiling" in secondary:
             c = secondary["calib_copy_ceiling"]["GB_s"]
             secondary["fused_frac_of_copy_ceiling"] = round(achieved / c, 4)
+        if "calib_mix_ceiling" in secondary:
+            c = secondary["calib_mix_ceiling"]["GB_s"]
+            secondary["fused_frac_of_mix_ceiling"] = round(achieved / c, 4)
 
     cpu = None
     if not args.no_cpu_baseline:

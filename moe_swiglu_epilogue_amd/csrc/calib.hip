@@ -67,6 +67,34 @@ __global__ __launch_bounds__(kThreads) void calib_read_kernel(const u32x4* __res
         out[blockIdx.x] = part[0];
 }
 
+// The fused quantize kernel's traffic mix without its compute: per 4 KB
+// tile of src (one wave: four coalesced 1 KB non-temporal loads) a 576-byte
+// piece of dst (lanes 0..35, 16 bytes each, through a buffer resource that
+// drops the other lanes' stores, with the fused kernel's sc0 sc1 policy).
+// One tile per wave and no loop: the hardware dispatches the workgroups in
+// order, which measured fastest for this mix. Dynamic LDS, never touched,
+// caps the workgroups per CU.
+constexpr int kMixTileBytes = 4096;
+constexpr int kMixOutBytes = 576;
+
+__global__ __launch_bounds__(kThreads) void calib_mix_kernel(const u32x4* __restrict__ src,
+                                                             uint8_t* __restrict__ dst, int64_t tiles)
+{
+    const int lane = threadIdx.x & 63;
+    const int64_t t = blockIdx.x * (int64_t)kWavesPerBlock + (threadIdx.x >> 6);
+    if (t >= tiles)
+        return;
+    const u32x4* in = src + t * (kMixTileBytes / 16);
+    u32x4 v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        v[j] = __builtin_nontemporal_load(in + j * 64 + lane);
+    const u32x4 x = v[0] ^ v[1] ^ v[2] ^ v[3];
+    const __amdgpu_buffer_rsrc_t out =
+        __builtin_amdgcn_make_buffer_rsrc(dst + t * kMixOutBytes, (short)0, kMixOutBytes, 0x00020000);
+    __builtin_amdgcn_raw_buffer_store_b128(x, out, lane * 16, 0, 17);
+}
+
 }  // namespace
 
 extern "C" {
@@ -90,6 +118,22 @@ int nvfp4_calib_read(const void* src, void* out, int64_t bytes, int32_t blocks, 
         return 0;
     hipLaunchKernelGGL(calib_read_kernel, dim3(blocks), dim3(kThreads), 0, stream,
                        (const u32x4*)src, (u32x4*)out, bytes / 16);
+    return hipGetLastError() == hipSuccess ? 0 : 4;
+}
+
+int nvfp4_calib_mix(const void* src, void* dst, int64_t bytes, int32_t lds_bytes, hipStream_t stream)
+{
+    if (bytes < 0 || bytes % kMixTileBytes != 0 || lds_bytes < 0 || lds_bytes > 65536 ||
+        ((uintptr_t)src | (uintptr_t)dst) % 16)
+        return 1;
+    const int64_t tiles = bytes / kMixTileBytes;
+    const int64_t blocks = (tiles + kWavesPerBlock - 1) / kWavesPerBlock;
+    if (blocks > INT32_MAX)
+        return 1;
+    if (tiles == 0)
+        return 0;
+    hipLaunchKernelGGL(calib_mix_kernel, dim3((unsigned)blocks), dim3(kThreads), lds_bytes, stream,
+                       (const u32x4*)src, (uint8_t*)dst, tiles);
     return hipGetLastError() == hipSuccess ? 0 : 4;
 }
 

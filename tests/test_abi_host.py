@@ -58,7 +58,7 @@ def test_calib_library_exports_its_header(lib):
     import ctypes as C
     from moe_swiglu_epilogue_amd import build
     names = _declared(CALIB_HEADER)
-    assert names == ["nvfp4_calib_copy", "nvfp4_calib_read"]
+    assert names == ["nvfp4_calib_copy", "nvfp4_calib_mix", "nvfp4_calib_read"]
     assert set(names) <= _exported(build.CALIB_LIB)
     cl = C.CDLL(build.CALIB_LIB)
     for fn in (cl.nvfp4_calib_copy, cl.nvfp4_calib_read):
@@ -67,6 +67,13 @@ def test_calib_library_exports_its_header(lib):
         assert fn(A16, A16 + 4, 32, 8, None) == 1    # misaligned
         assert fn(A16, A16, 32, 0, None) == 1        # no workgroups
         assert fn(A16, A16, 0, 8, None) == 0         # empty: no launch
+    mix = cl.nvfp4_calib_mix
+    mix.argtypes = [C.c_void_p, C.c_void_p, C.c_int64, C.c_int32, C.c_void_p]
+    assert mix(A16, A16, 4096 + 16, 0, None) == 1     # not whole 4 KB tiles
+    assert mix(A16, A16 + 4, 4096, 0, None) == 1      # misaligned
+    assert mix(A16, A16, 4096, -1, None) == 1         # negative LDS
+    assert mix(A16, A16, 4096, 65537, None) == 1      # more LDS than a workgroup can have
+    assert mix(A16, A16, 0, 0, None) == 0             # empty: no launch
 
 
 def test_header_compiles_as_c(tmp_path):
