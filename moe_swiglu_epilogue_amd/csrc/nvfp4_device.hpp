@@ -6,8 +6,9 @@
 // listing the quantization primitives and their five fixes).
 //
 // Every function here reproduces the binary32 definition of the method
-// exactly (bit for bit), except swiglu(), which is a fast FP32 evaluation
-// within a few ulps of the correctly rounded value.
+// exactly (bit for bit), except times_sigma(), the SwiGLU product through the
+// sigmoid table, which is the binary32 rounding of g * u * sigmoid(g) except
+// within about 2^-46 of a rounding midpoint.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -18,26 +19,6 @@ namespace nvfp4 {
 // ---- BF16 -> FP32 (exact: a BF16 is the top half of a binary32) ------------
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-
-// ---- SwiGLU: silu(g) * u = g * u / (1 + e^-g) in FP32 ----------------------
-// e^-g = 2^(-g log2 e). log2 e is split as kLog2eHi + kLog2eLo with kLog2eHi
-// holding 16 significant bits, so for a BF16 gate (8 significant bits) the
-// product p = -g * kLog2eHi is EXACT in FP32; 2^p comes from v_exp_f32 and
-// the tail 2^(-g kLog2eLo) = 1 + (-g kLog2eLo ln 2) is folded into the
-// denominator with one fma: den = 2^p * (1 + c) + 1. |c| < 4.3e-4 for
-// |g| < 89, so the neglected c^2/2 is < 1e-7. Error budget: v_exp_f32 and
-// v_rcp_f32 about 1 ulp each plus four roundings: ~5 ulp (6e-7 relative).
-// g < -88.7 overflows 2^p to +inf and gives y = +-0 (true |y| < 1e-36).
-// The gate must be a BF16 value (exactness of p).
-__device__ __forceinline__ float swiglu_bf16(float g, float u)
-{
-    const float kLog2eHi = 0x1.7154p+0f;          // log2 e to 16 bits
-    const float kLog2eLoLn2 = 0x1.480fb6p-18f;    // (log2 e - kLog2eHi) ln 2
-    const float e = __builtin_amdgcn_exp2f(-g * kLog2eHi);
-    const float c = __builtin_fmaf(-g, kLog2eLoLn2, 1.0f);
-    const float den = __builtin_fmaf(e, c, 1.0f);
-    return (g * u) * __builtin_amdgcn_rcpf(den);
-}
 
 // ---- SwiGLU through a table of sigmoid values ------------------------------
 // A BF16 gate has 65536 values; sigma(g) = 1 / (1 + e^-g) only varies in FP32
