@@ -97,6 +97,8 @@ def test_fused_swiglu_over_every_bf16_gate():
     assert rep.requant_mismatch == 0, rep
     assert rep.scale_mismatch == rep.scale_exempt, rep
     assert rep.code_mismatch == rep.code_exempt, rep
+    # with the sigmoid as a binary32 pair, every gate's bytes are the oracle's
+    assert rep.scale_mismatch == 0 and rep.code_mismatch == 0, rep
 
 
 def test_compact_swiglu_over_every_bf16_gate():
