@@ -512,3 +512,26 @@ def test_bad_arguments_raise(M):
         M.swiglu_nvfp4_quantize(x)
     with pytest.raises(M.Nvfp4Error):
         M.nvfp4_quantize(torch.zeros((4, 24), dtype=torch.bfloat16, device="cuda"))
+
+
+def test_outputs_as_torch_fp8_and_fp4_views(M):
+    """The outputs are valid torch views: scales as float8_e4m3fn (torch's own
+    decode of our scale bytes, on the GPU) and packed as float4_e2m1fn_x2;
+    codes decoded from the nibbles (even element in the low nibble) times
+    torch's scale values equal the library's dequantize exactly (gs = 1: the
+    products are exact in FP32)."""
+    x = W.random_fused(64, 1024, seed=21, scale=3.0)
+    say("swiglu_nvfp4_quantize for dtype views", x.shape)
+    p, s = M.swiglu_nvfp4_quantize(dev_bf16(x))
+    rows, cols = p.shape[0], p.shape[1] * 2
+    sv = s.view(torch.float8_e4m3fn)
+    pv = p.view(torch.float4_e2m1fn_x2)
+    assert sv.shape == s.shape and pv.shape == p.shape
+    dq = M.nvfp4_dequantize(p, s)
+    nib = torch.stack([p & 15, p >> 4], dim=-1).reshape(rows, cols).long()
+    e2m1 = torch.tensor([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0], device="cuda")
+    sign = 1.0 - 2.0 * (nib >> 3).float()
+    vals = e2m1[nib & 7] * sign * sv.float().repeat_interleave(16, dim=1)
+    torch.cuda.synchronize()
+    assert torch.equal(vals, dq)
+    assert int((s == 0x7F).sum()) == 0 and int((s == 0xFF).sum()) == 0   # never NaN
