@@ -321,21 +321,16 @@ def group_amax(y: np.ndarray, offsets: np.ndarray) -> np.ndarray:
     return out
 
 
-GS_MIN = np.float32(2.0 ** -100)
-GS_MAX = np.float32(2.0 ** 100)
-
-
 def expert_global_scale(amax: np.ndarray) -> np.ndarray:
-    """Two-level NVFP4 global scale per expert: gs_e = RN32(amax_e / (6*448)),
-    so that the largest block scale of the expert lands on the FP8 maximum.
-    An empty or all-zero expert gets 1.0 (its value is never used). The
-    result is clamped to [2^-100, 2^100], the global scales the quantizer is
-    defined for (reading: the pages do not consider experts whose amax lies
-    below 2688 * 2^-100 or above 2688 * 2^100; such an expert's block scales
-    stay below 448, or saturate at it)."""
+    """Two-level NVFP4 global scale per expert: gs_e = RN32(amax_e / (6*448))
+    (one IEEE binary32 division), so that the largest block scale of the
+    expert lands on the FP8 maximum 448 ("NVFP4-1.1_APPROACH_PART_2.md", the
+    l2_global_scale parameter of the fused kernel; the per-expert
+    amax / (6 * 448) recipe of the ragged grouped MoE workload). An empty or
+    all-zero expert gets 1.0 (its value is never used)."""
     a = np.asarray(amax, dtype=np.float32)
-    gs = a / np.float32(6.0 * 448.0)          # binary32 IEEE division
-    gs = np.minimum(np.maximum(gs, GS_MIN), GS_MAX)
+    with np.errstate(under="ignore"):
+        gs = a / np.float32(6.0 * 448.0)          # binary32 IEEE division
     return np.where(a > 0, gs, np.float32(1.0)).astype(np.float32)
 
 

@@ -3,9 +3,12 @@
 Each case plants one mistake in a private copy of the oracle's C source (the
 kinds of bug the pages record - round-half-up, m/1024 subnormals, no mantissa
 carry, a 240 clamp, bias 8 - plus a dropped sign, swapped nibbles, swapped
-gate/up, a dropped global scale and a wrong exponent sign), builds it with gcc
-into a temporary directory, swaps it in, and requires that at least one pin
-fails. The committed oracle is never modified.
+gate/up, a dropped global scale and a wrong exponent sign; and in the fused
+reference driver and the row drivers: swapped gate/up, a wrong subtile
+stride, a per-row global scale ignored or taken from the first row, a
+shifted FP32 output), builds it with gcc into a temporary directory, swaps it
+in, and requires that at least one pin fails. The committed oracle is never
+modified.
 """
 import os
 import subprocess
@@ -48,6 +51,22 @@ MUTANTS = {
     "swiglu_f32_stride": ("int64_t col = 16 * (j / 8) + j % 8;", "int64_t col = 8 * (j / 8) + j % 8;"),
     "swiglu_bf16_shifted": ("out[r * inter + j] = oracle_f32_to_bf16(y[j]);",
                             "out[r * inter + j] = oracle_f32_to_bf16(y[j ^ 1]);"),
+    # the fused reference driver and the per-row global scales of the row drivers
+    "fused_driver_swapped_gate_up": (
+        "float g = oracle_bf16_to_f32(row[base + col % 8]);\n                float u = oracle_bf16_to_f32(row[base + 8 + col % 8]);",
+        "float u = oracle_bf16_to_f32(row[base + col % 8]);\n                float g = oracle_bf16_to_f32(row[base + 8 + col % 8]);"),
+    "fused_driver_stride": ("int64_t base = 16 * (col / 8);", "int64_t base = 8 * (col / 8);"),
+    "fused_driver_ignores_gs": ("const uint16_t *row = in + r * ld_in;\n        float gs = gs_rows ? gs_rows[r] : 1.0f;",
+                                "const uint16_t *row = in + r * ld_in;\n        float gs = 1.0f;"),
+    "fused_driver_first_row_gs": ("const uint16_t *row = in + r * ld_in;\n        float gs = gs_rows ? gs_rows[r] : 1.0f;",
+                                  "const uint16_t *row = in + r * ld_in;\n        float gs = gs_rows ? gs_rows[0] : 1.0f;"),
+    "fused_driver_out_shifted": ("swiglu_out[r * inter + col] = blk[j];", "swiglu_out[r * inter + (col ^ 1)] = blk[j];"),
+    "bf16_driver_ignores_gs": ("float gs = gs_rows ? gs_rows[r] : 1.0f;\n        for (int64_t b = 0; b < nb; ++b) {\n            float blk[16];\n            for (int j = 0; j < 16; ++j)\n                blk[j] = oracle_bf16_to_f32(x[",
+                               "float gs = 1.0f;\n        for (int64_t b = 0; b < nb; ++b) {\n            float blk[16];\n            for (int j = 0; j < 16; ++j)\n                blk[j] = oracle_bf16_to_f32(x["),
+    "f32_driver_ignores_gs": ("float gs = gs_rows ? gs_rows[r] : 1.0f;\n        for (int64_t b = 0; b < nb; ++b) {\n            float bsf;",
+                              "float gs = 1.0f;\n        for (int64_t b = 0; b < nb; ++b) {\n            float bsf;"),
+    "dequant_first_row_gs": ("float gs = gs_rows ? gs_rows[r] : 1.0f;\n        for (int64_t c = 0; c < cols; ++c) {",
+                             "float gs = gs_rows ? gs_rows[0] : 1.0f;\n        for (int64_t c = 0; c < cols; ++c) {"),
 }
 
 FAST_PINS = [P.pin_page_facts, P.pin_fp8_decode_vs_torch, P.pin_fp8_saturation,
@@ -57,7 +76,8 @@ FAST_PINS = [P.pin_page_facts, P.pin_fp8_decode_vs_torch, P.pin_fp8_saturation,
              P.pin_group_amax, P.pin_expert_global_scale, P.pin_bf16_ties,
              P.pin_swiglu_bf16_vs_torch, lambda: P.pin_bf16_vs_torch(step=9973),
              P.pin_swiglu_f32, P.pin_moe_l1_gemm,
-             lambda: P.pin_fp8_encode_vs_torch(step=997)]
+             lambda: P.pin_fp8_encode_vs_torch(step=997),
+             P.pin_quantize_rows_gs, P.pin_fused_driver]
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
@@ -98,8 +118,9 @@ PY_MUTANTS = {
     "gs_reciprocal_multiply": lambda a: np.where(
         a > 0, np.asarray(a, np.float32) * (np.float32(1.0) / np.float32(2688.0)),
         np.float32(1.0)).astype(np.float32),
-    "gs_no_clamp": lambda a: np.where(a > 0, np.asarray(a, np.float32) / np.float32(2688.0),
-                                      np.float32(1.0)).astype(np.float32),
+    "gs_clamped": lambda a: np.where(a > 0, np.clip(np.asarray(a, np.float32) / np.float32(2688.0),
+                                                    np.float32(2.0 ** -100), np.float32(2.0 ** 100)),
+                                     np.float32(1.0)).astype(np.float32),
 }
 
 

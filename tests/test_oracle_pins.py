@@ -219,21 +219,25 @@ def pin_quantize_vs_twin():
 
 
 def pin_dequant_closed_form():
-    """All 127 finite scales x random nibbles x three global scales against
-    RN32(RN32(e2m1 * scale) * gs) computed from the format definitions."""
+    """All 127 finite scales x random nibbles x three global scales, and a
+    different global scale on every row, against RN32(RN32(e2m1 * scale) * gs)
+    computed from the format definitions."""
     rng = np.random.default_rng(31)
     scales = np.arange(0, 0x7F, dtype=np.uint8).reshape(-1, 1)
     rows = scales.shape[0]
-    for gs in (1.0, float(np.float32(rng.uniform(1e-3, 1.0))), float(np.float32(3.3e-3))):
+    per_row = (10.0 ** rng.uniform(-3, 1, rows)).astype(np.float32)   # a scale per row
+    for gs_rows in (np.full(rows, 1.0, np.float32),
+                    np.full(rows, np.float32(rng.uniform(1e-3, 1.0)), np.float32),
+                    np.full(rows, 3.3e-3, np.float32), per_row):
         p = rng.integers(0, 256, (rows, 8)).astype(np.uint8)
         p[0] = np.arange(0, 128, 16) | np.arange(1, 129, 16)   # all 16 nibbles once
-        out = oracle.dequantize(p, scales, np.full(rows, gs, np.float32))
+        out = oracle.dequantize(p, scales, gs_rows)
         for r in range(rows):
             for c in range(16):
                 byte = int(p[r, c // 2])
                 nib = byte & 15 if c % 2 == 0 else byte >> 4
-                want = twin.dequant_value(nib, int(scales[r, 0]), gs)
-                assert out[r, c] == float(want), (r, c, nib, scales[r, 0], gs)
+                want = twin.dequant_value(nib, int(scales[r, 0]), float(gs_rows[r]))
+                assert out[r, c] == float(want), (r, c, nib, scales[r, 0], gs_rows[r])
 
 
 def pin_group_amax():
@@ -258,10 +262,10 @@ def pin_group_amax():
 
 def pin_expert_global_scale():
     """gs = RN32(amax / (6 * 448)): exact powers of two, 1.0 for an all-zero
-    expert, the nearest binary32 to the exact rational quotient, and the
-    defining property that the expert's largest block gets scale byte 0x7e
-    (the FP8 maximum 448); clamped to [2^-100, 2^100] beyond that range
-    (scale byte below 0x7e under the lower bound, saturated above)."""
+    expert, the nearest binary32 to the exact rational quotient (also far
+    outside any practical range, down into the subnormals), and the defining
+    property that the expert's largest block gets scale byte 0x7e (the FP8
+    maximum 448)."""
     from fractions import Fraction as F
     ks = np.arange(-20, 21)
     amax = (2688.0 * 2.0 ** ks).astype(np.float32)
@@ -269,28 +273,22 @@ def pin_expert_global_scale():
     assert oracle.expert_global_scale(np.zeros(3, np.float32)).tolist() == [1.0, 1.0, 1.0]
     rng = np.random.default_rng(43)
     a = (10.0 ** rng.uniform(-6, 6, 400)).astype(np.float32)
+    edge = np.array([2688.0 * 2.0 ** -100, 2688.0 * 2.0 ** -120, 1e-30, 1e-40, 2.0 ** -149,
+                     2688.0 * 2.0 ** 101, 3.0e38], np.float32)
+    a = np.concatenate([a, edge])
     gs = oracle.expert_global_scale(a)
     for ai, gi in zip(a, gs):
         q = F(float(ai)) / 2688
         err = abs(F(float(gi)) - q)
         for nb in (np.nextafter(gi, np.float32(np.inf)), np.nextafter(gi, np.float32(0))):
-            assert err < abs(F(float(nb)) - q), (ai, gi)
+            assert err <= abs(F(float(nb)) - q), (ai, gi)
+    assert gs[-7] == np.float32(2.0 ** -100) and gs[-6] == np.float32(2.0 ** -120)
+    assert gs[-2] == np.float32(2.0 ** 101) and gs[-3] == 0.0     # 2^-149 / 2688 rounds to 0
     for ai, gi in zip(a[:100], gs[:100]):
         x = np.zeros(16, np.float32)
         x[5] = -ai
         _, sf, _, _ = oracle.quantize_block(x, float(gi))
         assert sf == 0x7E, (ai, gi, hex(sf))
-    # the clamp to [2^-100, 2^100]: exactly at both bounds, and beyond them
-    lo, hi = np.float32(2.0 ** -100), np.float32(2.0 ** 100)
-    edge = np.array([2688.0 * 2.0 ** -100, 2688.0 * 2.0 ** -101, 2688.0 * 2.0 ** -120, 1e-40,
-                     2688.0 * 2.0 ** 100, 2688.0 * 2.0 ** 101, 3.0e38], np.float32)
-    want = np.array([lo, lo, lo, lo, hi, hi, hi], np.float32)
-    assert np.array_equal(oracle.expert_global_scale(edge), want), oracle.expert_global_scale(edge)
-    for ai, gi, top in ((edge[2], lo, False), (edge[6], hi, True)):
-        x = np.zeros(16, np.float32)
-        x[3] = ai
-        _, sf, _, _ = oracle.quantize_block(x, float(gi))
-        assert (sf == 0x7E) if top else (sf < 0x7E), (ai, hex(sf))
 
 
 def pin_bf16_vs_torch(step: int = 997, chunk: int = 1 << 24):
@@ -374,6 +372,93 @@ def pin_moe_l1_gemm():
     assert np.allclose(one, xf @ wf[1].T, rtol=0, atol=1e-12)
 
 
+def _twin_rows(x, gs_rows, packed, scales, what, rows=None, blocks=None):
+    """Every block of the selected rows of FP32 x against the exact-rational
+    twin with that row's global scale."""
+    nb = x.shape[1] // 16
+    for r in (range(x.shape[0]) if rows is None else rows):
+        for b in (range(nb) if blocks is None else blocks):
+            tp, tsf, _, _ = twin.quantize_block(list(x[r, 16 * b:16 * b + 16]), float(gs_rows[r]))
+            assert scales[r, b] == tsf, (what, r, b, float(gs_rows[r]), scales[r, b], tsf)
+            assert list(packed[r, 8 * b:8 * b + 8]) == tp, (what, r, b, float(gs_rows[r]))
+
+
+def _row_scales(rows, seed):
+    """One global scale per row: general binary32 values over 10^[-3, 1]
+    (so the quantized bytes depend on them), with a few powers of two and 1.0."""
+    rng = np.random.default_rng(seed)
+    g = (10.0 ** rng.uniform(-3, 1, rows)).astype(np.float32)
+    g[::5] = np.float32(2.0) ** rng.integers(-6, 3, g[::5].size).astype(np.float32)
+    g[1] = np.float32(1.0)
+    return g
+
+
+def pin_quantize_rows_gs():
+    """The row drivers with one global scale per row: quantize_bf16 and
+    quantize_f32 against the exact-rational twin, block by block, on a ragged
+    shape whose rows each carry a different scale. A driver that ignores
+    gs_rows, uses one row's scale for every row or reads the wrong row's
+    scale fails here."""
+    rng = np.random.default_rng(81)
+    rows, cols = 9, 80
+    x = W.to_bf16_bits(rng.standard_normal((rows, cols)) * 10.0 ** rng.uniform(-2, 2, (rows, 1)))
+    gs = _row_scales(rows, 82)
+    p, s = oracle.quantize_bf16(x, gs)
+    _twin_rows(W.bf16_bits_to_f32(x), gs, p, s, "quantize_bf16")
+    xf = (rng.standard_normal((rows, cols)) * 10.0 ** rng.uniform(-3, 3, (rows, 1))).astype(np.float32)
+    p, s = oracle.quantize_f32(xf, gs)
+    _twin_rows(xf, gs, p, s, "quantize_f32")
+    # reversing the rows reverses the output rows (the scale travels with its row)
+    p2, s2 = oracle.quantize_f32(xf[::-1].copy(), gs[::-1].copy())
+    assert np.array_equal(p2, p[::-1]) and np.array_equal(s2, s[::-1])
+
+
+def pin_fused_driver():
+    """The fused reference driver, the source of the expected bytes of every
+    fused parity case, pinned through independent routes:
+    * its FP32 SwiGLU output against PyTorch's float64 SiLU of the gate and up
+      values that were interleaved into the input ([gate x8, up x8] subtiles,
+      built here from separate gate and up tensors), within 1 ulp;
+    * its bytes, block by block, against the exact-rational twin applied to
+      PyTorch's values, with a different global scale on every row (ragged:
+      the row length is not a multiple of 64 blocks)."""
+    rng = np.random.default_rng(83)
+    rows, inter = 7, 112
+    g = W.to_bf16_bits(rng.standard_normal((rows, inter)) * 2.0)
+    u = W.to_bf16_bits(rng.standard_normal((rows, inter)) * 10.0 ** rng.uniform(-2, 2, (rows, 1)))
+    x = W.interleave(g, u)
+    gs = _row_scales(rows, 84)
+    p, s, y = oracle.swiglu_quantize(x, gs)
+    gt = torch.from_numpy(W.bf16_bits_to_f32(g).astype(np.float64))
+    ut = torch.from_numpy(W.bf16_bits_to_f32(u).astype(np.float64))
+    ref = (torch.nn.functional.silu(gt) * ut).to(torch.float32).numpy()
+    ulps = np.abs(y.view(np.int32).astype(np.int64) - ref.view(np.int32).astype(np.int64))
+    assert np.all(ulps <= 1) and np.all(np.signbit(y) == np.signbit(ref)), "fused driver swiglu"
+    assert np.mean(ulps == 0) > 0.99
+    nb = inter // 16
+    same = (y.view(np.uint32) == ref.view(np.uint32)).reshape(rows, nb, 16).all(axis=2)
+    assert same.mean() > 0.9
+    for r in range(rows):
+        _twin_rows(ref, gs, p, s, "fused driver", rows=[r],
+                   blocks=[b for b in range(nb) if same[r, b]])
+    # without gs every row uses 1.0
+    p1, s1, _ = oracle.swiglu_quantize(x)
+    _twin_rows(ref, np.ones(rows, np.float32), p1, s1, "fused driver gs=1",
+               rows=[0, rows - 1], blocks=[b for b in range(nb) if same[0, b] and same[rows - 1, b]])
+
+
+def pin_rows_global_scale():
+    """Per-expert scales expanded to rows by the offsets rule (row r belongs
+    to expert e when offsets[e] <= r < offsets[e+1]), with empty experts,
+    checked row by row."""
+    off = np.array([0, 0, 3, 3, 4, 9, 9], np.int32)
+    gs = np.array([0.5, 0.25, 3.0, 0.125, 7.0, 9.0], np.float32)
+    got = oracle.rows_global_scale(gs, off, 9)
+    for r in range(9):
+        e = [i for i in range(gs.size) if off[i] <= r < off[i + 1]]
+        assert len(e) == 1 and got[r] == gs[e[0]], (r, got[r])
+
+
 def pin_paged_kv():
     """The paged KV-cache write and read against what the slot rule fixes:
     identity slots reduce to quantize_bf16 of the rows; permuting rows and
@@ -427,7 +512,8 @@ ALL_PINS = [pin_page_facts, pin_fp8_decode_vs_torch, pin_fp8_saturation,
             pin_fp8_roundtrip, pin_e2m1_format, pin_e2m1_table, pin_swiglu_vs_torch,
             pin_swiglu_closed_forms, pin_quantize_vs_twin, pin_dequant_closed_form,
             pin_group_amax, pin_expert_global_scale, pin_bf16_vs_torch, pin_bf16_ties,
-            pin_swiglu_bf16_vs_torch, pin_swiglu_f32, pin_moe_l1_gemm, pin_paged_kv]
+            pin_swiglu_bf16_vs_torch, pin_swiglu_f32, pin_moe_l1_gemm, pin_paged_kv,
+            pin_quantize_rows_gs, pin_fused_driver, pin_rows_global_scale]
 
 
 # ---- tests --------------------------------------------------------------------
