@@ -95,7 +95,7 @@ def test_gemm_exact_operands(M, tokens, hidden, inter, experts, seed):
     say("fused GEMM exact", rep)
     if rep.swiglu_bad:
         yg, yr = r["y"].astype(np.float64), ry.astype(np.float64)
-        bad = np.argwhere(~(((np.abs(yg - yr) <= 2e-6 * np.abs(yr)) | (np.abs(yr) < 1e-30))
+        bad = np.argwhere(~((np.abs(yg - yr) <= np.maximum(2e-6 * np.abs(yr), P.SWIGLU_ABS))
                             & (np.signbit(yg) == np.signbit(yr))))
         for t, j in bad[:8]:
             col = 16 * (j // 8) + j % 8
@@ -120,7 +120,7 @@ def check_random(g, r, rows, gs=None):
     acc = oracle.moe_l1_gemm(g.x, g.w1, g.offsets, rows=rows)
     mag = oracle.moe_l1_gemm(g.x & np.uint16(0x7FFF), g.w1 & np.uint16(0x7FFF), g.offsets, rows=rows)
     hidden = g.x.shape[1]
-    bound = hidden * 2.0 ** -24 * mag + 1e-30
+    bound = hidden * 2.0 ** -24 * mag + P.SWIGLU_ABS
     # BF16 output: within half a BF16 ulp of the exact sum, plus the bound
     got = (r["bf16"][rows].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
     half_ulp = np.abs(acc) * 2.0 ** -8 + 2.0 ** -134
@@ -133,7 +133,7 @@ def check_random(g, r, rows, gs=None):
     sg = 1.0 / (1.0 + np.exp(-np.clip(gg, -700, 700)))
     y_ref = gg * sg * uu
     tol = (np.abs(uu) * np.abs(sg * (1 + gg * (1 - sg))) * bg + np.abs(gg * sg) * bu
-           + 2e-6 * np.abs(y_ref) + 1e-30)
+           + np.maximum(2e-6 * np.abs(y_ref), P.SWIGLU_ABS))
     err = np.abs(r["y"][rows].astype(np.float64) - y_ref)
     assert np.all(err <= tol), ("swiglu outside the bound", float((err / tol).max()))
     # bytes: the oracle quantizer on the kernel's own FP32 SwiGLU values
@@ -231,7 +231,7 @@ def test_gemm_epilogue_over_every_bf16_gate(M):
     say("every-gate epilogue:", rep)
     if rep.swiglu_bad:
         yg, yr = r["y"].astype(np.float64), ry.astype(np.float64)
-        bad = np.argwhere(~(((np.abs(yg - yr) <= 2e-6 * np.abs(yr)) | (np.abs(yr) < 1e-30))
+        bad = np.argwhere(~((np.abs(yg - yr) <= np.maximum(2e-6 * np.abs(yr), P.SWIGLU_ABS))
                             & (np.signbit(yg) == np.signbit(yr))))
         for t, j in bad[:: max(1, len(bad) // 24)][:24]:
             col = 16 * (j // 8) + j % 8
