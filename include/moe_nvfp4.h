@@ -67,10 +67,15 @@
  *   num_experts >= 1 exactly when expert_offsets != NULL; rows < 2^31 and
  *   rows * ceil(cols / 1024) <= 2^30 (tiles of 64 blocks).
  *   rows == 0 or cols == 0 is a successful no-op.
- * Not checked (device data, asynchronous): finite inputs; gs finite, > 0
- *   and within [2^-100, 2^100]; the offset rules above. Violations give
- *   unspecified output bytes, never out-of-bounds accesses on the output
- *   region for rows that the offsets place inside [0, rows).
+ * Not checked (device data, asynchronous): finite inputs; gs within
+ *   [2^-64, 2^64] (there every quotient of the quantizer is correctly
+ *   rounded: its remainders stay in the normal binary32 range); the offset
+ *   rules above. Violations give unspecified output bytes, never
+ *   out-of-bounds accesses on the output region for rows that the offsets
+ *   place inside [0, rows). Within them no quotient overflows or turns into
+ *   NaN: in a block whose scale saturates, every value beyond 6 scale units
+ *   gets the largest magnitude with its own sign, an infinite SwiGLU value
+ *   (finite gate and up whose product exceeds the FP32 range) included.
  * Errors: a launch failure reported by hipGetLastError() returns
  *   NVFP4_ERROR_LAUNCH; faults during execution surface at the caller's next
  *   synchronization, as usual for HIP.
@@ -116,10 +121,15 @@ nvfp4_status_t nvfp4_quantize(const uint16_t *x, int64_t rows, int64_t cols,
  * packed[rows][inter/2], scales[rows][inter/16] and, when swiglu_out is not
  * NULL, the FP32 y values [rows][inter] (a debug output: the quantized bytes
  * are the same with or without it). Each y is the binary32 rounding of the
- * exact gate * up * sigmoid(gate), except where that value lies within about
- * 2^-46 (relative) of a rounding midpoint, where it may be the neighbouring
- * binary32 value, and except for |gate| < 2^-24, where sigmoid(+-2^-24)
- * stands for sigmoid(gate) (less than 2^-26 away).
+ * exact gate * up * sigmoid(gate), for every finite BF16 gate and up, except:
+ * where that value lies within about 2^-46 (relative) of a rounding
+ * midpoint, or below 2^-100 in magnitude, it may be the neighbouring binary32
+ * value (one subnormal step below 2^-126); for |gate| < 2^-24,
+ * sigmoid(+-2^-24) stands for sigmoid(gate) (less than 2^-26 away). Gates at
+ * or below -64 (sigmoid leaves the binary32 range from -87.3 down) and
+ * products gate * up beyond the FP32 range take a binary64 path, within
+ * about 2^-51 of a midpoint. y is never NaN; it is +-inf only where the
+ * exact value rounds to it.
  */
 nvfp4_status_t swiglu_nvfp4_quantize(const uint16_t *gate_up, int64_t rows,
                                      int64_t inter, int64_t ld_in,
@@ -148,9 +158,9 @@ nvfp4_status_t nvfp4_dequantize(const uint8_t *packed, const uint8_t *scales,
  *     gs[e] = RN(amax_e / (6 * 448))        (1.0 when amax_e == 0 or the
  *                                            expert has no rows),
  * which puts the expert's largest block scale on the FP8 maximum 448,
- * clamped to [2^-100, 2^100], the global scales the quantize calls accept
- * (an expert with amax below 2688 * 2^-100 keeps block scales under 448; one
- * above 2688 * 2^100 saturates them).
+ * clamped to [2^-64, 2^64], the global scales the quantize calls accept
+ * (an expert with amax below 2688 * 2^-64 keeps block scales under 448; one
+ * above 2688 * 2^64 saturates them).
  * Page: "NVFP4-1.1_APPROACH_PART_2.md" (the fused kernel's l2_global_scale
  * parameter, the decode-direction global scale in the FP8 scale rule), with
  * the per-expert amax / (6 * 448) recipe of the ragged grouped MoE workload.

@@ -1,5 +1,6 @@
-"""Build libmoe_nvfp4.so (HIP kernels for gfx950 + the C ABI) and the
-bandwidth-calibration library libnvfp4_calib.so with hipcc.
+"""Build libmoe_nvfp4.so (HIP kernels for gfx950 + the C ABI), the
+bandwidth-calibration library libnvfp4_calib.so and the quotient-check
+library libnvfp4_divcheck.so with hipcc.
 
 The library is built in-tree, next to this file, so that it travels with the
 source tree. Run ``python -m moe_swiglu_epilogue_amd.build``.
@@ -15,6 +16,8 @@ GEMM_SRC = os.path.join(HERE, "csrc", "moe_gemm.hip")
 LIB = os.path.join(HERE, "libmoe_nvfp4.so")
 CALIB_SRC = os.path.join(HERE, "csrc", "calib.hip")
 CALIB_LIB = os.path.join(HERE, "libnvfp4_calib.so")
+DIVCHECK_SRC = os.path.join(HERE, "csrc", "divcheck.hip")
+DIVCHECK_LIB = os.path.join(HERE, "libnvfp4_divcheck.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
@@ -28,8 +31,9 @@ FLAGS = [
 
 
 def build(verbose: bool = False) -> str:
-    """Build both libraries; return the path of libmoe_nvfp4.so."""
+    """Build the three libraries; return the path of libmoe_nvfp4.so."""
     _build_one([CALIB_SRC], CALIB_LIB, verbose)
+    _build_one([DIVCHECK_SRC], DIVCHECK_LIB, verbose)
     return _build_one([SRC, GEMM_SRC], LIB, verbose)
 
 

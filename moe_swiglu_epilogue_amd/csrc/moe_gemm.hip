@@ -450,30 +450,37 @@ __device__ __forceinline__ void stage_accumulators(float* c, const f32x16 (&acc)
 }
 
 // ---- SwiGLU of FP32 values -------------------------------------------------
-// silu(g) u = g u / (1 + e^-g), e^-g = 2^(-g log2 e). log2 e = kL2eHi + kL2eLo
-// (kL2eHi = RN(log2 e)); the product -g kL2eHi is split into its rounded
-// value p and exact error (fma), so 2^(-g log2 e) = 2^p 2^t with
-// t = perr - g kL2eLo, |t| < 2e-5 for |g| <= 128, and 2^t = 1 + t ln 2 to
-// better than 1e-10. v_exp_f32 and v_rcp_f32 are about 1 ulp each: about
-// 4 ulp in all. The sigmoid's argument is clamped to [-128, 128], where it
-// has already saturated in FP32 (1 above; below, 2^p overflows, 1/(1 + inf)
-// is 0 and y is a zero with the sign of g u): unclamped, -g log2 e overflows
-// for |g| > 2.3e38 and the split turns into 0 * inf (NaN) or a zero of the
-// wrong sign.
+// silu(g) u = g u sigma(g), sigma(g) = 1 / (1 + e^-|g|) for g >= 0 and
+// e^-|g| / (1 + e^-|g|) for g < 0, with a = |g| clamped to 300 (beyond it
+// sigma is 1 to binary32 precision, or so small that g u sigma(g) rounds to
+// zero for any FP32 g and u: |g u| < 2^256 and e^-300 < 2^-432).
+// e^-a = 2^(-a log2 e): log2 e = kL2eHi + kL2eLo (kL2eHi = RN(log2 e)); the
+// product -a kL2eHi is split into its rounded value p and exact error (fma),
+// so e^-a = 2^p 2^t with t = perr - a kL2eLo, |t| < 2e-4, and 2^t = 1 + t ln 2
+// to better than 2e-8 relative. 2^p is formed as 2^(p + k) 2^-k with k the
+// multiple of 64 that puts p + k in (-64, 0] (p + k is exact), so that
+// v_exp_f32 and the sigmoid stay in the normal range down to g = -300;
+// v_exp_f32 and v_rcp_f32 are about 1 ulp each: about 4 ulp in all. The
+// product g u (sigma 2^k) 2^-k is formed in binary64 (g u exact, one rounding,
+// an exact power-of-two scaling) and rounded once to binary32, so neither
+// g u nor a tiny sigma leaves the range on the way: y has sigma's relative
+// error down into the binary32 subnormals, and a zero keeps the sign of g u.
 __device__ __forceinline__ float swiglu_f32(float g, float u)
 {
     const float kL2eHi = 0x1.715476p+0f;
     const float kL2eLo = 0x1.4ae0bep-26f;
     const float kLn2 = 0x1.62e430p-1f;
-    const float gc = __builtin_fminf(__builtin_fmaxf(g, -128.0f), 128.0f);
-    const float p = -gc * kL2eHi;
-    const float perr = __builtin_fmaf(-gc, kL2eHi, -p);
-    const float t = __builtin_fmaf(-gc, kL2eLo, perr);
-    const float e0 = __builtin_amdgcn_exp2f(p);
-    // e0 (1 + t ln 2), not e0 + e0 t ln 2: when 2^p overflows the factor is
-    // positive and inf stays inf (inf - inf would be NaN)
-    const float e = e0 * __builtin_fmaf(t, kLn2, 1.0f);
-    return (g * u) * __builtin_amdgcn_rcpf(1.0f + e);
+    const float a = __builtin_fminf(__builtin_fabsf(g), 300.0f);
+    const float p = -a * kL2eHi;
+    const float perr = __builtin_fmaf(-a, kL2eHi, -p);
+    const float t = __builtin_fmaf(-a, kL2eLo, perr);
+    const int k = (int)(-p * 0.015625f) * 64;
+    const float es = __builtin_amdgcn_exp2f(p + (float)k) * __builtin_fmaf(t, kLn2, 1.0f);
+    const float r = __builtin_amdgcn_rcpf(1.0f + __builtin_ldexpf(es, -k));
+    const bool neg = g < 0.0f;
+    const float ss = neg ? es * r : r;          // sigma(g) 2^kk
+    const int kk = neg ? k : 0;
+    return (float)__builtin_ldexp((double)g * (double)u * (double)ss, -kk);
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
@@ -518,7 +525,7 @@ __device__ __forceinline__ void fused_block(const Gemm& g, const TileRef& tr, in
         y[8 + j] = swiglu_f32(v[16 + j], v[24 + j]);
     }
     uint32_t sf;
-    const uint2 q = nvfp4::quantize16(y, rs, sf);
+    const uint2 q = nvfp4::quantize16(y, nvfp4::block_amax(y), rs, sf);
     const int trow = pass_row(pass, row);
     if (trow < tr.rows) {
         const int64_t grow = tr.row0 + trow;

@@ -222,30 +222,65 @@ struct FusedBlock {
     // the prefill shape, 12 or 16 waves per CU are 4-6% slower and 4 waves
     // per CU 25% slower.
     static constexpr int kWaves = 8;
-    static constexpr int kBlocksPerCU = 1;   // 64 KB sigma table + 8 x 4.25 KB staging
+    static constexpr int kBlocksPerCU = 1;   // 66 KB sigma table + 8 x 4.25 KB staging
     static constexpr bool kSigmaTable = true;
     // Consecutive tiles per wave with wide stores (their scale bytes leave
     // as one piece). Measured on the prefill shape: 2 and 4 are 1.5-1.7%
     // slower than 1 and 8 is 6% slower; the walk's read order matters more
     // here than the size of the scale pieces.
     static constexpr int kScaleGroup = 1;
-    // y = silu(gate) * up = (gate * up) * sigma(gate) for the 16 outputs.
-    __device__ static __forceinline__ void values(const u32x4 (&c)[4], float (&y)[16],
+    // The block's 16 values y = silu(gate) * up = (gate * up) * sigma(gate)
+    // and their largest magnitude, with sigma from the table in LDS. All 16
+    // table reads are issued before the first product, so that their
+    // latencies overlap. The common path is the binary32 pair product
+    // (times_sigma). Its amax (NaN-propagating) is finite unless the block
+    // holds a gate at or below -64, whose marked entry makes the product
+    // +-inf (or NaN for g u = 0), or a product g u beyond the FP32 range
+    // (+-inf; only gates or ups of magnitude near 2^64 and beyond make one).
+    // Such blocks take the exact binary64 product for every value instead
+    // (swiglu_wide; lanes diverge, waves without such a block skip it), so
+    // the common path pays one compare for both cases.
+    __device__ static __forceinline__ float block(const u32x4 (&c)[4], float (&y)[16],
                                                   const uint8_t* sig)
     {
         const uint32_t gw[8] = {c[0].x, c[0].y, c[0].z, c[0].w, c[2].x, c[2].y, c[2].z, c[2].w};
         const uint32_t uw[8] = {c[1].x, c[1].y, c[1].z, c[1].w, c[3].x, c[3].y, c[3].z, c[3].w};
+        float2 e[16];
+        uint32_t o[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            uint32_t o = nvfp4::sigma_offsets(gw[i]);
+            o[i] = nvfp4::sigma_offsets(gw[i]);
             // keep o whole: one shift-or builds it, then one mask and one
             // shift split it (the compiler would otherwise rebuild each half)
-            asm("" : "+v"(o));
-            const float2 s0 = *reinterpret_cast<const float2*>(sig + (o & 0xffffu));
-            const float2 s1 = *reinterpret_cast<const float2*>(sig + (o >> 16));
-            y[2 * i] = nvfp4::times_sigma(nvfp4::bf16_lo(gw[i]) * nvfp4::bf16_lo(uw[i]), s0);
-            y[2 * i + 1] = nvfp4::times_sigma(nvfp4::bf16_hi(gw[i]) * nvfp4::bf16_hi(uw[i]), s1);
+            asm("" : "+v"(o[i]));
+            e[2 * i] = *reinterpret_cast<const float2*>(sig + (o[i] & 0xffffu));
+            e[2 * i + 1] = *reinterpret_cast<const float2*>(sig + (o[i] >> 16));
         }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            y[2 * i] = nvfp4::times_sigma(nvfp4::bf16_lo(gw[i]) * nvfp4::bf16_lo(uw[i]), e[2 * i]);
+            y[2 * i + 1] = nvfp4::times_sigma(nvfp4::bf16_hi(gw[i]) * nvfp4::bf16_hi(uw[i]),
+                                              e[2 * i + 1]);
+        }
+        float amax = nvfp4::block_amax(y);
+        if (!(amax < __builtin_inff())) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const uint32_t off = h ? o[i] >> 16 : o[i] & 0xffffu;
+                    const double sigma =
+                        off >= nvfp4::kSigWideOffset
+                            ? *reinterpret_cast<const double*>(sig + off + nvfp4::kSigWideShift)
+                            : (double)e[2 * i + h].x + (double)e[2 * i + h].y;
+                    const float g = h ? nvfp4::bf16_hi(gw[i]) : nvfp4::bf16_lo(gw[i]);
+                    const float u = h ? nvfp4::bf16_hi(uw[i]) : nvfp4::bf16_lo(uw[i]);
+                    y[2 * i + h] = nvfp4::swiglu_wide(g, u, sigma);
+                }
+            }
+            amax = nvfp4::block_amax(y);
+        }
+        return amax;
     }
 };
 
@@ -257,7 +292,7 @@ struct PlainBlock {
     // 128-byte scale pieces: 1.5% faster than 1 tile on 65536 x 3072
     // (4 tiles: level with 1; 8 tiles: 3% slower).
     static constexpr int kScaleGroup = 2;
-    __device__ static __forceinline__ void values(const u32x4 (&c)[2], float (&y)[16],
+    __device__ static __forceinline__ float block(const u32x4 (&c)[2], float (&y)[16],
                                                   const uint8_t*)
     {
         const uint32_t w[8] = {c[0].x, c[0].y, c[0].z, c[0].w, c[1].x, c[1].y, c[1].z, c[1].w};
@@ -266,6 +301,7 @@ struct PlainBlock {
             y[2 * i] = nvfp4::bf16_lo(w[i]);
             y[2 * i + 1] = nvfp4::bf16_hi(w[i]);
         }
+        return nvfp4::block_amax(y);
     }
 };
 
@@ -274,8 +310,8 @@ struct PlainBlock {
 // groups further on (G = 1: every `stride`-th tile). The caller has
 // tile < geo.tiles, and runs `setup` itself on waves without a tile so that
 // every wave reaches its barrier once.
-// keeps one tile in flight and calls op(tile, t, b, y) with each lane's block b of
-// tile t and its 16 values y. Loop invariant: tile t is staged in LDS and no
+// keeps one tile in flight and calls op(tile, t, b, y, amax) with each lane's
+// block b of tile t, its 16 values y and their largest magnitude. Loop invariant: tile t is staged in LDS and no
 // loads are in flight. Each pass issues the loads of the next tile first,
 // computes tile t from LDS and runs op, then stages the next tile; op may
 // store (its stores are the only memory operations younger than those
@@ -318,8 +354,8 @@ __device__ __forceinline__ void walk_tiles(const uint16_t* in, int64_t ld_in, co
         for (int k = 0; k < P; ++k)
             c[k] = lds[lds_slot(b * P + k)];
         float y[16];
-        Block::values(c, y, sig);
-        op(tile, t, b, y);
+        const float amax = Block::block(c, y, sig);
+        op(tile, t, b, y, amax);
         if (!has_next)
             break;
         wave_lds_sync();
@@ -399,35 +435,45 @@ struct ExpertBatch {
     }
 };
 
-// sigma(g) = 1 / (1 + e^-g) as binary32 pairs {RZ(sigma), RN(sigma - hi)}
-// (bit patterns) for the table's gates: positive magnitudes m = 0 ..
-// kSigSpan - 1, then the negative ones (generated by gen_sigma_table.py with
-// 150-digit arithmetic). The LDS table is a plain copy of it.
+// sigma(g) = 1 / (1 + e^-g) for the table's gates (generated by
+// gen_sigma_table.py with 150-digit arithmetic): the main table, two 32-bit
+// words per entry (a binary32 pair {RZ(sigma), RN(sigma - hi)}, or +inf, +inf
+// for the last kSigWide negative entries), positive magnitudes m = 0 ..
+// kSigSpan - 1, then the negative ones; then the wide table, kSigWide binary64
+// values for the marked gates, low word first. The LDS table is a plain copy
+// of it.
 __device__ const uint32_t kSigmaBits[] __attribute__((aligned(16))) = {
 #include "sigma_table.inc"
 };
-static_assert(sizeof(kSigmaBits) == nvfp4::kSigFloats * 4, "one pair per gate");
+static_assert(sizeof(kSigmaBits) == nvfp4::kSigFloats * 4, "main and wide tables");
 
 // Fills the workgroup's sigmoid table in LDS (fused input only) from
-// kSigmaBits: 64 KB, eight 16-byte loads per thread, served by L2 after the
-// first workgroups. Every wave of the workgroup takes part, so all of them
-// reach the barrier.
+// kSigmaBits: 66 KB, eight or nine 16-byte loads per thread, served by L2
+// after the first workgroups. Every wave of the workgroup takes part, so all
+// of them reach the barrier.
 template <class Block>
 __device__ __forceinline__ void fill_sigma_table(float* sig)
 {
     if constexpr (Block::kSigmaTable) {
         constexpr int kThreadsPerBlock = Block::kWaves * kWave;
         constexpr int kWords = nvfp4::kSigFloats / 4;   // 16-byte words
-        static_assert(kWords % kThreadsPerBlock == 0, "whole words per thread");
+        constexpr int kFull = kWords / kThreadsPerBlock;
+        constexpr int kRest = kWords - kFull * kThreadsPerBlock;
+        static_assert(kRest < kThreadsPerBlock, "one more word for some threads");
         const u32x4* src = reinterpret_cast<const u32x4*>(kSigmaBits);
         u32x4* dst = reinterpret_cast<u32x4*>(sig);
-        u32x4 v[kWords / kThreadsPerBlock];
+        u32x4 v[kFull + 1];
 #pragma unroll
-        for (int k = 0; k < kWords / kThreadsPerBlock; ++k)
+        for (int k = 0; k < kFull; ++k)
             v[k] = src[k * kThreadsPerBlock + threadIdx.x];
+        const bool rest = threadIdx.x < kRest;
+        if (rest)
+            v[kFull] = src[kFull * kThreadsPerBlock + threadIdx.x];
 #pragma unroll
-        for (int k = 0; k < kWords / kThreadsPerBlock; ++k)
+        for (int k = 0; k < kFull; ++k)
             dst[k * kThreadsPerBlock + threadIdx.x] = v[k];
+        if (rest)
+            dst[kFull * kThreadsPerBlock + threadIdx.x] = v[kFull];
     }
 }
 
@@ -470,7 +516,7 @@ __global__ __launch_bounds__(Block::kWaves * kWave) void quantize_tiles_kernel(
     int n = 0;   // tiles done by this wave
     walk_tiles<Block, G>(in, ld_in, geo, tile, stride, lane, lds,
                          reinterpret_cast<const uint8_t*>(sig), setup,
-                         [&](int tile_index, const Tile& t, int b, const float (&y)[16]) {
+                         [&](int tile_index, const Tile& t, int b, const float (&y)[16], float amax) {
         if (lds_experts) {
             const int j = n & (kWave - 1);
             if (j == 0)
@@ -481,7 +527,7 @@ __global__ __launch_bounds__(Block::kWaves * kWave) void quantize_tiles_kernel(
             rs = nvfp4::row_scale(nvfp4::row_global_scale(gs, offsets, num_experts, t.row));
         }
         uint32_t sf;
-        const uint2 q = nvfp4::quantize16(y, rs, sf);
+        const uint2 q = nvfp4::quantize16(y, amax, rs, sf);
         if constexpr (kWide)
             store_tile_outputs_grouped<G>(reinterpret_cast<uint8_t*>(lds),
                                           reinterpret_cast<uint8_t*>(win[wave]), q, sf, t,
@@ -538,13 +584,13 @@ __global__ __launch_bounds__(PlainBlock::kWaves * kWave) void quantize_paged_ker
         return;
     const nvfp4::RowScale rs = nvfp4::row_scale(gs != nullptr ? gs[0] : 1.0f);
     walk_tiles<PlainBlock>(in, ld_in, geo, tile, gridDim.x * kWaves, lane, stage[wave], nullptr,
-                           [] {}, [&](int, const Tile& t, int b, const float (&y)[16]) {
+                           [] {}, [&](int, const Tile& t, int b, const float (&y)[16], float amax) {
         const int64_t slot = slots[t.row];
         const bool keep = slot >= 0 && slot < num_slots;
         Tile o = t;
         o.row = keep ? (int)slot : 0;
         uint32_t sf;
-        const uint2 q = nvfp4::quantize16(y, rs, sf);
+        const uint2 q = nvfp4::quantize16(y, amax, rs, sf);
         store_tile_outputs<kWide>(reinterpret_cast<uint8_t*>(stage[wave]), q, sf, o, b, lane, geo,
                                   packed, scales, keep);
     });
@@ -572,7 +618,7 @@ __global__ __launch_bounds__(FusedBlock::kWaves * kWave) void swiglu_bf16_kernel
     }
     walk_tiles<Block>(in, ld_in, geo, tile, gridDim.x * kWaves, lane, lds,
                       reinterpret_cast<const uint8_t*>(sig), setup,
-                      [&](int, const Tile& t, int b, const float (&y)[16]) {
+                      [&](int, const Tile& t, int b, const float (&y)[16], float) {
         u32x4 w[2];
 #pragma unroll
         for (int h = 0; h < 2; ++h)
@@ -660,7 +706,7 @@ __global__ __launch_bounds__(Block::kWaves * kWave) void amax_tiles_kernel(
         };
         walk_tiles<Block>(in, ld_in, geo, tile, stride, lane, stage[wave],
                           reinterpret_cast<const uint8_t*>(sig), setup,
-                          [&](int tile_index, const Tile&, int, const float (&y)[16]) {
+                          [&](int tile_index, const Tile&, int, const float (&)[16], float amax) {
             int e = 0;
             if (offsets != nullptr) {
                 const int j = n & (kWave - 1);
@@ -675,9 +721,7 @@ __global__ __launch_bounds__(Block::kWaves * kWave) void amax_tiles_kernel(
                 cur = e;
                 run = 0.0f;
             }
-#pragma unroll
-            for (int i = 0; i < 16; ++i)
-                run = fmaxf(run, fabsf(y[i]));
+            run = fmaxf(run, amax);
         });
         flush();
     }
@@ -689,15 +733,19 @@ __global__ __launch_bounds__(Block::kWaves * kWave) void amax_tiles_kernel(
     }
 }
 
-// gs[e] = RN(amax[e] / 2688) (IEEE division) clamped to [2^-100, 2^100], the
-// global scales the quantizers are defined for; 1.0 for an empty or all-zero
-// expert. acc holds the amax bits and may be the gs array itself.
+// gs[e] = RN(amax[e] / 2688) (IEEE division) for a non-empty expert with a
+// nonzero amax, 1.0 otherwise; then clamped to [kGsMin, kGsMax], the global
+// scales the quantizers are exact for (outside it the remainders of their
+// quotients can leave the normal binary32 range). acc holds the amax bits
+// and may be the gs array itself.
+constexpr float kGsMin = 0x1p-64f, kGsMax = 0x1p+64f;
+
 __global__ void global_scale_kernel(const uint32_t* acc, float* gs, int n)
 {
-    const float lo = 0x1p-100f, hi = 0x1p+100f;
     for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) {
         const float a = __uint_as_float(acc[i]);
-        gs[i] = a > 0.0f ? __builtin_fminf(__builtin_fmaxf(a / kFp4Fp8Max, lo), hi) : 1.0f;
+        const float g = a > 0.0f ? a / kFp4Fp8Max : 1.0f;
+        gs[i] = __builtin_fminf(__builtin_fmaxf(g, kGsMin), kGsMax);
     }
 }
 

@@ -6,9 +6,10 @@
 // listing the quantization primitives and their five fixes).
 //
 // Every function here reproduces the binary32 definition of the method
-// exactly (bit for bit), except times_sigma(), the SwiGLU product through the
-// sigmoid table, which is the binary32 rounding of g * u * sigmoid(g) except
-// within about 2^-46 of a rounding midpoint.
+// exactly (bit for bit), except the SwiGLU products through the sigmoid
+// table (times_sigma, swiglu_wide), which are the binary32 rounding of
+// g * u * sigmoid(g) except within about 2^-46 (relative) of a rounding
+// midpoint, and within one binary32 step of it below 2^-100.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -24,20 +25,36 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 // A BF16 gate has 65536 values; sigma(g) = 1 / (1 + e^-g) only varies in FP32
 // for 2^-24 <= |g| < 256. The table holds sigma for every BF16 magnitude in
 // that range (exponent field 103..134, all 128 mantissas: kSigSpan values)
-// and both signs, each entry a pair of floats hi = sigma rounded toward zero,
-// lo = RN(sigma - hi) >= 0 (8 bytes; hi + lo carries sigma to about 2^-47). Positive
-// gates use entries [0, kSigSpan), negative ones [kSigSpan, 2 kSigSpan):
-// kSigSpan * 8 = 32768 is bit 15 of a BF16 half-word, so the sign bit serves
-// as the sign's byte offset where it stands. Magnitudes below the range read
-// the first entry (sigma = 1/2 +- 2^-26 +- ... there), magnitudes above it the
-// last (sigma is 1 to within 2^-367, or below 2^-367 for negative g). The
-// entries are computed at build time (gen_sigma_table.py) and copied into
-// LDS once per workgroup; a lookup then replaces exp and rcp per element.
+// and both signs, 8 bytes per entry. Positive gates use entries
+// [0, kSigSpan), negative ones [kSigSpan, 2 kSigSpan): kSigSpan * 8 = 32768
+// is bit 15 of a BF16 half-word, so the sign bit serves as the sign's byte
+// offset where it stands. Magnitudes below the range read the first entry
+// (sigma = 1/2 +- 2^-26 +- ... there), magnitudes above it the last.
+// Main table entries (gen_sigma_table.py):
+//   * gates above -64: a pair of binary32, hi = sigma rounded toward zero and
+//     lo = RN(sigma - hi) >= 0, both normal (hi + lo carries sigma to about
+//     2^-47): times_sigma below;
+//   * gates at or below -64 (the last kSigWide negative entries): the pair
+//     (+inf, +inf), a marker: from -87.3 down sigma leaves the binary32
+//     normal range (it reaches about 2^-368 at -255), so the pair product is
+//     replaced by swiglu_wide with sigma from the wide table that follows the
+//     main one (kSigWide binary64 values, byte offset of an entry = its main
+//     offset + kSigWideShift). The last wide entry, read for every gate at or
+//     below -255, holds 2^-1000, which makes the product a zero with the sign
+//     of g u there, as the exact value rounds.
+// The entries are computed at build time and copied into LDS once per
+// workgroup; a lookup then replaces exp and rcp per element.
 constexpr uint32_t kSigLo = 103u << 7;
 constexpr uint32_t kSigHi = (134u << 7) | 127u;
 constexpr int kSigSpan = (int)(kSigHi - kSigLo + 1);   // 4096
-constexpr int kSigFloats = 4 * kSigSpan;                // 16384 (64 KB)
+constexpr int kSigWide = 256;                           // gates -64 .. -255
+constexpr int kSigFloats = 4 * kSigSpan + 2 * kSigWide; // 16896 32-bit words (66 KB)
+// main byte offset (as produced by sigma_offsets) of the first marked entry
+constexpr uint32_t kSigWideOffset = 0x8000u + 8u * (uint32_t)(kSigSpan - kSigWide);
+// wide byte offset = main byte offset + kSigWideShift (wide table at 64 KB)
+constexpr uint32_t kSigWideShift = 4u * 4u * (uint32_t)kSigSpan - kSigWideOffset;
 static_assert(kSigSpan * 8 == 0x8000, "sign bit is the offset of the negative half");
+static_assert(kSigWideOffset == 0xF800u, "gate -64 = BF16 0xC280 starts the marked entries");
 
 // Byte offsets of the table entries for the two BF16 gates of w, in the
 // matching halves of the result. Both halves are done at once in packed
@@ -55,16 +72,29 @@ __device__ __forceinline__ uint32_t sigma_offsets(uint32_t w)
     return (__builtin_bit_cast(uint32_t, m) << 3) | (w & 0x80008000u);
 }
 
-// (g u) sigma for a table entry {hi, lo}: g u is exact in FP32 for BF16 g and
-// u (8 significant bits each); fma adds (g u) hi and RN((g u) lo) exactly and
-// rounds once, so the result is RN((g u) sigma) unless (g u) sigma lies
-// within about 2^-46 (relative) of a rounding midpoint. hi and lo are both
-// >= 0, so both terms carry the sign of g u: g u = -0 gives -0, and a g u
-// that overflowed to +-inf gives +-inf (a negative lo would add -0 to -0
-// as +0, or make inf - inf).
+// (g u) sigma for a pair entry {hi, lo}: g u is exact in FP32 for BF16 g and
+// u (8 significant bits each) unless it overflows or falls below 2^-126; fma
+// adds (g u) hi and RN((g u) lo) exactly and rounds once, so the result is
+// RN((g u) sigma) unless (g u) sigma lies within about 2^-46 (relative) of a
+// rounding midpoint, or is below 2^-100 in magnitude: there (g u) lo (about
+// 2^-24 of it) can fall below the normal range, and the result may be one
+// binary32 step (a subnormal step below 2^-126) from RN((g u) sigma). hi
+// and lo are both >= 0, so both terms carry the sign of g u: g u = -0 gives
+// -0, and a g u that overflowed to +-inf gives +-inf (which the caller
+// recomputes with swiglu_wide).
 __device__ __forceinline__ float times_sigma(float gu, float2 s)
 {
     return __builtin_fmaf(gu, s.x, gu * s.y);
+}
+
+// RN32(RN64(g u sigma)) with g u exact in binary64 (any BF16 g and u) and
+// sigma as a binary64: within about 2^-51 of RN32(g u sigma). The callers
+// use it for the marked entries (sigma from the wide table) and, with
+// sigma = hi + lo (exact in binary64), for pair entries whose FP32 product
+// overflowed.
+__device__ __forceinline__ float swiglu_wide(float g, float u, double sigma)
+{
+    return (float)(((double)g * (double)u) * sigma);
 }
 
 // ---- FP8 E4M3 ("fn") encode of a non-negative block scale -------------------
@@ -119,14 +149,18 @@ __device__ __forceinline__ RowScale row_scale(float gs)
     return r;
 }
 
-// Correctly rounded quotient a / b from rb = RN(1 / b): q0 = RN(a rb), then
-// one Newton/Markstein correction with the exact remainder. The remainder is
-// formed as q0 b - a and applied with -rb, which keeps the IEEE sign of a in
-// the result also when a is -0 or the quotient underflows. Checked
-// exhaustively on the CPU for every binary32 numerator mantissa against the
-// 8 E4M3 mantissas as divisors (the power-of-two global-scale case); in
-// general it is Markstein's theorem (rb within half an ulp of 1/b, q0
-// faithful, exact remainder).
+// Correctly rounded quotient a / b from a reciprocal rb of b: q0 = RN(a rb),
+// then one Newton/Markstein correction with the exact remainder. The
+// remainder is formed as q0 b - a and applied with -rb, which keeps the IEEE
+// sign of a in the result also when a is -0 or the quotient underflows.
+// Checked exhaustively, for quotients whose intermediates stay in the
+// normal binary32 range (the result then depends only on the two
+// significands):
+//   * rb = RN(1 / b) for every pair of binary32 significands (2^46 pairs, on
+//     the GPU against the remainder criterion of correct rounding);
+//   * rb = RN(1 / b) and both of its neighbours (a faithful reciprocal such
+//     as v_rcp_f32) for every numerator significand against the 8 E4M3
+//     significands as divisors (on the CPU against IEEE division).
 __device__ __forceinline__ float div_rn(float a, float b, float rb)
 {
     const float q0 = a * rb;
@@ -136,16 +170,20 @@ __device__ __forceinline__ float div_rn(float a, float b, float rb)
 
 // amax -> scale byte and element-quantizer constants.
 //   bsf = RN(amax / k), sf = E4M3(bsf), d = RN(decode(sf) * gs).
-// The element quotients need a reciprocal of d/2 for div_rn. When gs is a
-// power of two, d/2 has one of the 8 E4M3 mantissas, and for those divisors
-// the div_rn correction is exact for every numerator even when the
-// reciprocal is off by one ulp (checked exhaustively on the CPU), so the
-// faithful v_rcp_f32 is enough. Otherwise the reciprocal is the correctly
-// rounded IEEE division. The branch is uniform (gs is per row).
+// amax is first capped at 1024 k (an exact power-of-two multiple): every
+// amax above it has bsf >= 1024 and saturates to 448 anyway, and the cap
+// keeps the quotient finite for an infinite amax. rk = RN(1 / k) is an IEEE
+// division. The element quotients need a reciprocal of d/2. When gs is a
+// power of two, d/2 has an E4M3 significand, for which div_rn is exact even
+// with the faithful v_rcp_f32 as the reciprocal; otherwise the reciprocal is
+// the correctly rounded IEEE division. The branch is uniform (gs is per
+// row). Both hold for gs in [2^-64, 2^64], where every remainder stays in the
+// normal range.
 __device__ __forceinline__ BlockScale block_scale(float amax, const RowScale& rs)
 {
     BlockScale s;
-    const float bsf = div_rn(amax, rs.k, rs.rk);
+    const float a = __builtin_fminf(amax, 1024.0f * rs.k);
+    const float bsf = div_rn(a, rs.k, rs.rk);
     s.sf = fp8_e4m3_encode(bsf);
     const float d = fp8_e4m3_decode(s.sf) * rs.gs;
     s.half_d = 0.5f * d;
@@ -169,6 +207,26 @@ __device__ __forceinline__ float half_steps(float x, const BlockScale& s)
     return __builtin_rintf(div_rn(x, s.half_d, s.rcp));
 }
 
+// The 16 counts of a block. When amax / (d/2) may exceed 16 (a saturated
+// scale, or an infinite value), the values are first clamped to
+// [-16 d/2, 16 d/2] (v_med3_f32 returns x itself inside the range): every
+// such value has |s| > 6 and keeps its largest-magnitude code and its sign,
+// and no quotient overflows (an overflowed q0 would turn the correction into
+// inf - inf). amax * rcp is within 2 ulp of amax / (d/2), and 0 when d == 0.
+__device__ __forceinline__ void half_steps16(const float (&y)[16], float amax,
+                                             const BlockScale& s, float (&h)[16])
+{
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+        h[j] = half_steps(y[j], s);
+    if (amax * s.rcp > 16.0f) {
+        const float lim = 16.0f * s.half_d;
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+            h[j] = half_steps(__builtin_amdgcn_fmed3f(y[j], -lim, lim), s);
+    }
+}
+
 // Two signed half-step counts -> one byte of E2M1 codes (first value in the
 // low nibble) placed at byte `sel` of `word`. The convert divides by its
 // power-of-two scale (2 here, exact) and rounds to nearest even onto E2M1,
@@ -181,20 +239,25 @@ __device__ __forceinline__ uint32_t pack_e2m1(uint32_t word, float h0, float h1)
     return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, h0, h1, 2.0f, sel);
 }
 
-// 16 FP32 values -> 8 bytes of packed E2M1 codes (returned as uint2) and the
-// scale byte.
-__device__ __forceinline__ uint2 quantize16(const float (&y)[16], const RowScale& rs,
-                                            uint32_t& sf_out)
+// max |y_j| of a block (exact), NaN if some y_j is NaN (v_maximum3_f32
+// propagates NaN, unlike v_max3_f32).
+__device__ __forceinline__ float block_amax(const float (&y)[16])
 {
     float amax = 0.0f;
 #pragma unroll
     for (int j = 0; j < 16; ++j)
-        amax = fmaxf(amax, __builtin_fabsf(y[j]));
+        amax = __builtin_elementwise_maximum(amax, __builtin_fabsf(y[j]));
+    return amax;
+}
+
+// 16 FP32 values and their amax -> 8 bytes of packed E2M1 codes (returned
+// as uint2) and the scale byte.
+__device__ __forceinline__ uint2 quantize16(const float (&y)[16], float amax, const RowScale& rs,
+                                            uint32_t& sf_out)
+{
     const BlockScale s = block_scale(amax, rs);
     float h[16];
-#pragma unroll
-    for (int j = 0; j < 16; ++j)
-        h[j] = half_steps(y[j], s);
+    half_steps16(y, amax, s, h);
     uint32_t w0 = 0, w1 = 0;
     w0 = pack_e2m1<0>(w0, h[0], h[1]);
     w0 = pack_e2m1<1>(w0, h[2], h[3]);

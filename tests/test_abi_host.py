@@ -12,6 +12,7 @@ import torch
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "moe_nvfp4.h")
 CALIB_HEADER = os.path.join(ROOT, "include", "nvfp4_calib.h")
+DIVCHECK_HEADER = os.path.join(ROOT, "include", "nvfp4_divcheck.h")
 
 OK, INVALID, SHAPE, MISALIGNED = 0, 1, 2, 3
 
@@ -76,9 +77,24 @@ def test_calib_library_exports_its_header(lib):
     assert mix(A16, A16, 0, 0, None) == 0             # empty: no launch
 
 
+def test_divcheck_library_exports_its_header():
+    import ctypes as C
+    from moe_swiglu_epilogue_amd import build
+    names = _declared(DIVCHECK_HEADER)
+    assert names == ["nvfp4_divcheck"]
+    assert set(names) <= _exported(build.DIVCHECK_LIB)
+    fn = C.CDLL(build.DIVCHECK_LIB).nvfp4_divcheck
+    fn.argtypes = [C.c_uint32, C.c_uint32, C.c_int, C.c_void_p, C.c_void_p, C.c_void_p]
+    assert fn(0, 0, 0, A16, A16, None) == 1               # no divisors
+    assert fn(1 << 23, 1, 0, A16, A16, None) == 1         # first beyond the significands
+    assert fn((1 << 23) - 4, 5, 0, A16, A16, None) == 1   # range beyond them
+    assert fn(0, 1, 0, None, A16, None) == 1              # no counter
+    assert fn(0, 1, 0, A16, None, None) == 1              # no witness
+
+
 def test_header_compiles_as_c(tmp_path):
     src = tmp_path / "t.c"
-    src.write_text('#include "moe_nvfp4.h"\n#include "nvfp4_calib.h"\n'
+    src.write_text('#include "moe_nvfp4.h"\n#include "nvfp4_calib.h"\n#include "nvfp4_divcheck.h"\n'
                    'int main(void){return (int)NVFP4_SUCCESS;}\n')
     subprocess.run(["gcc", "-std=c11", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"),
                     "-I", "/opt/rocm/include", "-c", str(src), "-o", str(tmp_path / "t.o")],

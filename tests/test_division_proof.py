@@ -15,7 +15,12 @@ the correctly rounded division a / b:
   power of two): the correction still gives the correctly rounded quotient;
 * the sign of zero for +-0 numerators;
 * a large random sample of arbitrary divisor mantissas (general global
-  scales), where correctness rests on Markstein's theorem.
+  scales; every pair of significands is checked on the GPU by
+  test_gpu_division_exhaustive.py);
+* the remainder criterion that GPU check accepts quotients by, against IEEE
+  division: it accepts RN(a / b) and rejects both binary32 neighbours, for
+  random pairs and for quotients next to powers of two (where the gap below
+  is half the gap above).
 """
 import os
 import subprocess
@@ -34,6 +39,16 @@ static float div_rn(float a, float b, float rb) {
     float q0 = a * rb;
     float rem = fmaf(q0, b, -a);
     return fmaf(rem, -rb, q0);
+}
+/* the acceptance criterion of the GPU's exhaustive check (divcheck.hip) */
+static int correctly_rounded(float a, float b, float q) {
+    float r = fmaf(-q, b, a);
+    uint32_t qb = f2u(q);
+    int e = (int)(qb >> 23) - 127;
+    float half_gap = ldexpf(b, e - 24);
+    if ((qb & 0x7fffffu) == 0u && r < 0.0f) half_gap *= 0.5f;
+    float ar = fabsf(r);
+    return ar < half_gap || (ar == half_gap && (qb & 1u) == 0u);
 }
 int main(int argc, char** argv) {
     long bad = 0, n = 0;
@@ -80,7 +95,21 @@ int main(int argc, char** argv) {
             rbad += f2u(div_rn(a, bb, rbb)) != f2u(a / bb);
         }
     }
-    printf("%ld %ld %ld %ld\n", n, bad, rn_, rbad);
+    /* the criterion: accepts a / b, rejects its neighbours */
+    long cbad = 0, cn = 0;
+    srand(777);
+    for (long t = 0; t < 20000000; ++t) {
+        uint32_t ma = ((uint32_t)rand() ^ ((uint32_t)rand() << 15)) & 0x7fffffu;
+        uint32_t mb = ((uint32_t)rand() ^ ((uint32_t)rand() << 15)) & 0x7fffffu;
+        if (t % 4 == 0) ma = mb;                         /* quotient exactly 1 */
+        if (t % 4 == 1) ma = (mb + (rand() & 7)) & 0x7fffffu;   /* just above or below 1 */
+        float a = u2f((127u << 23) | ma), b = u2f((127u << 23) | mb), q = a / b;
+        cn += 3;
+        cbad += !correctly_rounded(a, b, q);
+        cbad += correctly_rounded(a, b, nextafterf(q, INFINITY));
+        cbad += correctly_rounded(a, b, nextafterf(q, 0.0f));
+    }
+    printf("%ld %ld %ld %ld %ld %ld\n", n, bad, rn_, rbad, cn, cbad);
     return 0;
 }
 """
@@ -95,7 +124,8 @@ def test_markstein_quotient_matches_ieee_division(tmp_path):
                     "-std=c11", str(c), "-o", str(exe), "-lm"], check=True)
     out = subprocess.run([str(exe), "256"], capture_output=True, text=True, check=True,
                          env={**os.environ, "OMP_NUM_THREADS": str(min(8, os.cpu_count() or 1))})
-    n, bad, rn, rbad = map(int, out.stdout.split())
+    n, bad, rn, rbad, cn, cbad = map(int, out.stdout.split())
     assert n == 8 * 3 * 3 * (1 << 23) * 3 * 2
     assert bad == 0, "exhaustive E4M3-mantissa check failed in %d cases" % bad
     assert rn > 0 and rbad == 0, "random-divisor check failed in %d of %d cases" % (rbad, rn)
+    assert cn == 60000000 and cbad == 0, "remainder criterion wrong in %d of %d cases" % (cbad, cn)

@@ -13,8 +13,14 @@ quotient) and a general one (the IEEE-division path).
 
 The fused path gets the same treatment for its SwiGLU: every finite BF16 gate
 value (both signs, zero and subnormals included: every entry of the kernel's
-sigmoid table and both clamped ends) times up values 1, -1, 0.5 and -0.75,
-each y checked against the oracle with the fused acceptance rules."""
+sigmoid table and both clamped ends) times up values of every size: 1, -1,
+0.5 and -0.75; 1e30 and -3e35 (so that gates far below -87, whose sigmoid is
+below the binary32 normal range, give SwiGLU values well inside it); the
+largest BF16 (g u then overflows FP32 for |g| >= 1, though y may not); and
+the smallest subnormal BF16 (products below the normal range). Each y is
+checked against the oracle with the fused acceptance rules."""
+from decimal import Decimal, localcontext
+
 import numpy as np
 import pytest
 import torch
@@ -69,7 +75,10 @@ def test_standalone_quantize_over_bf16_space(gs):
 
 def gate_sweep_input(inter=2048):
     gates = np.concatenate([np.arange(0, 0x7F80), np.arange(0x8000, 0xFF80)]).astype(np.uint16)
-    ups = np.array([0x3F80, 0xBF80, 0x3F00, 0xBF40], np.uint16)        # 1, -1, 0.5, -0.75
+    # 1, -1, 0.5, -0.75, 1e30, -3e35, the largest finite BF16, -2^-133
+    ups = np.concatenate([np.array([0x3F80, 0xBF80, 0x3F00, 0xBF40], np.uint16),
+                          W.to_bf16_bits(np.array([1e30, -3e35])),
+                          np.array([0x7F7F, 0x8001], np.uint16)])
     g = np.tile(gates, ups.size)
     u = np.repeat(ups, gates.size)
     n = -(-g.size // inter) * inter
@@ -97,15 +106,41 @@ def test_fused_swiglu_over_every_bf16_gate():
     assert rep.requant_mismatch == 0, rep
     assert rep.scale_mismatch == rep.scale_exempt, rep
     assert rep.code_mismatch == rep.code_exempt, rep
-    # with the sigmoid as a binary32 pair, every gate's bytes are the oracle's
+    # with the sigmoid to 2^-47 (binary64 for gates at or below -64), every
+    # gate's bytes are the oracle's
     assert rep.scale_mismatch == 0 and rep.code_mismatch == 0, rep
+    # and every y of magnitude 2^-100 or more is the oracle's, bit for bit,
+    # unless the exact g u sigma(g) lies within 2^-46 (relative) of the
+    # midpoint between the two values, which 60-digit arithmetic decides here
+    # for each such value (a handful on this sweep, at gates near +-2^-16,
+    # whose SwiGLU value sits next to a midpoint by construction); below
+    # 2^-100 the FP32 product (g u) lo of the sigmoid pair can fall below the
+    # normal range, so y may be one binary32 step away, which the SwiGLU rule
+    # allows
+    differ = y.view(np.uint32) != ry.view(np.uint32)
+    big = np.abs(ry) >= np.float32(2.0 ** -100)
+    odd = np.argwhere(differ & big)
+    say("every-gate sweep: %d of %d SwiGLU values differ from the oracle's, %d of them "
+        "of magnitude 2^-100 or more" % (differ.sum(), y.size, len(odd)))
+    assert len(odd) <= 32
+    gf = W.bf16_bits_to_f32(x)
+    for r, c in odd:
+        col = 16 * (c // 8) + c % 8
+        with localcontext() as ctx:
+            ctx.prec = 60
+            g, u = Decimal(float(gf[r, col])), Decimal(float(gf[r, col + 8]))
+            exact = g * u / (1 + (-g).exp())
+            mid = (Decimal(float(y[r, c])) + Decimal(float(ry[r, c]))) / 2
+            rel = abs(exact - mid) / abs(exact)
+        say("  g %r u %r: kernel %r oracle %r, exact value %.3g from their midpoint"
+            % (float(g), float(u), float(y[r, c]), float(ry[r, c]), float(rel)))
+        assert rel <= Decimal(2) ** -46
 
 
 def test_compact_swiglu_over_every_bf16_gate():
     """The compact BF16 SwiGLU pass (same sigmoid table, then round to BF16)
     over the same sweep: every output equals the oracle's BF16 rounding of
-    its SwiGLU, except within the SwiGLU tolerance of a BF16 midpoint (and
-    zeros below the tiny floor with matching sign)."""
+    its SwiGLU, except within the SwiGLU tolerance of a BF16 midpoint."""
     import moe_swiglu_epilogue_amd as M
     x = gate_sweep_input()
     say("compact swiglu over every finite BF16 gate:", x.shape)
@@ -115,4 +150,4 @@ def test_compact_swiglu_over_every_bf16_gate():
     got = out.view(torch.int16).cpu().numpy().view(np.uint16)
     rep = P.bf16_report(got, oracle.swiglu_bf16(x), oracle.swiglu(x))
     say("every-gate compact:", rep)
-    assert rep.mismatch == rep.exempt + rep.tiny, rep
+    assert rep.mismatch == rep.exempt, rep

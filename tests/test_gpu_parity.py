@@ -284,9 +284,100 @@ def test_fused_ragged_experts_and_dequant(M):
     P.assert_bytes_equal("ragged scales, every row", s, rsa)
     P.assert_bytes_equal("ragged packed, every row", p, rpa)
     del rpa, rsa
-    # dequant round trip: bit-exact against the oracle's dequant of the GPU bytes
-    rdq = oracle.dequantize(p[sel], s[sel], gs_rows[sel])
-    P.assert_bytes_equal("dequant", dq[sel].view(np.uint32), rdq.view(np.uint32))
+    # dequant round trip, every row: bit-exact against the oracle's dequant of
+    # the GPU bytes (equal to the oracle's own bytes, checked above)
+    say("oracle dequant over every ragged row")
+    rdq = oracle.dequantize(p, s, gs_rows)
+    P.assert_bytes_equal("dequant, every row", dq.view(np.uint32), rdq.view(np.uint32))
+
+
+# ---- more experts than the LDS expert table holds -------------------------------------
+@pytest.mark.parametrize("experts,empty,seed", [(1025, 100, 31), (1500, 300, 32), (4000, 1500, 33)])
+def test_many_experts_scalar_lookup(M, experts, empty, seed):
+    """Above 1024 experts the quantize kernels find each tile's expert by a
+    per-tile scalar binary search instead of the workgroup's LDS table, and
+    the dequantize always does: standalone quantize, fused quantize and
+    dequantize against the oracle's per-row scales, with empty experts
+    (including the first and the last) and a ragged row length (1040 values:
+    one full and one partial tile per row). The global-scale calls, whose
+    per-workgroup maxima live in LDS, reject that many experts."""
+    rows, cols = 6000, 1040
+    rng = np.random.default_rng(seed)
+    off = W.random_offsets(rows, experts, seed, empty=empty)
+    assert np.count_nonzero(np.diff(off) == 0) >= empty // 2
+    gs = (10.0 ** rng.uniform(-3, 1, experts)).astype(np.float32)
+    gs[::7] = np.float32(2.0) ** rng.integers(-8, 3, gs[::7].size).astype(np.float32)
+    gs_rows = oracle.rows_global_scale(gs, off, rows)
+    gst, offt = gs_tensor(gs), dev(off)
+    x = W.random_plain(rows, cols, seed, scale=3.0)
+    say("nvfp4_quantize", rows, cols, "experts", experts)
+    p, s = M.nvfp4_quantize(dev_bf16(x), gst, offt)
+    rp, rs = oracle.quantize_bf16(x, gs_rows)
+    P.assert_bytes_equal("scales", host(s), rs)
+    P.assert_bytes_equal("packed", host(p), rp)
+    say("nvfp4_dequantize", rows, cols, "experts", experts)
+    dq = host(M.nvfp4_dequantize(p, s, gst, offt))
+    P.assert_bytes_equal("dequant", dq.view(np.uint32), oracle.dequantize(rp, rs, gs_rows).view(np.uint32))
+    xf = W.random_fused(rows, cols, seed + 100, 2.0)
+    fused_check(M, xf, "fused, %d experts" % experts, gs=gs, off=off)
+    with pytest.raises(M.Nvfp4Error):
+        M.nvfp4_global_scale(dev_bf16(x), offt)
+
+
+# ---- extreme values: saturated scales, overflowing quotients, infinite SwiGLU --------
+def _huge_blocks(rows, cols, rng):
+    """BF16 values spread over the whole finite range, both signs, with
+    blocks of one huge value among small ones, zeros of both signs and the
+    largest finite BF16."""
+    x = rng.standard_normal((rows, cols)) * 10.0 ** rng.uniform(-5, 38.5, (rows, 1))
+    x = np.clip(x, -3.38e38, 3.38e38)
+    x[0, :16] = 0.0
+    x[0, 16:32] = -0.0
+    x[1, :16] = rng.standard_normal(16)
+    x[1, 5] = 3.38e38
+    x[2, 16:32] = -3.38e38
+    x[3, :16] = rng.standard_normal(16) * 1e-30
+    x[3, 7] = -2.0e38
+    return W.to_bf16_bits(x)
+
+
+@pytest.mark.parametrize("gs", [2.0 ** -60, 3.0e-17, 1.0, 2.0 ** 60],
+                         ids=["gs_2^-60", "gs_3e-17", "gs_1", "gs_2^60"])
+def test_standalone_saturated_and_overflowing_quotients(M, gs):
+    """Tiny global scales (down to the range's end, power of two and general)
+    with values up to the largest finite BF16: the block scales saturate at
+    448 and many quotients x / (d/2) lie beyond the binary32 range, which the
+    kernel clamps before dividing. Bit-exact against the oracle, which divides
+    in IEEE arithmetic (an infinite quotient gives the largest code)."""
+    rows, cols = 64, 512
+    x = _huge_blocks(rows, cols, np.random.default_rng(71))
+    g = np.float32(gs)
+    say("nvfp4_quantize extremes, gs", float(g))
+    p, s = M.nvfp4_quantize(dev_bf16(x), gs_tensor(g))
+    rp, rs = oracle.quantize_bf16(x, np.full(rows, g, np.float32))
+    P.assert_bytes_equal("scales", host(s), rs)
+    P.assert_bytes_equal("packed", host(p), rp)
+    assert (rs == 0x7E).any()
+
+
+@pytest.mark.parametrize("gs", [1.0, 2.0 ** -60, 3.0e-17], ids=["gs_1", "gs_2^-60", "gs_3e-17"])
+def test_fused_infinite_and_tiny_swiglu(M, gs):
+    """Gates and ups whose products leave the FP32 range (SwiGLU values that
+    are infinite, and finite ones behind an overflowed g u), gates far below
+    -87 (sigmoid below the binary32 range) and tiny products, with ordinary
+    and tiny global scales: the fused acceptance rules (no SwiGLU floor but
+    one subnormal step) and the re-quantize rule."""
+    rng = np.random.default_rng(72)
+    rows, inter = 64, 512
+    gvals = np.array([200.0, -200.0, 1.5, -1.5, -90.0, -100.0, -300.0, 40.0, 0.5, -0.0])
+    uvals = np.array([3.38e38, -3.38e38, 2.5e38, 1e30, -3e35, 1e-38, -2.0 ** -133, 1.0])
+    g = rng.choice(gvals, (rows, inter)) * rng.uniform(0.5, 1.0, (rows, inter))
+    u = rng.choice(uvals, (rows, inter)) * rng.uniform(0.5, 1.0, (rows, inter))
+    g[:8] = rng.standard_normal((8, inter))            # ordinary rows too
+    x = W.to_bf16_bits(W.interleave(g, u))
+    y = oracle.swiglu(x)
+    assert np.isinf(y).any() and (np.abs(y[np.isfinite(y)]) > 1e37).any()
+    fused_check(M, x, "infinite and tiny swiglu, gs %r" % gs, gs=np.float32(gs))
 
 
 # ---- global-scale pre-pass ----------------------------------------------------------------
@@ -360,9 +451,11 @@ def test_global_scale_empty_and_zero(M):
 
 
 def test_global_scale_clamped_range(M):
-    """Experts with tiny (~1e-30) and huge (~1e36) values get global scales
-    clamped to 2^-100 and 2^100, bit-exact against the oracle, and the
-    quantize with those scales stays bit-exact."""
+    """Product behaviour outside the quantizers' global-scale range: experts
+    with tiny (~1e-30) and huge (~1e36) values get the oracle's
+    RN32(amax / 2688) clamped to [2^-64, 2^64] (the range the kernels'
+    quotients are exact for), and the quantize with those scales is
+    bit-exact against the oracle fed the same scales."""
     rng = np.random.default_rng(61)
     rows, cols = 48, 256
     x = rng.standard_normal((rows, cols))
@@ -376,8 +469,9 @@ def test_global_scale_clamped_range(M):
     ref_am = oracle.group_amax(W.bf16_bits_to_f32(xb), off)
     ref_gs = oracle.expert_global_scale(ref_am)
     assert np.array_equal(am.view(np.uint32), ref_am.view(np.uint32))
-    assert np.array_equal(gs.view(np.uint32), ref_gs.view(np.uint32))
-    assert gs[0] == np.float32(2.0 ** -100) and gs[1] == np.float32(2.0 ** 100)
+    assert ref_gs[0] < 2.0 ** -64 and ref_gs[1] > 2.0 ** 64 and 2.0 ** -64 < ref_gs[2] < 2.0 ** 64
+    want = np.clip(ref_gs, np.float32(2.0 ** -64), np.float32(2.0 ** 64)).astype(np.float32)
+    assert np.array_equal(gs.view(np.uint32), want.view(np.uint32)), (gs, ref_gs)
     p, s = M.nvfp4_quantize(dev_bf16(xb), dev(gs), dev(off))
     rp, rs = oracle.quantize_bf16(xb, oracle.rows_global_scale(gs, off, rows))
     P.assert_bytes_equal("scales", host(s), rs)

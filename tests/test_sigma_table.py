@@ -1,8 +1,13 @@
 """The sigmoid table of the fused SwiGLU kernels (csrc/sigma_table.inc): it is
-what its generator writes, and each entry is the pair hi = RZ(sigma) (toward
-zero), lo = RN(sigma - hi) >= 0 of binary32 values for sigma(g) = 1 / (1 + e^-g),
-checked against float64 arithmetic, against the exact Taylor series of the
-sigmoid near 0 and against its exact properties. CPU only."""
+what its generator writes; each main entry for a gate above -64 is the pair
+hi = RZ(sigma) (toward zero), lo = RN(sigma - hi) >= 0 of normal binary32
+values for sigma(g) = 1 / (1 + e^-g), each main entry for a gate at or below
+-64 is the marker (+inf, +inf), and the wide table after the main one holds
+RN64(sigma) for those gates (the last, read for gates at or below -255,
+2^-1000).
+Checked against float64 arithmetic, against the exact Taylor series of the
+sigmoid near 0, against an exact-rational series for e^g at the binary64
+entries, and against the sigmoid's exact properties. CPU only."""
 import importlib.util
 import os
 import struct
@@ -22,22 +27,42 @@ def _gen():
     return mod
 
 
-def _table():
-    """(hi, lo) float32 arrays of 8192 entries: g > 0, then g < 0."""
+WIDE = 8192 - 256          # first binary64 entry: the gate -64
+
+
+def _words():
     bits = []
     with open(os.path.join(CSRC, "sigma_table.inc")) as f:
         for line in f:
             if line.startswith("0x"):
                 bits += [int(t.rstrip("u,"), 16) for t in line.split()]
-    t = np.array(bits, np.uint32).view(np.float32)
-    assert t.size == 2 * 8192
-    return t[0::2], t[1::2]
+    w = np.array(bits, np.uint32)
+    assert w.size == 2 * 8192 + 2 * 256
+    return w
 
 
-def _gates():
+def _table():
+    """(hi, lo) float32 arrays of the 7936 pair entries: g > 0 (0..4095), then
+    g < 0 down to the gate -63.75 (4096..7935)."""
+    t = _words().view(np.float32)
+    return t[0::2][:WIDE], t[1::2][:WIDE]
+
+
+def _wide():
+    """The wide table: 256 binary64 entries, gates -64 .. -255."""
+    return _words()[2 * 8192:].view(np.float64)
+
+
+def test_marked_entries():
+    """The main entries of the gates -64 .. -255 are (+inf, +inf)."""
+    w = _words()[2 * WIDE:2 * 8192]
+    assert np.all(w == 0x7F800000)
+
+
+def _gates(n=WIDE):
     a = ((((103 << 7) + np.arange(4096)).astype(np.uint32)) << 16).view(np.float32)
     a = a.astype(np.float64)
-    return np.concatenate([a, -a])
+    return np.concatenate([a, -a])[:n]
 
 
 def _nearest_binary32(q):
@@ -79,8 +104,7 @@ def test_table_against_float64():
     float64 value to within 2^-47."""
     hi, lo = _table()
     g = _gates()
-    with np.errstate(over="ignore"):
-        s64 = 1.0 / (1.0 + np.exp(-g))
+    s64 = 1.0 / (1.0 + np.exp(-g))
     near = s64.astype(np.float32)
     below = np.where(near.astype(np.float64) <= s64, near, np.nextafter(near, np.float32(0)))
     above = np.nextafter(below, np.float32(np.inf))
@@ -91,13 +115,13 @@ def test_table_against_float64():
     # the rest are small gates, where sigma = 1/2 + g/4 - g^3/48 + ... sits
     # next to a binary32 value by construction (the series test pins them),
     # and gates above about 33, where sigma is within 1e-14 of 1 (pinned below)
-    assert clear.sum() >= 7100
+    assert clear.sum() >= 6900
     assert np.array_equal(hi[clear], below[clear])
     # the pair: |hi + lo - sigma| <= 2^-48 sigma (lo rounded to 24 bits, lo
-    # below 2^-23 sigma) plus float64's error, plus one binary32 subnormal
-    # step where lo (for sigma below about 1e-29) reaches the bottom of the range
+    # below 2^-23 sigma) plus float64's error; both halves normal
     pair = hi.astype(np.float64) + lo.astype(np.float64)
-    assert np.all(np.abs(pair - s64) <= 2.0 ** -47 * s64 + 2.0 ** -149)
+    assert np.all(np.abs(pair - s64) <= 2.0 ** -47 * s64)
+    assert np.all(hi >= np.float32(2.0 ** -126)) and np.all((lo == 0) | (lo >= np.float32(2.0 ** -126)))
     # lo is the remainder: non-negative and below one ulp of hi
     assert np.all(lo >= 0) and not np.any(np.signbit(lo))
     assert np.all(lo.astype(np.float64) <= np.spacing(hi).astype(np.float64))
@@ -141,22 +165,67 @@ def test_table_exact_properties():
     assert np.all(np.diff(pos) >= 0) and np.all(np.diff(neg) <= 0)
     assert np.all(pos >= 0.5) and np.all(neg < 0.5) and np.all(neg >= 0)
     # sigma(g) + sigma(-g) = 1: to the pairs' accuracy, in exact arithmetic
-    for i in range(0, 4096, 37):
+    for i in range(0, WIDE - 4096, 37):
         s = (Fraction(float(hi[i])) + Fraction(float(lo[i])) + Fraction(float(hi[4096 + i]))
              + Fraction(float(lo[4096 + i])))
         assert abs(s - 1) <= Fraction(1, 2 ** 46), i
-    # the largest magnitudes: sigma(+255) = 1 - 1.8e-111 is 1 - 2^-24 plus lo =
-    # 2^-24; sigma(-255) (about 1.8e-111) is 0 in both halves
+    # the largest magnitude: sigma(+255) = 1 - 1.8e-111 is 1 - 2^-24 plus lo =
+    # 2^-24
     assert pos[-1] == 1.0 - 2.0 ** -24 and lo[4095] == np.float32(2.0 ** -24)
-    assert neg[-1] == 0.0 and lo[8191] == 0.0
-    # subnormal binary32 hi for g in (-103.3, -87.3), zero below
-    g = _gates()[4096:]
-    assert np.any((neg > 0) & (neg < 2.0 ** -126))
-    assert np.all(neg[g < -104.0] == 0.0)
     # sigma(1) = 1 / (1 + 1/e) = 0.7310585786300049, between the binary32
     # values 0x3f3b26a7 and 0x3f3b26a8: truncated, 0x3f3b26a7
     one = (127 - 103) * 128
     assert struct.pack("<f", np.float32(pos[one])) == struct.pack("<I", 0x3f3b26a7)
+    # the pair entries end at the gate -63.75 (BF16 0xC27F), the binary64 ones
+    # start at -64 (0xC280)
+    a = ((((103 << 7) + np.arange(4096)).astype(np.uint32)) << 16).view(np.float32)
+    assert a[WIDE - 4096 - 1] == np.float32(63.75) and a[WIDE - 4096] == np.float32(64.0)
+
+
+def _exp_neg(x: Fraction, terms: int = 400):
+    """e^-x for 0 <= x <= 256 as an exact rational with an error bound:
+    e^-x = (e^-(x/2^k))^(2^k), the inner value by its alternating Taylor
+    series (remainder below the first omitted term), then squared k times
+    (the relative error grows by at most a factor 2^k * (1 + err))."""
+    k = 9
+    y = x / 2 ** k                         # at most 1/2
+    s, t = Fraction(0), Fraction(1)
+    for n in range(1, 40):
+        s += t
+        t = t * (-y) / n
+    rel = abs(t) / s * 2                   # relative bound of the truncated series
+    for _ in range(k):
+        s = s * s
+        rel = 2 * rel + rel * rel
+    return s, rel
+
+
+def test_wide_entries_exact():
+    """The binary64 entries (gates -64 .. -254.x) are the binary64 values
+    nearest to sigma(g) = e^g / (1 + e^g), computed here from an
+    exact-rational series for e^-|g| (independent of the generator's decimal
+    arithmetic) wherever its error bound decides the rounding; the last entry
+    is 2^-1000."""
+    wide = _wide()
+    gates = -_gates(8192)[WIDE:]
+    assert gates[0] == 64.0 and gates[-1] == 255.0
+    assert wide[-1] == 2.0 ** -1000
+    decided = 0
+    for i in range(0, 255, 3):
+        e, rel = _exp_neg(Fraction(float(gates[i])))
+        sig = e / (1 + e)                   # sigma(-|g|)
+        got = Fraction(float(wide[i]))
+        ulp = Fraction(float(np.spacing(wide[i])))
+        # the entry is within half an ulp of sigma, up to the series' error
+        assert abs(got - sig) <= ulp / 2 + 2 * rel * sig, (i, float(gates[i]))
+        if abs(abs(got - sig) - ulp / 2) > 2 * rel * sig:
+            assert abs(got - sig) < ulp / 2, (i, float(gates[i]))
+            decided += 1
+    assert decided >= 80
+    # against float64: sigma(-x) = exp(-x) / (1 + exp(-x)) within 4 ulp
+    f64 = np.exp(-gates[:-1]) / (1.0 + np.exp(-gates[:-1]))
+    assert np.all(np.abs(wide[:-1] - f64) <= 4 * np.spacing(f64))
+    assert np.all(np.diff(wide[:-1]) < 0) and np.all(wide > 0)
 
 
 def test_large_gates():
