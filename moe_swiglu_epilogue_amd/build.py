@@ -26,6 +26,9 @@ FLAGS = [
     "-ffp-contract=off", "-fhip-fp32-correctly-rounded-divide-sqrt",
     # no packed FP32 (v_pk_*_f32) instructions in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # atomics stay as written: the tile queue's one-lane LDS claim must not be
+    # rewritten into a wave-wide form that waits for its result at once
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     "-Wall",
 ]
 
