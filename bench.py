@@ -16,7 +16,8 @@ in-repo read / copy kernels over the same input as HBM ceilings, and a kernel
 that moves the fused kernel's exact traffic mix (4 KB read, 576 B written
 per wave tile) without its compute; the ragged
 256-expert workload (pre-pass, quantize with per-expert scales, dequantize);
-the decode-shaped workload over 8 rotating buffer sets; the paged KV-cache
+the decode-shaped workload over 8 rotating buffer sets, with the read and
+traffic-mix ceilings at that size over the same rotation; the paged KV-cache
 write and read (65536 tokens x 8 heads x 128, 131072 slots); the two small
 cache-resident shapes (standalone 128 x 256, fused 512 x 4096) as launch
 rates; the MoE L1 grouped GEMM with the fused epilogue against the unfused
@@ -151,8 +152,16 @@ class GpuStateSampler:
         return self
 
     def mark_timed(self, on: bool):
-        """Tag the following samples as taken inside (or outside) the timed region."""
-        self.timed = on
+        """Tag the following samples as taken inside (or outside) the timed
+        region, and take one sample right at the boundary (the timed region
+        of a short run can end before the 5 ms sampler fires): the sample at
+        the start is tagged timed, the one at the end too."""
+        if on:
+            self.timed = True
+        if self.base:
+            self.samples.append(self._sample())
+        if not on:
+            self.timed = False
 
     def __exit__(self, *exc):
         self._stop.set()
@@ -466,11 +475,43 @@ def secondary_figures(M, W, x, packed, scales, args, dev):
             xi, pi, si = sets[k[0] % 8]
             k[0] += 1
             M.swiglu_nvfp4_quantize(xi, packed=pi, scales=si)
-        sec["decode_shaped"] = measure(
+        dec = measure(
             "decode-shaped swiglu_nvfp4_quantize", rotating, dr * di * BYTES_PER_ELEM, dr * di,
             max(st, 80), ms, {"shape": [dr, 2 * di], "note": "8 rotating input/output sets",
                               "input_sha256": decode_sha})
-        del sets
+        dec["graph_ms"] = round(graph_ms(rotating, launches=80, replays=10), 5)
+        # the HBM ceilings at this size, over the same 8 rotating inputs: the
+        # read kernel and the traffic-mix kernel (the fused kernel's 4 KB read
+        # and 576 B written per wave tile, without compute)
+        calib = load_calib()
+        stream = torch.cuda.current_stream().cuda_stream
+        nb = dr * 2 * di * 2
+        scratch = torch.empty(8192 * 16, dtype=torch.uint8, device=dev)
+        mix_out = [torch.empty(nb // 4096 * 576, dtype=torch.uint8, device=dev) for _ in range(8)]
+
+        def read_rot(blocks):
+            xi = sets[k[0] % 8][0]
+            k[0] += 1
+            checked(calib.nvfp4_calib_read(xi.data_ptr(), scratch.data_ptr(), nb, blocks, stream))
+
+        def mix_rot():
+            i = k[0] % 8
+            k[0] += 1
+            checked(calib.nvfp4_calib_mix(sets[i][0].data_ptr(), mix_out[i].data_ptr(), nb, 0,
+                                          stream))
+        best = None
+        for blocks in (1024, 1536, 4096):
+            r = measure("decode-size read ceiling, %d workgroups" % blocks,
+                        lambda: read_rot(blocks), nb, nb // 2, max(st, 80), ms, {"workgroups": blocks})
+            best = r if best is None or r["GB_s"] > best["GB_s"] else best
+        mix = measure("decode-size traffic-mix ceiling", mix_rot, nb + nb // 4096 * 576, nb // 2,
+                      max(st, 80), ms)
+        dec["read_ceiling"] = best
+        dec["mix_ceiling"] = mix
+        dec["frac_of_mix_ceiling"] = round(dec["GB_s"] / mix["GB_s"], 4)
+        dec["frac_of_read_ceiling"] = round(dec["GB_s"] / best["GB_s"], 4)
+        sec["decode_shaped"] = dec
+        del sets, scratch, mix_out
     if "small" in want:
         # the two small shapes: 128 x 256 standalone (84 KB moved) and
         # 512 x 4096 fused (4.8 MB). Both live in the Infinity Cache and a

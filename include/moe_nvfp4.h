@@ -121,15 +121,14 @@ nvfp4_status_t nvfp4_quantize(const uint16_t *x, int64_t rows, int64_t cols,
  * packed[rows][inter/2], scales[rows][inter/16] and, when swiglu_out is not
  * NULL, the FP32 y values [rows][inter] (a debug output: the quantized bytes
  * are the same with or without it). Each y is the binary32 rounding of the
- * exact gate * up * sigmoid(gate), for every finite BF16 gate and up, except:
- * where that value lies within about 2^-46 (relative) of a rounding
- * midpoint, or below 2^-100 in magnitude, it may be the neighbouring binary32
- * value (one subnormal step below 2^-126); for |gate| < 2^-24,
- * sigmoid(+-2^-24) stands for sigmoid(gate) (less than 2^-26 away). Gates at
- * or below -64 (sigmoid leaves the binary32 range from -87.3 down) and
- * products gate * up beyond the FP32 range take a binary64 path, within
- * about 2^-51 of a midpoint. y is never NaN; it is +-inf only where the
- * exact value rounds to it.
+ * exact gate * up * sigmoid(gate), for every finite BF16 gate and up, except
+ * where that value lies within about 2^-52 (relative) of a rounding
+ * midpoint, and where |gate * up| < 2^-126: there y may be the neighbouring
+ * value, one subnormal step (2^-149) away. sigmoid comes from a binary64
+ * table of every BF16 gate's value; for |gate| < 2^-24 its entry for
+ * +-2^-24 stands in (less than 2^-26 away), which gives the same y. y is
+ * never NaN for finite inputs; it is +-inf only where the exact value
+ * rounds to it.
  */
 nvfp4_status_t swiglu_nvfp4_quantize(const uint16_t *gate_up, int64_t rows,
                                      int64_t inter, int64_t ld_in,

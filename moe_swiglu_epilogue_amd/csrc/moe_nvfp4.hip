@@ -222,61 +222,53 @@ struct FusedBlock {
     // the prefill shape, 12 or 16 waves per CU are 4-6% slower and 4 waves
     // per CU 25% slower.
     static constexpr int kWaves = 8;
-    static constexpr int kBlocksPerCU = 1;   // 66 KB sigma table + 8 x 4.25 KB staging
+    static constexpr int kBlocksPerCU = 1;   // 64 KB sigma table + 8 x 4.25 KB staging
     static constexpr bool kSigmaTable = true;
+    // element quotients: guarded fast path (full-significand FP32 values)
+    static constexpr bool kFastQuotient = true;
     // Consecutive tiles per wave with wide stores (their scale bytes leave
     // as one piece). Measured on the prefill shape: 2 and 4 are 1.5-1.7%
     // slower than 1 and 8 is 6% slower; the walk's read order matters more
     // here than the size of the scale pieces.
     static constexpr int kScaleGroup = 1;
     // The block's 16 values y = silu(gate) * up = (gate * up) * sigma(gate)
-    // and their largest magnitude, with sigma from the table in LDS. All 16
+    // and their largest magnitude, with sigma from the table in LDS: all 16
     // table reads are issued before the first product, so that their
-    // latencies overlap. The common path is the binary32 pair product
-    // (times_sigma). Its amax (NaN-propagating) is finite unless the block
-    // holds a gate at or below -64, whose marked entry makes the product
-    // +-inf (or NaN for g u = 0), or a product g u beyond the FP32 range
-    // (+-inf; only gates or ups of magnitude near 2^64 and beyond make one).
-    // Such blocks take the exact binary64 product for every value instead
-    // (swiglu_wide; lanes diverge, waves without such a block skip it), so
-    // the common path pays one compare for both cases.
+    // latencies overlap. Each value is swiglu_product of the binary32 g u.
+    // Its amax (NaN-propagating) is finite unless some g u left the binary32
+    // range (only gates or ups of magnitude near 2^64 and beyond make one)
+    // or an input is not finite; such blocks take swiglu, with g u in
+    // binary64, for every value (lanes diverge; waves without such a block
+    // skip it).
     __device__ static __forceinline__ float block(const u32x4 (&c)[4], float (&y)[16],
                                                   const uint8_t* sig)
     {
         const uint32_t gw[8] = {c[0].x, c[0].y, c[0].z, c[0].w, c[2].x, c[2].y, c[2].z, c[2].w};
         const uint32_t uw[8] = {c[1].x, c[1].y, c[1].z, c[1].w, c[3].x, c[3].y, c[3].z, c[3].w};
-        float2 e[16];
-        uint32_t o[8];
+        double e[16];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            o[i] = nvfp4::sigma_offsets(gw[i]);
+            uint32_t o = nvfp4::sigma_offsets(gw[i]);
             // keep o whole: one shift-or builds it, then one mask and one
             // shift split it (the compiler would otherwise rebuild each half)
-            asm("" : "+v"(o[i]));
-            e[2 * i] = *reinterpret_cast<const float2*>(sig + (o[i] & 0xffffu));
-            e[2 * i + 1] = *reinterpret_cast<const float2*>(sig + (o[i] >> 16));
+            asm("" : "+v"(o));
+            e[2 * i] = *reinterpret_cast<const double*>(sig + (o & 0xffffu));
+            e[2 * i + 1] = *reinterpret_cast<const double*>(sig + (o >> 16));
         }
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            y[2 * i] = nvfp4::times_sigma(nvfp4::bf16_lo(gw[i]) * nvfp4::bf16_lo(uw[i]), e[2 * i]);
-            y[2 * i + 1] = nvfp4::times_sigma(nvfp4::bf16_hi(gw[i]) * nvfp4::bf16_hi(uw[i]),
-                                              e[2 * i + 1]);
+            y[2 * i] = nvfp4::swiglu_product(nvfp4::bf16_lo(gw[i]) * nvfp4::bf16_lo(uw[i]),
+                                             e[2 * i]);
+            y[2 * i + 1] = nvfp4::swiglu_product(nvfp4::bf16_hi(gw[i]) * nvfp4::bf16_hi(uw[i]),
+                                                 e[2 * i + 1]);
         }
         float amax = nvfp4::block_amax(y);
         if (!(amax < __builtin_inff())) {
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const uint32_t off = h ? o[i] >> 16 : o[i] & 0xffffu;
-                    const double sigma =
-                        off >= nvfp4::kSigWideOffset
-                            ? *reinterpret_cast<const double*>(sig + off + nvfp4::kSigWideShift)
-                            : (double)e[2 * i + h].x + (double)e[2 * i + h].y;
-                    const float g = h ? nvfp4::bf16_hi(gw[i]) : nvfp4::bf16_lo(gw[i]);
-                    const float u = h ? nvfp4::bf16_hi(uw[i]) : nvfp4::bf16_lo(uw[i]);
-                    y[2 * i + h] = nvfp4::swiglu_wide(g, u, sigma);
-                }
+                y[2 * i] = nvfp4::swiglu(nvfp4::bf16_lo(gw[i]), nvfp4::bf16_lo(uw[i]), e[2 * i]);
+                y[2 * i + 1] = nvfp4::swiglu(nvfp4::bf16_hi(gw[i]), nvfp4::bf16_hi(uw[i]),
+                                             e[2 * i + 1]);
             }
             amax = nvfp4::block_amax(y);
         }
@@ -289,6 +281,8 @@ struct PlainBlock {
     static constexpr int kWaves = 4;
     static constexpr int kBlocksPerCU = 3;   // 12 waves per CU: measured best (8: -9%, 24: -7%)
     static constexpr bool kSigmaTable = false;
+    // element quotients: exact path only (BF16 values often sit on a tie)
+    static constexpr bool kFastQuotient = false;
     // 128-byte scale pieces: 1.5% faster than 1 tile on 65536 x 3072
     // (4 tiles: level with 1; 8 tiles: 3% slower).
     static constexpr int kScaleGroup = 2;
@@ -484,19 +478,16 @@ struct ExpertBatch {
 };
 
 // sigma(g) = 1 / (1 + e^-g) for the table's gates (generated by
-// gen_sigma_table.py with 150-digit arithmetic): the main table, two 32-bit
-// words per entry (a binary32 pair {RZ(sigma), RN(sigma - hi)}, or +inf, +inf
-// for the last kSigWide negative entries), positive magnitudes m = 0 ..
-// kSigSpan - 1, then the negative ones; then the wide table, kSigWide binary64
-// values for the marked gates, low word first. The LDS table is a plain copy
-// of it.
+// gen_sigma_table.py with 150-digit arithmetic): one binary64 per entry, low
+// word first, positive magnitudes m = 0 .. kSigSpan - 1, then the negative
+// ones. The LDS table is a plain copy of it.
 __device__ const uint32_t kSigmaBits[] __attribute__((aligned(16))) = {
 #include "sigma_table.inc"
 };
-static_assert(sizeof(kSigmaBits) == nvfp4::kSigFloats * 4, "main and wide tables");
+static_assert(sizeof(kSigmaBits) == nvfp4::kSigFloats * 4, "one binary64 per entry");
 
 // Fills the workgroup's sigmoid table in LDS (fused input only) from
-// kSigmaBits: 66 KB, eight or nine 16-byte loads per thread, served by L2
+// kSigmaBits: 64 KB, eight 16-byte loads per thread, served by L2
 // after the first workgroups. Every wave of the workgroup takes part, so all
 // of them reach the barrier.
 template <class Block>
@@ -581,7 +572,7 @@ __global__ __launch_bounds__(Block::kWaves * kWave) void quantize_tiles_kernel(
             rs = nvfp4::row_scale(nvfp4::row_global_scale(gs, offsets, num_experts, t.row));
         }
         uint32_t sf;
-        const uint2 q = nvfp4::quantize16(y, amax, rs, sf);
+        const uint2 q = nvfp4::quantize16<Block::kFastQuotient>(y, amax, rs, sf);
         if constexpr (kWide)
             store_tile_outputs_grouped<G>(reinterpret_cast<uint8_t*>(lds),
                                           reinterpret_cast<uint8_t*>(win[wave]), q, sf, t,
@@ -656,7 +647,7 @@ __global__ __launch_bounds__(PlainBlock::kWaves * kWave) void quantize_paged_ker
         Tile o = t;
         o.row = keep ? (int)slot : 0;
         uint32_t sf;
-        const uint2 q = nvfp4::quantize16(y, amax, rs, sf);
+        const uint2 q = nvfp4::quantize16<PlainBlock::kFastQuotient>(y, amax, rs, sf);
         store_tile_outputs<kWide>(reinterpret_cast<uint8_t*>(stage[wave]), q, sf, o, b, lane, geo,
                                   packed, scales, keep);
     });
@@ -670,19 +661,22 @@ __global__ __launch_bounds__(FusedBlock::kWaves * kWave) void swiglu_bf16_kernel
     constexpr int kWaves = Block::kWaves;
     __shared__ u32x4 stage[kWaves][kStageSlots(Block::P)];
     __shared__ __attribute__((aligned(16))) float sig[nvfp4::kSigFloats];
+    __shared__ int queue;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = uniform(threadIdx.x / kWave);
     u32x4* lds = stage[wave];
     const int tile = blockIdx.x * kWaves + wave;
     auto setup = [&]() {
         fill_sigma_table<Block>(sig);
+        if (threadIdx.x == 0)
+            queue = kWaves;
         __syncthreads();
     };
     if (tile >= geo.tiles) {
         setup();
         return;
     }
-    StaticWalk walk{(int)gridDim.x * kWaves};
+    WorkgroupQueue<kWaves> walk{&queue, (int)gridDim.x * kWaves, lane, 0};
     walk_tiles<Block>(in, ld_in, geo, tile, walk, lane, lds,
                       reinterpret_cast<const uint8_t*>(sig), setup,
                       [&](int, const Tile& t, int b, const float (&y)[16], float) {
@@ -744,16 +738,22 @@ __global__ __launch_bounds__(Block::kWaves * kWave) void amax_tiles_kernel(
     __shared__ __attribute__((aligned(16))) float sig[Block::kSigmaTable ? nvfp4::kSigFloats : 1];
     __shared__ uint32_t part[kMaxScaleGroups];
     __shared__ ExpertTable tab;
+    __shared__ int queue;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = uniform(threadIdx.x / kWave);
     const int tile = blockIdx.x * kWaves + wave;
     const int stride = gridDim.x * kWaves;
+    // the SwiGLU pre-pass without experts shares its tiles through the LDS
+    // queue, as the fused quantize does
+    const bool queued = Block::kSigmaTable && offsets == nullptr;
     auto setup = [&]() {
         fill_sigma_table<Block>(sig);
         for (int i = threadIdx.x; i < groups; i += kWaves * kWave)
             part[i] = 0u;
         if (offsets != nullptr)
             fill_expert_table<kWaves * kWave>(tab, offsets, nullptr, groups);
+        if (threadIdx.x == 0)
+            queue = kWaves;
         __syncthreads();
     };
     if (tile >= geo.tiles)
@@ -771,10 +771,7 @@ __global__ __launch_bounds__(Block::kWaves * kWave) void amax_tiles_kernel(
             if (lane == 0)
                 atomicMax(&part[cur], __float_as_uint(m));
         };
-        StaticWalk walk{stride};
-        walk_tiles<Block>(in, ld_in, geo, tile, walk, lane, stage[wave],
-                          reinterpret_cast<const uint8_t*>(sig), setup,
-                          [&](int tile_index, const Tile&, int, const float (&)[16], float amax) {
+        auto body = [&](int tile_index, const Tile&, int, const float (&)[16], float amax) {
             int e = 0;
             if (offsets != nullptr) {
                 const int j = n & (kWave - 1);
@@ -790,7 +787,16 @@ __global__ __launch_bounds__(Block::kWaves * kWave) void amax_tiles_kernel(
                 run = 0.0f;
             }
             run = fmaxf(run, amax);
-        });
+        };
+        if (queued) {
+            WorkgroupQueue<kWaves> walk{&queue, stride, lane, 0};
+            walk_tiles<Block>(in, ld_in, geo, tile, walk, lane, stage[wave],
+                              reinterpret_cast<const uint8_t*>(sig), setup, body);
+        } else {
+            StaticWalk walk{stride};
+            walk_tiles<Block>(in, ld_in, geo, tile, walk, lane, stage[wave],
+                              reinterpret_cast<const uint8_t*>(sig), setup, body);
+        }
         flush();
     }
     __syncthreads();

@@ -6,10 +6,10 @@
 // listing the quantization primitives and their five fixes).
 //
 // Every function here reproduces the binary32 definition of the method
-// exactly (bit for bit), except the SwiGLU products through the sigmoid
-// table (times_sigma, swiglu_wide), which are the binary32 rounding of
-// g * u * sigmoid(g) except within about 2^-46 (relative) of a rounding
-// midpoint, and within one binary32 step of it below 2^-100.
+// exactly (bit for bit), except the SwiGLU product through the sigmoid table
+// (swiglu_product, swiglu), which is the binary32 rounding of
+// g * u * sigmoid(g) except within about 2^-52 (relative) of a rounding
+// midpoint, and within one subnormal step when |g u| < 2^-126.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -25,36 +25,23 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 // A BF16 gate has 65536 values; sigma(g) = 1 / (1 + e^-g) only varies in FP32
 // for 2^-24 <= |g| < 256. The table holds sigma for every BF16 magnitude in
 // that range (exponent field 103..134, all 128 mantissas: kSigSpan values)
-// and both signs, 8 bytes per entry. Positive gates use entries
-// [0, kSigSpan), negative ones [kSigSpan, 2 kSigSpan): kSigSpan * 8 = 32768
-// is bit 15 of a BF16 half-word, so the sign bit serves as the sign's byte
-// offset where it stands. Magnitudes below the range read the first entry
-// (sigma = 1/2 +- 2^-26 +- ... there), magnitudes above it the last.
-// Main table entries (gen_sigma_table.py):
-//   * gates above -64: a pair of binary32, hi = sigma rounded toward zero and
-//     lo = RN(sigma - hi) >= 0, both normal (hi + lo carries sigma to about
-//     2^-47): times_sigma below;
-//   * gates at or below -64 (the last kSigWide negative entries): the pair
-//     (+inf, +inf), a marker: from -87.3 down sigma leaves the binary32
-//     normal range (it reaches about 2^-368 at -255), so the pair product is
-//     replaced by swiglu_wide with sigma from the wide table that follows the
-//     main one (kSigWide binary64 values, byte offset of an entry = its main
-//     offset + kSigWideShift). The last wide entry, read for every gate at or
-//     below -255, holds 2^-1000, which makes the product a zero with the sign
-//     of g u there, as the exact value rounds.
-// The entries are computed at build time and copied into LDS once per
+// and both signs, one binary64 RN64(sigma) per entry (gen_sigma_table.py).
+// Positive gates use entries [0, kSigSpan), negative ones [kSigSpan,
+// 2 kSigSpan): kSigSpan * 8 = 32768 is bit 15 of a BF16 half-word, so the
+// sign bit serves as the sign's byte offset where it stands. Magnitudes
+// below the range read the first entry (sigma = 1/2 +- 2^-26 there, and
+// y = (g u) / 2 exactly after rounding for every smaller gate), magnitudes
+// above it the last. binary64 holds sigma as a normal number down to gate
+// -255 (about 2^-368), far below the binary32 range that sigma leaves from
+// -87.3 down; the last negative entry, read for every gate at or below -255,
+// holds 2^-1000, which makes the product a zero with the sign of g u there,
+// as the exact value rounds. The entries are copied into LDS once per
 // workgroup; a lookup then replaces exp and rcp per element.
 constexpr uint32_t kSigLo = 103u << 7;
 constexpr uint32_t kSigHi = (134u << 7) | 127u;
 constexpr int kSigSpan = (int)(kSigHi - kSigLo + 1);   // 4096
-constexpr int kSigWide = 256;                           // gates -64 .. -255
-constexpr int kSigFloats = 4 * kSigSpan + 2 * kSigWide; // 16896 32-bit words (66 KB)
-// main byte offset (as produced by sigma_offsets) of the first marked entry
-constexpr uint32_t kSigWideOffset = 0x8000u + 8u * (uint32_t)(kSigSpan - kSigWide);
-// wide byte offset = main byte offset + kSigWideShift (wide table at 64 KB)
-constexpr uint32_t kSigWideShift = 4u * 4u * (uint32_t)kSigSpan - kSigWideOffset;
+constexpr int kSigFloats = 4 * kSigSpan;               // 16384 32-bit words (64 KB)
 static_assert(kSigSpan * 8 == 0x8000, "sign bit is the offset of the negative half");
-static_assert(kSigWideOffset == 0xF800u, "gate -64 = BF16 0xC280 starts the marked entries");
 
 // Byte offsets of the table entries for the two BF16 gates of w, in the
 // matching halves of the result. Both halves are done at once in packed
@@ -72,27 +59,25 @@ __device__ __forceinline__ uint32_t sigma_offsets(uint32_t w)
     return (__builtin_bit_cast(uint32_t, m) << 3) | (w & 0x80008000u);
 }
 
-// (g u) sigma for a pair entry {hi, lo}: g u is exact in FP32 for BF16 g and
-// u (8 significant bits each) unless it overflows or falls below 2^-126; fma
-// adds (g u) hi and RN((g u) lo) exactly and rounds once, so the result is
-// RN((g u) sigma) unless (g u) sigma lies within about 2^-46 (relative) of a
-// rounding midpoint, or is below 2^-100 in magnitude: there (g u) lo (about
-// 2^-24 of it) can fall below the normal range, and the result may be one
-// binary32 step (a subnormal step below 2^-126) from RN((g u) sigma). hi
-// and lo are both >= 0, so both terms carry the sign of g u: g u = -0 gives
-// -0, and a g u that overflowed to +-inf gives +-inf (which the caller
-// recomputes with swiglu_wide).
-__device__ __forceinline__ float times_sigma(float gu, float2 s)
+// The SwiGLU value from gu = RN32(g u) and the binary64 sigma:
+// RN32(RN64(gu sigma)). g u of two BF16 numbers (8 significant bits each) is
+// exact in binary32 for 2^-126 <= |g u| < 2^128; then the only errors before
+// the final rounding are that of sigma (2^-53 relative) and of the binary64
+// product, and the result is RN32(g u sigma) unless that lies within about
+// 2^-52 (relative) of a binary32 rounding midpoint. Below 2^-126, gu is off
+// by at most 2^-150 and so is the product (sigma < 1): the result is then
+// within one subnormal step (2^-149) of RN32(g u sigma). A g u beyond the
+// binary32 range is +-inf here (the callers redo those with swiglu). g u =
+// -0 gives -0; the table never holds a zero sigma.
+__device__ __forceinline__ float swiglu_product(float gu, double sigma)
 {
-    return __builtin_fmaf(gu, s.x, gu * s.y);
+    return (float)((double)gu * sigma);
 }
 
-// RN32(RN64(g u sigma)) with g u exact in binary64 (any BF16 g and u) and
-// sigma as a binary64: within about 2^-51 of RN32(g u sigma). The callers
-// use it for the marked entries (sigma from the wide table) and, with
-// sigma = hi + lo (exact in binary64), for pair entries whose FP32 product
-// overflowed.
-__device__ __forceinline__ float swiglu_wide(float g, float u, double sigma)
+// RN32(RN64(RN64(g u) sigma)) with g u formed in binary64, where it is exact
+// for any BF16 g and u (|g u| < 2^256): the rounding of swiglu_product at
+// every magnitude, infinite and NaN inputs following IEEE.
+__device__ __forceinline__ float swiglu(float g, float u, double sigma)
 {
     return (float)(((double)g * (double)u) * sigma);
 }
@@ -207,23 +192,58 @@ __device__ __forceinline__ float half_steps(float x, const BlockScale& s)
     return __builtin_rintf(div_rn(x, s.half_d, s.rcp));
 }
 
-// The 16 counts of a block. When amax / (d/2) may exceed 16 (a saturated
-// scale, or an infinite value), the values are first clamped to
+// Largest distance of a fast quotient from its nearest integer that
+// half_steps16 accepts: 2^-17 short of a half (a possible tie).
+constexpr float kTieGuard = 0.5f - 0x1p-17f;
+
+// The 16 counts of a block. Fast path: q0 = RN(y rcp), one product in place
+// of the correctly rounded q = 2y/d. rcp is within one ulp of 2/d and q0 adds
+// one rounding, so |q0 - RN(q)| <= |q| 2^-22 (both in the normal range; a q0
+// below it is a zero count on both sides, with the sign of y):
+//   * for |q| < 16 that is below 2^-18, so when q0 lies more than 2^-17 from
+//     every half-integer, RN(q) lies strictly on the same side of each of
+//     them, and rint(q0) == rint(RN(q)), sign included;
+//   * for |q| >= 16 both counts are at least 15 in magnitude, with the sign
+//     of y, and the E2M1 convert saturates them to the same code.
+// So the fast counts are taken when every |q0 - rint(q0)| of the block is
+// below kTieGuard. Otherwise (a value near a possible tie, or a non-finite
+// q0: an infinite value, or an overflowed product) the block takes the exact
+// path. The fast path pays for FP32 values with full significands (SwiGLU
+// products, GEMM accumulators), whose quotients come near a half-integer
+// about 2^-16 of the time; BF16 values (8 significant bits) over E4M3
+// divisors land exactly on one for a few percent of elements, so their
+// callers ask for the exact path alone (kFast = false). The exact path:
+// div_rn per value, and when amax / (d/2) may exceed 16 (a saturated
+// scale, or an infinite value) the values are first clamped to
 // [-16 d/2, 16 d/2] (v_med3_f32 returns x itself inside the range): every
 // such value has |s| > 6 and keeps its largest-magnitude code and its sign,
 // and no quotient overflows (an overflowed q0 would turn the correction into
-// inf - inf). amax * rcp is within 2 ulp of amax / (d/2), and 0 when d == 0.
+// inf - inf). amax * rcp is within 2 ulp of amax / (d/2), and 0 when d == 0
+// (rcp == 0 makes every count +-0 on both paths).
+template <bool kFast>
 __device__ __forceinline__ void half_steps16(const float (&y)[16], float amax,
                                              const BlockScale& s, float (&h)[16])
 {
+    float far = __builtin_inff();
+    if constexpr (kFast) {
+        far = 0.0f;
 #pragma unroll
-    for (int j = 0; j < 16; ++j)
-        h[j] = half_steps(y[j], s);
-    if (amax * s.rcp > 16.0f) {
-        const float lim = 16.0f * s.half_d;
+        for (int j = 0; j < 16; ++j) {
+            const float q0 = y[j] * s.rcp;
+            h[j] = __builtin_rintf(q0);
+            far = __builtin_elementwise_maximum(far, __builtin_fabsf(q0 - h[j]));
+        }
+    }
+    if (!(far < kTieGuard)) {
 #pragma unroll
         for (int j = 0; j < 16; ++j)
-            h[j] = half_steps(__builtin_amdgcn_fmed3f(y[j], -lim, lim), s);
+            h[j] = half_steps(y[j], s);
+        if (amax * s.rcp > 16.0f) {
+            const float lim = 16.0f * s.half_d;
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+                h[j] = half_steps(__builtin_amdgcn_fmed3f(y[j], -lim, lim), s);
+        }
     }
 }
 
@@ -251,13 +271,14 @@ __device__ __forceinline__ float block_amax(const float (&y)[16])
 }
 
 // 16 FP32 values and their amax -> 8 bytes of packed E2M1 codes (returned
-// as uint2) and the scale byte.
+// as uint2) and the scale byte; kFast as in half_steps16.
+template <bool kFast>
 __device__ __forceinline__ uint2 quantize16(const float (&y)[16], float amax, const RowScale& rs,
                                             uint32_t& sf_out)
 {
     const BlockScale s = block_scale(amax, rs);
     float h[16];
-    half_steps16(y, amax, s, h);
+    half_steps16<kFast>(y, amax, s, h);
     uint32_t w0 = 0, w1 = 0;
     w0 = pack_e2m1<0>(w0, h[0], h[1]);
     w0 = pack_e2m1<1>(w0, h[2], h[3]);

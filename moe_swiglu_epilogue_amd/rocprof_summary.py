@@ -62,10 +62,41 @@ def stats(args):
         lines.append("%-40s %6s %12.3f %12.3f %12.3f %7.2f" % (
             _short(r["Name"])[:40], r["Calls"], float(r["AverageNs"]) / 1e3,
             float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
+    if args.clusters:
+        lines += ["", "duration clusters of %s (calls sorted by duration, split where one is"
+                  " more than %.1fx the one before)" % (args.clusters, args.gap),
+                  "%-12s %6s %12s %12s %12s %12s" % ("cluster", "calls", "avg_us", "p50_us",
+                                                     "min_us", "max_us")]
+        for k, c in enumerate(_clusters(args.dir, args.clusters, args.gap)):
+            lines.append("%-12d %6d %12.3f %12.3f %12.3f %12.3f" % (
+                k, len(c), statistics.fmean(c), statistics.median(c), c[0], c[-1]))
     text = "\n".join(lines) + "\n"
     with open(args.out, "w") as f:
         f.write(text)
     print(text)
+
+
+def _clusters(dir_, kernel, gap):
+    """Durations (us) of one kernel's dispatches from the kernel trace, sorted
+    and split into groups wherever a duration exceeds the previous one by
+    more than the factor `gap` (one kernel launched on inputs of very
+    different sizes, with the same grid)."""
+    d = []
+    for path in _one(dir_, "kernel_trace.csv"):
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if _short(r["Kernel_Name"]) == kernel:
+                    d.append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    d.sort()
+    out, cur = [], []
+    for v in d:
+        if cur and v > gap * cur[-1]:
+            out.append(cur)
+            cur = []
+        cur.append(v)
+    if cur:
+        out.append(cur)
+    return out
 
 
 def _counter(dir_, counter):
@@ -150,6 +181,9 @@ def main(argv=None):
     a.add_argument("dir")
     a.add_argument("out")
     a.add_argument("--cmd", required=True)
+    a.add_argument("--clusters", metavar="KERNEL",
+                   help="also split this kernel's dispatches into duration clusters")
+    a.add_argument("--gap", type=float, default=1.5)
     b = sub.add_parser("pmc")
     b.add_argument("fetch_dir")
     b.add_argument("write_dir")

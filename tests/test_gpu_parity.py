@@ -127,10 +127,11 @@ def run_fused(M, x, gs=None, off=None, rows_gs=None, debug=True):
     return [host(t) for t in out]
 
 
-# The seeded workloads below also assert exact bytes: with sigma as a binary32
-# pair the kernel's y is the oracle's except within about 2^-46 of a binary32
-# rounding midpoint, and on these inputs none of those few values sits at a
-# quantization boundary (the acceptance rule above stays the contract).
+# The seeded workloads below also assert exact bytes: with sigma and the
+# product in binary64 the kernel's y is the oracle's except within about
+# 2^-52 of a binary32 rounding midpoint, and on these inputs none of those
+# few values sits at a quantization boundary (the acceptance rule above stays
+# the contract).
 def assert_exact(rep, what):
     assert rep.scale_mismatch == 0 and rep.code_mismatch == 0, "%s not byte-exact: %s" % (what, rep)
 
