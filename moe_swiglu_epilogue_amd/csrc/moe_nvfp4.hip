@@ -348,8 +348,9 @@ struct WorkgroupQueue {
 
 // A wave's walk over its tiles: groups of G consecutive tiles, the first
 // group starting at `tile` (a multiple of G), the next ones from `sched`.
-// The caller has tile < geo.tiles, and runs `setup` itself on waves without
-// a tile so that every wave reaches its barrier once. The walk keeps one tile
+// The caller has tile < geo.tiles, and runs `setup` (setup(0), then
+// setup(1)) itself on waves without a tile so that every wave reaches its
+// barrier once. The walk keeps one tile
 // in flight and calls op(tile, t, b, y, amax) with each lane's block b of
 // tile t, its 16 values y and their largest magnitude. Loop invariant: tile
 // t is staged in LDS and no loads are in flight. Each pass issues the loads
@@ -366,10 +367,12 @@ __device__ __forceinline__ void walk_tiles(const uint16_t* in, int64_t ld_in, co
     constexpr int P = Block::P;
     Tile t = tile_at(tile, geo);
     u32x4 v[P];
-    load_tile<P>(v, in, ld_in, t, lane);
     // the workgroup's one-time set-up (LDS tables, ending in a barrier) runs
-    // while the first tile's loads are in flight
-    setup();
+    // while the first tile's loads are in flight: phase 0 issues its global
+    // loads ahead of the tile's, phase 1 writes the tables and syncs
+    setup(0);
+    load_tile<P>(v, in, ld_in, t, lane);
+    setup(1);
     sched.start();
     stage_tile<P>(lds, v, lane);
     // Keeps the prologue's staging out of the loop: were the compiler to
@@ -486,35 +489,46 @@ __device__ const uint32_t kSigmaBits[] __attribute__((aligned(16))) = {
 };
 static_assert(sizeof(kSigmaBits) == nvfp4::kSigFloats * 4, "one binary64 per entry");
 
-// Fills the workgroup's sigmoid table in LDS (fused input only) from
-// kSigmaBits: 64 KB, eight 16-byte loads per thread, served by L2
-// after the first workgroups. Every wave of the workgroup takes part, so all
-// of them reach the barrier.
+// Copies the sigmoid table (fused input only) from kSigmaBits into the
+// workgroup's LDS: 64 KB, eight 16-byte loads per thread, served by L2 after
+// the first workgroups. Every wave of the workgroup takes part, so all of them
+// reach the barrier. Two phases: load() issues the global loads into
+// registers, store() writes them to LDS. A kernel issues load() before its
+// first tile's loads: the wait before store() then covers only the table's
+// own (L2) loads, which are older, and not the tile's HBM loads behind them
+// (the memory counter retires loads in order).
 template <class Block>
-__device__ __forceinline__ void fill_sigma_table(float* sig)
-{
-    if constexpr (Block::kSigmaTable) {
-        constexpr int kThreadsPerBlock = Block::kWaves * kWave;
-        constexpr int kWords = nvfp4::kSigFloats / 4;   // 16-byte words
-        constexpr int kFull = kWords / kThreadsPerBlock;
-        constexpr int kRest = kWords - kFull * kThreadsPerBlock;
-        static_assert(kRest < kThreadsPerBlock, "one more word for some threads");
-        const u32x4* src = reinterpret_cast<const u32x4*>(kSigmaBits);
-        u32x4* dst = reinterpret_cast<u32x4*>(sig);
-        u32x4 v[kFull + 1];
+struct SigmaCopy {
+    static constexpr int kThreadsPerBlock = Block::kWaves * kWave;
+    static constexpr int kWords = Block::kSigmaTable ? nvfp4::kSigFloats / 4 : 0;   // 16-byte words
+    static constexpr int kFull = kWords / kThreadsPerBlock;
+    static constexpr int kRest = kWords - kFull * kThreadsPerBlock;
+    static_assert(kRest < kThreadsPerBlock, "one more word for some threads");
+    u32x4 v[kFull + 1];
+
+    __device__ __forceinline__ void load()
+    {
+        if constexpr (Block::kSigmaTable) {
+            const u32x4* src = reinterpret_cast<const u32x4*>(kSigmaBits);
 #pragma unroll
-        for (int k = 0; k < kFull; ++k)
-            v[k] = src[k * kThreadsPerBlock + threadIdx.x];
-        const bool rest = threadIdx.x < kRest;
-        if (rest)
-            v[kFull] = src[kFull * kThreadsPerBlock + threadIdx.x];
-#pragma unroll
-        for (int k = 0; k < kFull; ++k)
-            dst[k * kThreadsPerBlock + threadIdx.x] = v[k];
-        if (rest)
-            dst[kFull * kThreadsPerBlock + threadIdx.x] = v[kFull];
+            for (int k = 0; k < kFull; ++k)
+                v[k] = src[k * kThreadsPerBlock + threadIdx.x];
+            if (kRest > 0 && threadIdx.x < kRest)
+                v[kFull] = src[kFull * kThreadsPerBlock + threadIdx.x];
+        }
     }
-}
+    __device__ __forceinline__ void store(float* sig) const
+    {
+        if constexpr (Block::kSigmaTable) {
+            u32x4* dst = reinterpret_cast<u32x4*>(sig);
+#pragma unroll
+            for (int k = 0; k < kFull; ++k)
+                dst[k * kThreadsPerBlock + threadIdx.x] = v[k];
+            if (kRest > 0 && threadIdx.x < kRest)
+                dst[kFull * kThreadsPerBlock + threadIdx.x] = v[kFull];
+        }
+    }
+};
 
 template <class Block, bool kWide>
 __global__ __launch_bounds__(Block::kWaves * kWave) void quantize_tiles_kernel(
@@ -542,8 +556,13 @@ __global__ __launch_bounds__(Block::kWaves * kWave) void quantize_tiles_kernel(
     // standalone quantize, whose waves carry little compute, keeps the static
     // walk (the queue measured 0.8% slower there).
     const bool queued = Block::kSigmaTable && offsets == nullptr;
-    auto setup = [&]() {
-        fill_sigma_table<Block>(sig);
+    SigmaCopy<Block> table;
+    auto setup = [&](int phase) {
+        if (phase == 0) {
+            table.load();
+            return;
+        }
+        table.store(sig);
         if (lds_experts)
             fill_expert_table<kWaves * kWave>(tab, offsets, gs, num_experts);
         if (queued && threadIdx.x == 0)
@@ -552,7 +571,8 @@ __global__ __launch_bounds__(Block::kWaves * kWave) void quantize_tiles_kernel(
             __syncthreads();
     };
     if (tile >= geo.tiles) {
-        setup();
+        setup(0);
+        setup(1);
         return;
     }
     // Without experts the global scale (and its reciprocal) is the same for
@@ -641,7 +661,7 @@ __global__ __launch_bounds__(PlainBlock::kWaves * kWave) void quantize_paged_ker
     const nvfp4::RowScale rs = nvfp4::row_scale(gs != nullptr ? gs[0] : 1.0f);
     StaticWalk walk{(int)gridDim.x * kWaves};
     walk_tiles<PlainBlock>(in, ld_in, geo, tile, walk, lane, stage[wave], nullptr,
-                           [] {}, [&](int, const Tile& t, int b, const float (&y)[16], float amax) {
+                           [](int) {}, [&](int, const Tile& t, int b, const float (&y)[16], float amax) {
         const int64_t slot = slots[t.row];
         const bool keep = slot >= 0 && slot < num_slots;
         Tile o = t;
@@ -666,14 +686,20 @@ __global__ __launch_bounds__(FusedBlock::kWaves * kWave) void swiglu_bf16_kernel
     const int wave = uniform(threadIdx.x / kWave);
     u32x4* lds = stage[wave];
     const int tile = blockIdx.x * kWaves + wave;
-    auto setup = [&]() {
-        fill_sigma_table<Block>(sig);
+    SigmaCopy<Block> table;
+    auto setup = [&](int phase) {
+        if (phase == 0) {
+            table.load();
+            return;
+        }
+        table.store(sig);
         if (threadIdx.x == 0)
             queue = kWaves;
         __syncthreads();
     };
     if (tile >= geo.tiles) {
-        setup();
+        setup(0);
+        setup(1);
         return;
     }
     WorkgroupQueue<kWaves> walk{&queue, (int)gridDim.x * kWaves, lane, 0};
@@ -746,8 +772,13 @@ __global__ __launch_bounds__(Block::kWaves * kWave) void amax_tiles_kernel(
     // the SwiGLU pre-pass without experts shares its tiles through the LDS
     // queue, as the fused quantize does
     const bool queued = Block::kSigmaTable && offsets == nullptr;
-    auto setup = [&]() {
-        fill_sigma_table<Block>(sig);
+    SigmaCopy<Block> table;
+    auto setup = [&](int phase) {
+        if (phase == 0) {
+            table.load();
+            return;
+        }
+        table.store(sig);
         for (int i = threadIdx.x; i < groups; i += kWaves * kWave)
             part[i] = 0u;
         if (offsets != nullptr)
@@ -756,8 +787,10 @@ __global__ __launch_bounds__(Block::kWaves * kWave) void amax_tiles_kernel(
             queue = kWaves;
         __syncthreads();
     };
-    if (tile >= geo.tiles)
-        setup();
+    if (tile >= geo.tiles) {
+        setup(0);
+        setup(1);
+    }
     if (tile < geo.tiles) {
         // Each lane keeps a running max over the wave's consecutive tiles of
         // one expert; the wave reduces it and folds it into the workgroup's
