@@ -111,9 +111,10 @@ __device__ __forceinline__ float fp8_e4m3_decode(uint32_t code)
 
 // Per-block constants of the element quantizer.
 struct BlockScale {
-    uint32_t sf;   // E4M3 scale byte
-    float half_d;  // d / 2, d = RN(decode(sf) * gs)
-    float rcp;     // RN(1 / half_d) = RN(2 / d); 0 when d == 0
+    uint32_t sf;    // E4M3 scale byte
+    float half_d;   // d / 2, d = RN(decode(sf) * gs)
+    float rcp;      // within one ulp of 2 / d; 0 when d == 0
+    bool div_ok;    // rcp serves div_rn: RN(2 / d), or d/2 has an E4M3 significand
 };
 
 // Per-row constants: k = RN(6 gs), rk = RN(1 / k) (IEEE division), and
@@ -160,10 +161,14 @@ __device__ __forceinline__ float div_rn(float a, float b, float rb)
 // keeps the quotient finite for an infinite amax. rk = RN(1 / k) is an IEEE
 // division. The element quotients need a reciprocal of d/2. When gs is a
 // power of two, d/2 has an E4M3 significand, for which div_rn is exact even
-// with the faithful v_rcp_f32 as the reciprocal; otherwise the reciprocal is
-// the correctly rounded IEEE division. The branch is uniform (gs is per
-// row). Both hold for gs in [2^-64, 2^64], where every remainder stays in the
-// normal range.
+// with the faithful v_rcp_f32 as the reciprocal. Otherwise div_rn needs the
+// correctly rounded IEEE division, which the exact path of half_steps16
+// computes itself when it runs; the guarded fast path (kFast) only needs a
+// reciprocal within one ulp, so with kFast the block takes v_rcp_f32 for
+// every gs and leaves the division to the blocks that fall back. The branch
+// is uniform (gs is per row). Both hold for gs in [2^-64, 2^64], where every
+// remainder stays in the normal range.
+template <bool kFast>
 __device__ __forceinline__ BlockScale block_scale(float amax, const RowScale& rs)
 {
     BlockScale s;
@@ -173,11 +178,12 @@ __device__ __forceinline__ BlockScale block_scale(float amax, const RowScale& rs
     const float d = fp8_e4m3_decode(s.sf) * rs.gs;
     s.half_d = 0.5f * d;
     float r;
-    if (rs.pow2)
+    if (kFast || rs.pow2)
         r = __builtin_amdgcn_rcpf(s.half_d);
     else
         r = 1.0f / s.half_d;                  // IEEE division, correctly rounded
     s.rcp = d != 0.0f ? r : 0.0f;
+    s.div_ok = !kFast || rs.pow2;
     return s;
 }
 
@@ -235,14 +241,17 @@ __device__ __forceinline__ void half_steps16(const float (&y)[16], float amax,
         }
     }
     if (!(far < kTieGuard)) {
+        BlockScale e = s;
+        if (!e.div_ok)
+            e.rcp = e.half_d != 0.0f ? 1.0f / e.half_d : 0.0f;   // IEEE division
 #pragma unroll
         for (int j = 0; j < 16; ++j)
-            h[j] = half_steps(y[j], s);
-        if (amax * s.rcp > 16.0f) {
-            const float lim = 16.0f * s.half_d;
+            h[j] = half_steps(y[j], e);
+        if (amax * e.rcp > 16.0f) {
+            const float lim = 16.0f * e.half_d;
 #pragma unroll
             for (int j = 0; j < 16; ++j)
-                h[j] = half_steps(__builtin_amdgcn_fmed3f(y[j], -lim, lim), s);
+                h[j] = half_steps(__builtin_amdgcn_fmed3f(y[j], -lim, lim), e);
         }
     }
 }
@@ -276,7 +285,7 @@ template <bool kFast>
 __device__ __forceinline__ uint2 quantize16(const float (&y)[16], float amax, const RowScale& rs,
                                             uint32_t& sf_out)
 {
-    const BlockScale s = block_scale(amax, rs);
+    const BlockScale s = block_scale<kFast>(amax, rs);
     float h[16];
     half_steps16<kFast>(y, amax, s, h);
     uint32_t w0 = 0, w1 = 0;

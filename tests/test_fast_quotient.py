@@ -2,10 +2,9 @@
 
 The element step of the method is h = rint(RN(x / (d/2))) (the signed
 half-step count; ties to even). The kernels first try q0 = RN(x * rcp), with
-rcp within one ulp of 2/d (v_rcp_f32 when d has an E4M3 significand, the
-correctly rounded division otherwise), and take h = rint(q0) for a whole
-block when every |q0 - rint(q0)| of it is below 0.5 - 2^-17; otherwise the
-block takes the exact quotient. This test runs both in binary32 on the CPU
+rcp = v_rcp_f32(d/2), within one ulp of 2/d, and take h = rint(q0) for a
+whole block when every |q0 - rint(q0)| of it is below 0.5 - 2^-17;
+otherwise the block takes the exact quotient. This test runs both in binary32 on the CPU
 (IEEE division, no contraction) and checks, wherever the guard accepts q0:
 
 * |h_exact| <= 14: rint(q0) == h_exact, bit for bit (the sign of zero
@@ -15,8 +14,9 @@ block takes the exact quotient. This test runs both in binary32 on the CPU
 
 exhaustively over every numerator significand in the 8 binades with
 quotients in [2^-3, 32) (and the negated values), for the 8 E4M3 divisor
-significands with the reciprocal RN(1/b) and both of its neighbours, and on a
-sample of numerators for random divisor significands with RN(1/b). It also
+significands, and on a sample of numerators for random divisor significands
+(general global scales), each with the reciprocal RN(1/b) and both of its
+neighbours (every value a one-ulp reciprocal can take). It also
 checks that exact ties (quotients on a half-integer) are always sent to the
 exact path, that tiny, zero and large numerators behave, and reports how
 often the guard rejects a value.
@@ -86,19 +86,24 @@ int main(int argc, char** argv) {
                              0x1p100f, -0x1.7p120f};
         for (int i = 0; i < 8; ++i) { long r = 0; bad += check(xs[i], hd, rcp, &r); ++n; }
     }
-    /* random divisor significands, RN(1/b), every 5th numerator significand */
+    /* random divisor significands, RN(1/b) and both neighbours, every 5th
+       numerator significand */
     srand(4242);
     const int ndiv = atoi(argv[1]);
     for (int t = 0; t < ndiv; ++t) {
         const uint32_t md = ((uint32_t)rand() ^ ((uint32_t)rand() << 15)) & 0x7fffffu;
-        const float hd = u2f((127u << 23) | md), rcp = 1.0f / hd;
-        #pragma omp parallel for reduction(+:bad,n,rej) schedule(static)
-        for (uint32_t mx = 0; mx < (1u << 23); mx += 5)
-            for (int e = -3; e <= 4; ++e) {
-                const float x = ldexpf(u2f((127u << 23) | mx), e);
-                bad += check(x, hd, rcp, &rej) + check(-x, hd, rcp, &rej);
-                n += 2;
-            }
+        const float hd = u2f((127u << 23) | md), r0 = 1.0f / hd;
+        const float rcps[3] = {r0, nextafterf(r0, 0.0f), nextafterf(r0, INFINITY)};
+        for (int k = 0; k < 3; ++k) {
+            const float rcp = rcps[k];
+            #pragma omp parallel for reduction(+:bad,n,rej) schedule(static)
+            for (uint32_t mx = 0; mx < (1u << 23); mx += 5)
+                for (int e = -3; e <= 4; ++e) {
+                    const float x = ldexpf(u2f((127u << 23) | mx), e);
+                    bad += check(x, hd, rcp, &rej) + check(-x, hd, rcp, &rej);
+                    n += 2;
+                }
+        }
     }
     printf("%ld %ld %ld %ld %ld\n", n, bad, rej, ties, tie_ok);
     return 0;
@@ -117,7 +122,7 @@ def test_guarded_fast_quotient_gives_the_exact_counts(tmp_path):
                          env={**os.environ, "OMP_NUM_THREADS": str(min(8, os.cpu_count() or 1))})
     n, bad, rej, ties, tie_ok = map(int, out.stdout.split())
     exhaustive = 8 * 3 * (1 << 23) * 8 * 2
-    sampled = 32 * (((1 << 23) + 4) // 5) * 8 * 2
+    sampled = 32 * 3 * (((1 << 23) + 4) // 5) * 8 * 2
     assert n == exhaustive + 8 * 8 + sampled
     assert bad == 0, "fast count accepted but wrong in %d of %d cases" % (bad, n)
     # every exact tie is sent to the exact path
