@@ -525,7 +525,7 @@ __device__ __forceinline__ void fused_block(const Gemm& g, const TileRef& tr, in
         y[8 + j] = swiglu_f32(v[16 + j], v[24 + j]);
     }
     uint32_t sf;
-    const uint2 q = nvfp4::quantize16<true>(y, nvfp4::block_amax(y), rs, sf);
+    const uint2 q = nvfp4::quantize16<true, false>(y, nvfp4::block_amax(y), rs, sf);
     const int trow = pass_row(pass, row);
     if (trow < tr.rows) {
         const int64_t grow = tr.row0 + trow;

@@ -164,11 +164,12 @@ __device__ __forceinline__ float div_rn(float a, float b, float rb)
 // with the faithful v_rcp_f32 as the reciprocal. Otherwise div_rn needs the
 // correctly rounded IEEE division, which the exact path of half_steps16
 // computes itself when it runs; the guarded fast path (kFast) only needs a
-// reciprocal within one ulp, so with kFast the block takes v_rcp_f32 for
-// every gs and leaves the division to the blocks that fall back. The branch
-// is uniform (gs is per row). Both hold for gs in [2^-64, 2^64], where every
+// reciprocal within one ulp, so with kLazyDiv the block takes v_rcp_f32 for
+// every gs and leaves the division to the blocks that fall back (the GEMM
+// epilogue, short of registers, divides up front instead). The branch is
+// uniform (gs is per row). Both hold for gs in [2^-64, 2^64], where every
 // remainder stays in the normal range.
-template <bool kFast>
+template <bool kLazyDiv>
 __device__ __forceinline__ BlockScale block_scale(float amax, const RowScale& rs)
 {
     BlockScale s;
@@ -178,12 +179,12 @@ __device__ __forceinline__ BlockScale block_scale(float amax, const RowScale& rs
     const float d = fp8_e4m3_decode(s.sf) * rs.gs;
     s.half_d = 0.5f * d;
     float r;
-    if (kFast || rs.pow2)
+    if (kLazyDiv || rs.pow2)
         r = __builtin_amdgcn_rcpf(s.half_d);
     else
         r = 1.0f / s.half_d;                  // IEEE division, correctly rounded
     s.rcp = d != 0.0f ? r : 0.0f;
-    s.div_ok = !kFast || rs.pow2;
+    s.div_ok = !kLazyDiv || rs.pow2;
     return s;
 }
 
@@ -280,12 +281,14 @@ __device__ __forceinline__ float block_amax(const float (&y)[16])
 }
 
 // 16 FP32 values and their amax -> 8 bytes of packed E2M1 codes (returned
-// as uint2) and the scale byte; kFast as in half_steps16.
-template <bool kFast>
+// as uint2) and the scale byte; kFast as in half_steps16, kLazyDiv as in
+// block_scale (only with kFast).
+template <bool kFast, bool kLazyDiv = kFast>
 __device__ __forceinline__ uint2 quantize16(const float (&y)[16], float amax, const RowScale& rs,
                                             uint32_t& sf_out)
 {
-    const BlockScale s = block_scale<kFast>(amax, rs);
+    static_assert(kFast || !kLazyDiv, "the exact path needs the divided reciprocal");
+    const BlockScale s = block_scale<kLazyDiv>(amax, rs);
     float h[16];
     half_steps16<kFast>(y, amax, s, h);
     uint32_t w0 = 0, w1 = 0;
