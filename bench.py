@@ -577,9 +577,11 @@ def secondary_figures(M, W, x, packed, scales, args, dev):
 
 def gemm_figures(M, W, args):
     """The MoE L1 grouped GEMM with the fused SwiGLU + NVFP4 epilogue against
-    the unfused flow on the same GEMM core (BF16 L1 output, then
-    swiglu_nvfp4_quantize), and hipBLASLt's plain BF16 GEMM (torch.matmul per
-    expert) for context: 32768 token rows, hidden 7168, I = 3072, 8 experts."""
+    the same GEMM core with a plain BF16 store (the cost of the fused
+    epilogue: `epilogue_cost`), the unfused flow on that core (BF16 L1 output,
+    then swiglu_nvfp4_quantize), and hipBLASLt's plain BF16 GEMM
+    (torch.matmul per expert) for context: 32768 token rows, hidden 7168,
+    I = 3072, 8 experts."""
     import numpy as np
     import torch
     print("[bench] generating MoE L1 GEMM workload", file=sys.stderr, flush=True)
@@ -604,6 +606,9 @@ def gemm_figures(M, W, args):
     def fused():
         M.moe_l1_gemm_swiglu_nvfp4(x, w, off, packed=p, scales=sc)
 
+    def bf16_output():
+        M.moe_l1_gemm_bf16(x, w, off, out=yb)
+
     def unfused():
         M.moe_l1_gemm_bf16(x, w, off, out=yb)
         M.swiglu_nvfp4_quantize(yb, packed=p, scales=sc)
@@ -615,7 +620,8 @@ def gemm_figures(M, W, args):
     res = {"shape": {"tokens": T, "hidden": H, "inter": inter, "experts": E},
            "flop_per_launch": flop}
     steps = max(5, args.secondary_steps // 4)
-    for name, fn in (("fused", fused), ("unfused", unfused), ("hipblaslt_bf16_gemm_only", library)):
+    for name, fn in (("fused", fused), ("bf16_output", bf16_output), ("unfused", unfused),
+                     ("hipblaslt_bf16_gemm_only", library)):
         _, ms, per = time_launches(fn, steps, 2, args.settle_ms)
         res[name] = {"ms": round(ms, 4), "TFLOP_s": round(flop / ms / 1e9, 1),
                      "frac_of_bf16_peak": round(flop / ms / 1e9 / PEAK_BF16_TFLOPS, 4),
@@ -623,6 +629,7 @@ def gemm_figures(M, W, args):
         print("[bench] MoE L1 GEMM %-26s %8.4f ms  %7.1f TFLOP/s" % (name, ms, flop / ms / 1e9),
               file=sys.stderr, flush=True)
     res["fusion_speedup"] = round(res["unfused"]["ms"] / res["fused"]["ms"], 4)
+    res["epilogue_cost"] = round(res["fused"]["ms"] / res["bf16_output"]["ms"] - 1.0, 4)
     return res
 
 
