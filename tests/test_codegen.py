@@ -100,6 +100,40 @@ def test_no_scalar_memory_writes(isa):
     assert not bad, bad
 
 
+def table_loads_precede_tile_loads(isa):
+    """For each kernel that copies the sigmoid table: in the code before its
+    set-up barrier, the table's eight 16-byte loads (plain) must all be
+    issued before the first tile's 16-byte loads (non-temporal), so that the
+    wait before the table's LDS writes does not also wait for the tile's HBM
+    loads (loads retire in order). Returns the kernels where they do not."""
+    ks = {n: body for n, body in _kernels(isa).items()
+          if "FusedBlock" in n or "swiglu_bf16_kernel" in n}
+    assert len(ks) == 4, sorted(ks)
+    bad = []
+    for name, body in ks.items():
+        seen = False
+        start = 0
+        for k, l in enumerate(body):
+            if not l.startswith("s_barrier"):
+                continue
+            seg = body[start:k]
+            start = k + 1
+            loads = [x for x in seg if x.startswith("global_load_dwordx4")]
+            nt = [j for j, x in enumerate(loads) if x.endswith(" nt")]
+            plain = [j for j, x in enumerate(loads) if not x.endswith(" nt")]
+            if nt and len(plain) >= 8:
+                seen = True
+                if plain[7] > nt[0]:
+                    bad.append(name)
+        if not seen:
+            bad.append(name + " (no set-up segment found)")
+    return bad
+
+
+def test_sigma_table_loads_go_out_before_the_first_tile(isa):
+    assert table_loads_precede_tile_loads(isa) == []
+
+
 def test_no_scratch_in_any_kernel(tmp_path):
     from moe_swiglu_epilogue_amd import build as B
     for src in (B.SRC, B.GEMM_SRC):
