@@ -19,24 +19,28 @@
 // output column n (the weight stored [out][in], K contiguous). Output column
 // n of the L1 GEMM follows the interleaved layout [gate x8, up x8, ...].
 //
-// Decomposition: one workgroup of 4 waves per CU (one wave per SIMD)
-// computes 256 x 256 output tiles; wave (wm, wn) owns rows 128 wm .. +128
-// and columns 128 wn .. +128 as 4 x 4 MFMA tiles of 32 x 32, whose 256
-// accumulator registers per lane sit in the SIMD's accumulation registers.
-// The K loop stages 256 x 64 slices of x and w in LDS (double-buffered,
-// 16-byte chunks XOR-swizzled against bank conflicts). The slices arrive by
-// buffer loads straight into LDS (buffer_load_dwordx4 ... lds, 16 bytes per
-// lane on gfx950) one slice ahead, so no register holds them on the way,
-// and each pass is software-pipelined by hand (the fragment reads for the
-// next K step interleaved with the MFMAs).
+// Decomposition: one workgroup of 8 waves per CU (two per SIMD) computes
+// 256 x 256 output tiles; group G of 4 waves owns rows 128 G .. +128 and
+// wave s of it columns 64 s .. +64, as 4 x 2 MFMA tiles of 32 x 32 (128
+// accumulator registers per lane). The K loop stages 256 x 64 slices of x
+// and w in LDS (double-buffered, 16-byte chunks XOR-swizzled against bank
+// conflicts). The slices arrive by buffer loads straight into LDS
+// (buffer_load_dwordx4 ... lds, 16 bytes per lane on gfx950), so no
+// register holds them on the way. The loop is a ping-pong: the two waves of
+// each SIMD take turns issuing a slice's 32 MFMAs and reading the next
+// slice's fragments (and issuing loads), so one wave feeds the SIMD's
+// matrix core while the other waits on LDS and memory.
 //
 // What bounds it: a 256 x 256 tile does 128 FLOP per byte of operand slices,
-// so the matrix-core peak would need about 19 TB/s of operands from L2. With
-// the loads taken out (a timing probe) the kernel runs at 60% of the BF16
-// peak, with the loads and LDS traffic out at 83%. The operand reads
-// therefore set the pace, and the walk order is chosen for cache reuse:
-// tiles of the same row group and expert run together on every XCD. 256 x
-// 256 is the largest tile the accumulation registers hold (4 SIMDs x 64 KB).
+// so the matrix-core peak would need about 19 TB/s of operands from L2, and
+// a CU's vector memory path (about 64 bytes per clock) is busy for about
+// 1024 of the 2048 clocks a slice's MFMAs take. The walk order is chosen
+// for cache reuse (tiles of the same row group and expert run together on
+// every XCD), and the loads are spread over the waves that are not issuing
+// MFMAs. 256 x 256 is the largest tile the registers of 8 waves hold with
+// their fragments (4 SIMDs x 2 waves x 32 KB of accumulators). The MFMA
+// streams take about 84% of the K loop's clocks; the clock itself is held
+// down by the board's power limit while the matrix cores are this busy.
 //
 // Tiles are enumerated per expert (ceil(rows_e / 256) row tiles each, from a
 // prefix sum the workgroup builds once in LDS) and handed to a persistent,
@@ -52,15 +56,15 @@ namespace {
 
 constexpr int kWave = 64;
 constexpr int kBM = 256, kBN = 256, kBK = 64;
-constexpr int kThreads = 256;                             // 4 waves: 2 x 2 wave tiles of 128 x 128
-constexpr int kWaveM = 128, kWaveN = 128;
-constexpr int kTM = kWaveM / 32, kTN = kWaveN / 32;       // 4 x 4 MFMA tiles per wave
+constexpr int kThreads = 512;                             // 8 waves, two per SIMD
+constexpr int kWaveM = 128, kWaveN = 64;                  // group G rows 128 G, wave s columns 64 s
+constexpr int kTM = kWaveM / 32, kTN = kWaveN / 32;       // 4 x 2 MFMA tiles per wave
+constexpr int kKSteps = kBK / 16;                         // MFMA K steps per slice
 constexpr int kMaxExperts = 512;
 constexpr int kRowBytes = kBK * 2;                        // 128 bytes per staged row
 constexpr int kRegionBytes = kBM * kRowBytes;             // 32 KB: one operand's slice
 constexpr int kStageBytes = 2 * kRegionBytes;             // x slice, then w slice
 constexpr int kDmaRows = kWave * 16 / kRowBytes;          // staged rows one LDS-DMA load fills (8)
-constexpr int kDmaLoads = kBM / (kThreads / kWave) / kDmaRows;   // per wave and operand (8)
 constexpr int kPassRows = 64;                             // epilogue rows per pass
 constexpr int kCPitch = kBN + 4;                          // floats per LDS row of the C buffer
 constexpr int kCBytes = kPassRows * kCPitch * 4;          // 66,560 B
@@ -193,10 +197,15 @@ __device__ __forceinline__ TileRef tile_ref(const Gemm& g, const int* off, const
 // the row. Every w row lies inside its window: one VGPR offset (chunk t % 8
 // of row t / 8), with the row step in the SGPR offset. Windows are at most
 // 256 rows of pitch < 2^22 elements: under 2^31 bytes.
+//
+// The loads of a slice are split by group (see gemm_tile): wave s of group 0
+// loads w rows 64 s .. +64 (8 loads), wave s of group 1 loads x rows
+// 32 s .. +32 of the upper half and 128 + 32 s .. +32 of the lower half
+// (4 loads each).
 struct TileSrc {
     u32x4 x, w;              // buffer descriptors (SGPRs)
-    int vx[kDmaLoads];       // x row offsets of this lane for load instruction j
-    int vw[2];               // w offsets (row within the 8-row group) for even / odd j
+    int vx[8];               // group 1: x row offsets of this lane, upper-half loads 0-3, lower 4-7
+    int vw[2];               // group 0: w offsets (row within the 8-row group) for even / odd loads
     int row_w;               // bytes of one w row
 };
 
@@ -210,21 +219,25 @@ __device__ __forceinline__ u32x4 window(const uint16_t* base, int bytes)
                  (uint32_t)uniform(bytes), 0x00020000u};
 }
 
-// Load instruction j of wave w fills staged rows 64 w + 8 j .. +8 (1 KB of
-// LDS, lane l at byte 16 l): lane l loads row 64 w + 8 j + l / 8, logical
-// chunk (l % 8) ^ swz(row) = (l % 8) ^ (4 (j % 2) + l / 16).
-__device__ __forceinline__ TileSrc tile_src(const Gemm& g, const TileRef& tr, int wave)
+// A load instruction fills 8 staged rows r0 .. r0 + 8 (r0 a multiple of 8;
+// 1 KB of LDS, lane l at byte 16 l): lane l loads row r0 + l / 8, logical
+// chunk (l % 8) ^ swz(row) = (l % 8) ^ (4 ((r0 / 8) % 2) + l / 16). The x
+// loads of wave s (group 1) start at rows 32 s + 8 i and 128 + 32 s + 8 i
+// (i = 0..3), the w loads of wave s (group 0) at 64 s + 8 j (j = 0..7):
+// r0 / 8 has the parity of i, resp. j.
+__device__ __forceinline__ TileSrc tile_src(const Gemm& g, const TileRef& tr, int s)
 {
     TileSrc t;
     t.x = window(g.x + (int64_t)tr.row0 * g.ld_x, tr.rows * (int)g.ld_x * 2);
     t.w = window(g.w + (int64_t)tr.e * g.w_expert + (int64_t)tr.n0 * g.ld_w, kBN * (int)g.ld_w * 2);
     const int l = threadIdx.x & (kWave - 1);
 #pragma unroll
-    for (int j = 0; j < kDmaLoads; ++j) {
-        const int c = (l & 7) ^ (4 * (j & 1) + (l >> 4));
-        t.vx[j] = (64 * wave + 8 * j + (l >> 3)) * (int)g.ld_x * 2 + 16 * c;
-        if (j < 2)
-            t.vw[j] = (l >> 3) * (int)g.ld_w * 2 + 16 * c;
+    for (int i = 0; i < 8; ++i) {
+        const int c = (l & 7) ^ (4 * (i & 1) + (l >> 4));
+        const int r0 = 128 * (i >> 2) + 32 * s + 8 * (i & 3);
+        t.vx[i] = (r0 + (l >> 3)) * (int)g.ld_x * 2 + 16 * c;
+        if (i < 2)
+            t.vw[i] = (l >> 3) * (int)g.ld_w * 2 + 16 * c;
     }
     t.row_w = (int)g.ld_w * 2;
     return t;
@@ -250,201 +263,218 @@ __device__ __forceinline__ void load_lds16(const u32x4& rsrc, uint32_t lds, int 
                  :: "s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "memory");
 }
 
-// Wave w's share of a 256 x 64 slice at K offset k0: staged rows 64 w ..
-// +64 of x and of w, 8 loads each.
-static_assert(kDmaRows == 8 && kDmaLoads == 8, "the swizzle and offsets assume 8 x 8 rows");
-__device__ __forceinline__ void load_slice(const TileSrc& src, uint8_t* stage, int k0, int wave)
+// Group 0 wave s's share of the w slice at K offset k0 into the stage at
+// LDS address `base`: staged w rows 64 s .. +64, 8 loads.
+static_assert(kDmaRows == 8, "the swizzle and offsets assume 8-row loads");
+__device__ __forceinline__ void load_w(const TileSrc& src, uint32_t base, int k0, int s)
 {
-    const uint32_t base = lds_addr(stage);
 #pragma unroll
-    for (int j = 0; j < kDmaLoads; ++j) {
-        const int row = 64 * wave + 8 * j;
-        load_lds16(src.x, base + row * kRowBytes, src.vx[j], uniform(2 * k0));
+    for (int j = 0; j < 8; ++j) {
+        const int row = 64 * s + 8 * j;
         load_lds16(src.w, base + kRegionBytes + row * kRowBytes, src.vw[j & 1],
                    uniform(row * src.row_w + 2 * k0));
     }
 }
 
-// The wave's MFMA operands for one 16-deep K step kk of the staged slice:
-// 4 A fragments (rows 128 wm + 32 t + lane % 32) and 4 B fragments (columns
-// 128 wn + 32 t + lane % 32), each 8 K values starting at 8 (2 kk + lane / 32).
-struct Frags {
-    bf16x8 a[kTM], b[kTN];
+// Group 1 wave s's share of one half of the x slice at K offset k0: staged
+// x rows 128 half + 32 s .. +32, 4 loads.
+__device__ __forceinline__ void load_x(const TileSrc& src, uint32_t base, int k0, int s, int half)
+{
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int row = 128 * half + 32 * s + 8 * i;
+        load_lds16(src.x, base + row * kRowBytes, src.vx[4 * half + i], uniform(2 * k0));
+    }
+}
+
+// The wave's MFMA operands for a whole staged slice: for each 16-deep K
+// step kk, 4 A fragments (rows 128 G + 32 t + lane % 32) and 2 B fragments
+// (columns 64 s + 32 t + lane % 32), each 8 K values starting at
+// 8 (2 kk + lane / 32). 24 reads of 16 bytes per lane, 96 registers.
+struct SliceFrags {
+    bf16x8 a[kKSteps][kTM], b[kKSteps][kTN];
 };
 
-__device__ __forceinline__ void read_frags(Frags& f, const uint8_t* stage, int kk, int wm, int wn,
+__device__ __forceinline__ void read_slice(SliceFrags& f, const uint8_t* stage, int grp, int s,
                                            int lane)
 {
-    // rows 32 t + lane % 32 (+ a multiple of 128): swz depends on the lane only
-    const int off = (lane & 31) * kRowBytes + (((2 * kk + (lane >> 5)) ^ swz(lane & 31)) << 4);
+    // rows 32 t + lane % 32 (+ a multiple of 32): swz depends on the lane only
+    const int row = (lane & 31) * kRowBytes;
+    const int c0 = (lane >> 5) ^ swz(lane & 31);            // chunk of K step kk: 2 kk ^ c0
 #pragma unroll
-    for (int t = 0; t < kTM; ++t)
-        f.a[t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
-                                                stage + (kWaveM * wm + 32 * t) * kRowBytes + off));
+    for (int kk = 0; kk < kKSteps; ++kk) {
+        const int off = row + (((2 * kk) ^ c0) << 4);
 #pragma unroll
-    for (int t = 0; t < kTN; ++t)
-        f.b[t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
-                                                stage + kRegionBytes + (kWaveN * wn + 32 * t) * kRowBytes + off));
-}
-
-// acc[tm][tn] += A fragment tm x B fragment tn for the kCount MFMA tiles
-// kFirst .. kFirst + kCount - 1 (tile i = row tile i / kTN, column tile
-// i % kTN); the whole step is 16 MFMAs.
-template <int kFirst = 0, int kCount = kTM * kTN>
-__device__ __forceinline__ void mma_step(f32x16 (&acc)[kTM][kTN], const Frags& f)
-{
+        for (int t = 0; t < kTM; ++t)
+            f.a[kk][t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
+                                                        stage + (kWaveM * grp + 32 * t) * kRowBytes + off));
 #pragma unroll
-    for (int i = kFirst; i < kFirst + kCount; ++i)
-        acc[i / kTN][i % kTN] =
-            __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i / kTN], f.b[i % kTN], acc[i / kTN][i % kTN], 0, 0, 0);
-}
-
-// Fixes the issue order of one pipeline phase for the scheduler: kPairs
-// times one MFMA then one instruction of kind kOther (0x100 LDS read, 0x200
-// LDS write), then the phase's remaining MFMAs. A fence closes the phase.
-template <int kOther, int kPairs>
-__device__ __forceinline__ void phase_order()
-{
-#pragma unroll
-    for (int i = 0; i < kPairs; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kOther, 1, 0);
-    }
-    if constexpr (kPairs < kTM * kTN)
-        __builtin_amdgcn_sched_group_barrier(0x008, kTM * kTN - kPairs, 0);
-    __builtin_amdgcn_sched_barrier(0);
-}
-
-// MFMAs of K step 3 that a pass leaves for after the next barrier.
-constexpr int kHeld = 16;
-constexpr int kStep = kTM * kTN;
-
-// The MFMAs of slice kb staged in stage kb % 2, software-pipelined by hand:
-// one wave per SIMD has no other wave to hide its waits behind, so the
-// fragments of K step kk + 1 are read from LDS while the MFMAs of step kk
-// issue. Two fragment sets suffice: a set is refilled only after every MFMA
-// reading it has issued. On entry f0 holds (or is being read with) step 0.
-// The pass stops kHeld MFMAs short of the end of step 3; f1 keeps that
-// step's fragments for them, and the caller issues them after the next
-// barrier, where they cover the latency of the next slice's first fragment
-// reads and the issue of its loads (otherwise the matrix core idles
-// through both).
-__device__ __forceinline__ void k_pass(const uint8_t* st, f32x16 (&acc)[kTM][kTN], Frags& f0,
-                                       Frags& f1, int wm, int wn, int lane)
-{
-    mma_step(acc, f0);
-    read_frags(f1, st, 1, wm, wn, lane);
-    phase_order<0x100, kTM + kTN>();
-    mma_step(acc, f1);
-    read_frags(f0, st, 2, wm, wn, lane);
-    phase_order<0x100, kTM + kTN>();
-    mma_step(acc, f0);
-    read_frags(f1, st, 3, wm, wn, lane);
-    phase_order<0x100, kTM + kTN>();
-    mma_step<0, kStep - kHeld>(acc, f1);
-    __builtin_amdgcn_sched_barrier(0);
-}
-
-// The held MFMAs of K step 3 of the previous slice (fragments in f1), with
-// the next slice's loads (k0) issued between them: load n of the wave is
-// its x (n even) or w (n odd) load of rows 64 w + 8 (n / 2) .. +8, so the
-// matrix core is not idle while they issue.
-__device__ __forceinline__ void mma_held_loading(f32x16 (&acc)[kTM][kTN], const Frags& f1,
-                                                 const TileSrc& src, uint8_t* stage, int k0,
-                                                 int wave)
-{
-    constexpr int kPer = 2 * kDmaLoads / kHeld;           // loads after each held MFMA
-    static_assert(kPer * kHeld == 2 * kDmaLoads, "the loads spread evenly over the held MFMAs");
-    const uint32_t base = lds_addr(stage);
-#pragma unroll
-    for (int j = 0; j < kHeld; ++j) {
-        const int i = kStep - kHeld + j;
-        acc[i / kTN][i % kTN] =
-            __builtin_amdgcn_mfma_f32_32x32x16_bf16(f1.a[i / kTN], f1.b[i % kTN], acc[i / kTN][i % kTN], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int q = 0; q < kPer; ++q) {
-            const int n = kPer * j + q;
-            const int row = 64 * wave + 8 * (n >> 1);
-            if ((n & 1) == 0)
-                load_lds16(src.x, base + row * kRowBytes, src.vx[n >> 1], uniform(2 * k0));
-            else
-                load_lds16(src.w, base + kRegionBytes + row * kRowBytes, src.vw[(n >> 1) & 1],
-                           uniform(row * src.row_w + 2 * k0));
-        }
-        __builtin_amdgcn_sched_barrier(0);
+        for (int t = 0; t < kTN; ++t)
+            f.b[kk][t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
+                                                        stage + kRegionBytes + (kWaveN * s + 32 * t) * kRowBytes + off));
     }
 }
 
-// The K loop of one tile. Slice kb + 1 is loaded straight into the other
-// stage while slice kb is computed; each wave waits for its own loads
-// (vmcnt(0)) and the barrier that follows makes every wave's loads visible
-// and ends all reads of the stage the next loads overwrite. Ends with a
-// barrier after the last slice's reads.
+constexpr int kSliceMfmas = kKSteps * kTM * kTN;             // 32
+
+// MFMA n of a slice: K step n / 8, row tile (n % 8) / kTN, column tile n % kTN.
+__device__ __forceinline__ void mma_one(f32x16 (&acc)[kTM][kTN], const SliceFrags& f, int n)
+{
+    const int kk = n / (kTM * kTN), i = n % (kTM * kTN);
+    acc[i / kTN][i % kTN] =
+        __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[kk][i / kTN], f.b[kk][i % kTN], acc[i / kTN][i % kTN], 0, 0, 0);
+}
+
+// The slice's 32 MFMAs back to back (about 1024 cycles of the SIMD's matrix
+// core).
+__device__ __forceinline__ void mma_slice(f32x16 (&acc)[kTM][kTN], const SliceFrags& f)
+{
+#pragma unroll
+    for (int n = 0; n < kSliceMfmas; ++n)
+        mma_one(acc, f, n);
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// A workgroup barrier that orders nothing by itself: the waits a phase needs
+// are written out before it. (__syncthreads() would also wait for every
+// outstanding load, the loader waves' LDS-DMA loads of the next slice
+// included.) The memory clobber keeps LDS accesses on their side of it.
+__device__ __forceinline__ void phase_barrier()
+{
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+__device__ __forceinline__ void wait_lds_reads() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// The K loop of one tile, as a ping-pong between the two waves of each SIMD.
+// Group 0 (waves 0-3) and group 1 (waves 4-7) hold the tile's upper and
+// lower 128 rows; wave w and wave w + 4 run on the same SIMD. Both groups
+// run the same loop, read a slice's fragments | barrier | issue its 32
+// MFMAs | barrier, group 1 one phase behind group 0:
+//
+//   phase 2j         group 0 reads slice j      group 1 computes slice j - 1
+//   phase 2j + 1     group 0 computes slice j   group 1 reads slice j
+//
+// (group 1 idles through phase 0, group 0 through the last phase), so each
+// SIMD's matrix core runs one wave's MFMAs while the other wave's LDS reads
+// are in flight, and a barrier costs a few cycles instead of the drift
+// between four waves that all compute. Slice j sits in stage j % 2.
+//
+// The LDS-DMA loads are issued in the read phases: a load can stall the
+// issuing wave for tens of cycles while the CU's vector memory path (about
+// 64 bytes per clock, so about 1024 clocks per 64 KB slice) works through
+// the loads before it, which a read phase has time for and an MFMA stream
+// has not. They are spread over both groups' read phases, 32 loads each,
+// by what each group reads: group 0 reads x rows 0-127 and all of w, group
+// 1 rows 128-255 and all of w.
+//   * phase 2j: group 0 loads w of slice j + 1 into stage (j + 1) % 2 (both
+//     groups read the w there, of slice j - 1, in phases 2j - 2 and 2j - 1),
+//     and waits for it at the end of phase 2j + 1;
+//   * phase 2j + 1: group 1 loads the lower x half of slice j + 1 into stage
+//     (j + 1) % 2 (it read the one there itself in phase 2j - 1) and waits
+//     for it at the end of phase 2j + 2, and the upper x half of slice j + 2
+//     into stage j % 2 (group 0 read the one there in phase 2j), waiting for
+//     it at the end of phase 2j + 3, before group 0 reads it in phase 2j + 4.
+// Each wave waits for its own reads before the barrier that closes its read
+// phase, so a stage part is free when the next barrier has passed; waits for
+// loads use the exact in-order count of loads issued after them (or wait for
+// all at the end of the K loop). Every wave runs 2 + 2 K / 64 barriers
+// (s_barrier counts arrivals, not places in the code). Ends after the last
+// slice's MFMAs have issued, with every LDS read and load complete.
 __device__ __forceinline__ void gemm_tile(const Gemm& g, const TileRef& tr, uint8_t* smem,
-                                          f32x16 (&acc)[kTM][kTN], int wave, int wm, int wn,
-                                          int lane)
+                                          f32x16 (&acc)[kTM][kTN], int grp, int s, int lane)
 {
 #pragma unroll
     for (int tm = 0; tm < kTM; ++tm)
 #pragma unroll
         for (int tn = 0; tn < kTN; ++tn)
             acc[tm][tn] = f32x16{};
-    const int last = g.k / kBK - 1;
-    const TileSrc src = tile_src(g, tr, wave);
-    load_slice(src, smem, 0, wave);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    Frags f0, f1;
-    read_frags(f0, smem, 0, wm, wn, lane);
-    if (last > 0)
-        load_slice(src, smem + kStageBytes, kBK, wave);
-    __builtin_amdgcn_sched_barrier(0);
-    k_pass(smem, acc, f0, f1, wm, wn, lane);
-    // slices 1 .. last - 1, each loading the next
-    for (int kb = 1; kb < last; ++kb) {
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        const uint8_t* st = smem + (kb & 1) * kStageBytes;
-        read_frags(f0, st, 0, wm, wn, lane);
-        __builtin_amdgcn_sched_barrier(0);
-        mma_held_loading(acc, f1, src, smem + ((kb + 1) & 1) * kStageBytes, (kb + 1) * kBK, wave);
-        k_pass(st, acc, f0, f1, wm, wn, lane);
+    const int slices = g.k / kBK;
+    const bool g0 = grp == 0;
+    const TileSrc src = tile_src(g, tr, s);
+    const uint32_t stages = lds_addr(smem);
+    // slice 0 (all of it) and the upper x half of slice 1
+    if (g0) {
+        load_w(src, stages, 0, s);
+        wait_loads();
+    } else {
+        load_x(src, stages, 0, s, 0);
+        load_x(src, stages, 0, s, 1);
+        if (slices > 1) {
+            load_x(src, stages + kStageBytes, kBK, s, 0);
+            asm volatile("s_waitcnt vmcnt(8)" ::: "memory");     // upper x half of slice 0
+        } else {
+            asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+        }
     }
-    if (last > 0) {
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        const uint8_t* st = smem + (last & 1) * kStageBytes;
-        read_frags(f0, st, 0, wm, wn, lane);
-        __builtin_amdgcn_sched_barrier(0);
-        mma_step<kStep - kHeld, kHeld>(acc, f1);
-        __builtin_amdgcn_sched_barrier(0);
-        k_pass(st, acc, f0, f1, wm, wn, lane);
+    phase_barrier();                                       // slice 0's upper half and w staged
+    if (!g0) {
+        // group 1 idles through phase 0: the lower x half of slice 0
+        if (slices > 1)
+            asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+        else
+            wait_loads();
+        phase_barrier();
     }
-    mma_step<kStep - kHeld, kHeld>(acc, f1);
-    __syncthreads();
+    for (int j = 0; j < slices; ++j) {
+        const uint32_t cur = uniform((j & 1) * kStageBytes), nxt = uniform(((j + 1) & 1) * kStageBytes);
+        SliceFrags f;
+        read_slice(f, smem + cur, grp, s, lane);
+        const bool more = j + 2 < slices;
+        if (g0) {
+            if (j + 1 < slices)
+                load_w(src, stages + nxt, (j + 1) * kBK, s);
+        } else {
+            if (j + 1 < slices)
+                load_x(src, stages + nxt, (j + 1) * kBK, s, 1);
+            if (more)
+                load_x(src, stages + cur, (j + 2) * kBK, s, 0);
+        }
+        wait_lds_reads();
+        if (!g0) {
+            // the upper x half of slice j + 1 (8 loads were issued after it)
+            if (more)
+                asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+            else
+                wait_loads();
+        }
+        phase_barrier();
+        mma_slice(acc, f);
+        if (g0)
+            wait_loads();                                  // w of slice j + 1
+        else if (more)
+            asm volatile("s_waitcnt vmcnt(4)" ::: "memory");     // lower x half of slice j + 1
+        else
+            wait_loads();
+        phase_barrier();
+    }
+    if (g0)
+        phase_barrier();                                   // group 0 idles through the last phase
 }
 
 // Epilogue pass p holds the tile rows of MFMA row tile p of every wave:
-// C buffer row r is tile row 128 (r / 32) + 32 p + r % 32. All 4 waves
-// write their tile p (no branch, and 64 accumulators per lane per pass):
-// row 32 wm + 8 (i / 4) + 4 (lane / 32) + i % 4, column 128 wn + 32 tn +
-// lane % 32 (the v_mfma_f32_32x32x16 result layout).
+// C buffer row r is tile row 128 (r / 32) + 32 p + r % 32. All 8 waves
+// write their tile p (no branch, and 32 accumulators per lane per pass):
+// row 32 G + 8 (i / 4) + 4 (lane / 32) + i % 4, column 64 s + 32 tn +
+// lane % 32 (the v_mfma_f32_32x32x16 result layout) for wave s of group G.
 __device__ __forceinline__ int pass_row(int pass, int r)
 {
     return kWaveM * (r >> 5) + 32 * pass + (r & 31);
 }
 
 template <int kPass>
-__device__ __forceinline__ void stage_accumulators(float* c, const f32x16 (&acc)[kTM][kTN], int wm,
-                                                   int wn, int lane)
+__device__ __forceinline__ void stage_accumulators(float* c, const f32x16 (&acc)[kTM][kTN], int grp,
+                                                   int s, int lane)
 {
 #pragma unroll
     for (int tn = 0; tn < kTN; ++tn)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            const int row = 32 * wm + (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3);
-            const int col = kWaveN * wn + 32 * tn + (lane & 31);
+            const int row = 32 * grp + (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3);
+            const int col = kWaveN * s + 32 * tn + (lane & 31);
             c[row * kCPitch + col] = acc[kPass][tn][i];
         }
 }
@@ -596,7 +626,7 @@ __global__ __launch_bounds__(kThreads) void moe_gemm_kernel(Gemm g, Out o)
     const int tiles = row_tiles * (g.n / kBN);
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = uniform(threadIdx.x / kWave);
-    const int wm = wave >> 1, wn = wave & 1;
+    const int grp = wave >> 2, s = wave & 3;               // waves w and w + 4 share a SIMD
     float* c = reinterpret_cast<float*>(smem);
     int first = blockIdx.x;
     if (gridDim.x % kXcds == 0)
@@ -604,7 +634,7 @@ __global__ __launch_bounds__(kThreads) void moe_gemm_kernel(Gemm g, Out o)
     f32x16 acc[kTM][kTN];
     for (int tile = first; tile < tiles; tile += gridDim.x) {
         const TileRef tr = tile_ref(g, off, pre, row_tiles, tile);
-        gemm_tile(g, tr, smem, acc, wave, wm, wn, lane);
+        gemm_tile(g, tr, smem, acc, grp, s, lane);
         const nvfp4::RowScale rs = nvfp4::row_scale(expert_scale(o, tr.e));
         // the thread index taken afresh per tile: the epilogue's addresses
         // are then computed here, not hoisted out of the tile loop, where
@@ -614,7 +644,7 @@ __global__ __launch_bounds__(kThreads) void moe_gemm_kernel(Gemm g, Out o)
         const int el = tid & (kWave - 1);
         static_assert(kBM / kPassRows == kTM && kPassRows == 2 * 32, "one MFMA row tile per pass");
         auto pass = [&](auto p) {
-            stage_accumulators<decltype(p)::value>(c, acc, wm, wn, el);
+            stage_accumulators<decltype(p)::value>(c, acc, grp, s, el);
             __syncthreads();
             epilogue(g, tr, decltype(p)::value, c, o, rs, tid);
             __syncthreads();   // the next pass (or tile) overwrites the buffer
