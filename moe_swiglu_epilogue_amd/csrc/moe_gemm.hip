@@ -263,28 +263,37 @@ __device__ __forceinline__ void load_lds16(const u32x4& rsrc, uint32_t lds, int 
                  :: "s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "memory");
 }
 
-// Group 0 wave s's share of the w slice at K offset k0 into the stage at
-// LDS address `base`: staged w rows 64 s .. +64, 8 loads.
+// Load jj (0..7) of group 0 wave s's share of the w slice at K offset k0
+// into the stage at LDS address `base`: staged w rows 64 s + 8 jj .. +8.
 static_assert(kDmaRows == 8, "the swizzle and offsets assume 8-row loads");
+__device__ __forceinline__ void load_w_one(const TileSrc& src, uint32_t base, int k0, int s, int jj)
+{
+    const int row = 64 * s + 8 * jj;
+    load_lds16(src.w, base + kRegionBytes + row * kRowBytes, src.vw[jj & 1],
+               uniform(row * src.row_w + 2 * k0));
+}
+
+// Load i (0..3) of group 1 wave s's share of one half of the x slice at K
+// offset k0: staged x rows 128 half + 32 s + 8 i .. +8.
+__device__ __forceinline__ void load_x_one(const TileSrc& src, uint32_t base, int k0, int s,
+                                           int half, int i)
+{
+    const int row = 128 * half + 32 * s + 8 * i;
+    load_lds16(src.x, base + row * kRowBytes, src.vx[4 * half + i], uniform(2 * k0));
+}
+
 __device__ __forceinline__ void load_w(const TileSrc& src, uint32_t base, int k0, int s)
 {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const int row = 64 * s + 8 * j;
-        load_lds16(src.w, base + kRegionBytes + row * kRowBytes, src.vw[j & 1],
-                   uniform(row * src.row_w + 2 * k0));
-    }
+    for (int jj = 0; jj < 8; ++jj)
+        load_w_one(src, base, k0, s, jj);
 }
 
-// Group 1 wave s's share of one half of the x slice at K offset k0: staged
-// x rows 128 half + 32 s .. +32, 4 loads.
 __device__ __forceinline__ void load_x(const TileSrc& src, uint32_t base, int k0, int s, int half)
 {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int row = 128 * half + 32 * s + 8 * i;
-        load_lds16(src.x, base + row * kRowBytes, src.vx[4 * half + i], uniform(2 * k0));
-    }
+    for (int i = 0; i < 4; ++i)
+        load_x_one(src, base, k0, s, half, i);
 }
 
 // The wave's MFMA operands for a whole staged slice: for each 16-deep K
@@ -295,24 +304,32 @@ struct SliceFrags {
     bf16x8 a[kKSteps][kTM], b[kKSteps][kTN];
 };
 
-__device__ __forceinline__ void read_slice(SliceFrags& f, const uint8_t* stage, int grp, int s,
-                                           int lane)
+// A lane's byte offset of K step kk within a staged row group: rows
+// 32 t + lane % 32 (+ a multiple of 32), so swz depends on the lane only,
+// and chunk 2 kk + lane / 32 sits in slot (2 kk) ^ (lane / 32 ^ swz).
+struct FragOffset {
+    int row, c0;
+    __device__ __forceinline__ explicit FragOffset(int lane)
+        : row((lane & 31) * kRowBytes), c0((lane >> 5) ^ swz(lane & 31)) {}
+    __device__ __forceinline__ int at(int kk) const { return row + (((2 * kk) ^ c0) << 4); }
+};
+
+__device__ __forceinline__ void read_a(SliceFrags& f, const uint8_t* stage, int grp, int kk,
+                                       const FragOffset& fo)
 {
-    // rows 32 t + lane % 32 (+ a multiple of 32): swz depends on the lane only
-    const int row = (lane & 31) * kRowBytes;
-    const int c0 = (lane >> 5) ^ swz(lane & 31);            // chunk of K step kk: 2 kk ^ c0
 #pragma unroll
-    for (int kk = 0; kk < kKSteps; ++kk) {
-        const int off = row + (((2 * kk) ^ c0) << 4);
+    for (int t = 0; t < kTM; ++t)
+        f.a[kk][t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
+                                                    stage + (kWaveM * grp + 32 * t) * kRowBytes + fo.at(kk)));
+}
+
+__device__ __forceinline__ void read_b(SliceFrags& f, const uint8_t* stage, int s, int kk,
+                                       const FragOffset& fo)
+{
 #pragma unroll
-        for (int t = 0; t < kTM; ++t)
-            f.a[kk][t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
-                                                        stage + (kWaveM * grp + 32 * t) * kRowBytes + off));
-#pragma unroll
-        for (int t = 0; t < kTN; ++t)
-            f.b[kk][t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
-                                                        stage + kRegionBytes + (kWaveN * s + 32 * t) * kRowBytes + off));
-    }
+    for (int t = 0; t < kTN; ++t)
+        f.b[kk][t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
+                                                    stage + kRegionBytes + (kWaveN * s + 32 * t) * kRowBytes + fo.at(kk)));
 }
 
 constexpr int kSliceMfmas = kKSteps * kTM * kTN;             // 32
@@ -363,21 +380,28 @@ __device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)"
 // are in flight, and a barrier costs a few cycles instead of the drift
 // between four waves that all compute. Slice j sits in stage j % 2.
 //
-// The LDS-DMA loads are issued in the read phases: a load can stall the
-// issuing wave for tens of cycles while the CU's vector memory path (about
-// 64 bytes per clock, so about 1024 clocks per 64 KB slice) works through
-// the loads before it, which a read phase has time for and an MFMA stream
-// has not. They are spread over both groups' read phases, 32 loads each,
-// by what each group reads: group 0 reads x rows 0-127 and all of w, group
-// 1 rows 128-255 and all of w.
+// The LDS-DMA loads are issued in the read phases, two after each K step's
+// fragment reads: a load can stall the issuing wave for tens of cycles
+// while the CU's vector memory path (about 64 bytes per clock, so about
+// 1024 clocks per 64 KB slice) works through the loads before it, which a
+// read phase has time for and an MFMA stream has not, and the LDS reads
+// proceed meanwhile. They are spread over both groups' read phases, 32
+// loads each, by what each group reads: group 0 reads x rows 0-127 and all
+// of w, group 1 rows 128-255 and all of w.
 //   * phase 2j: group 0 loads w of slice j + 1 into stage (j + 1) % 2 (both
-//     groups read the w there, of slice j - 1, in phases 2j - 2 and 2j - 1),
-//     and waits for it at the end of phase 2j + 1;
+//     groups read the w there, of slice j - 1, in phases 2j - 2 and 2j - 1).
+//     Wave s of group 0 loads exactly the w rows its own B fragments read
+//     (64 s .. +64), so it waits for them only in phase 2j + 2, after its x
+//     fragment reads and before its w ones; group 1's wave s reads them in
+//     phase 2j + 3, past the barrier. No MFMA phase of group 0 waits.
 //   * phase 2j + 1: group 1 loads the lower x half of slice j + 1 into stage
-//     (j + 1) % 2 (it read the one there itself in phase 2j - 1) and waits
-//     for it at the end of phase 2j + 2, and the upper x half of slice j + 2
-//     into stage j % 2 (group 0 read the one there in phase 2j), waiting for
-//     it at the end of phase 2j + 3, before group 0 reads it in phase 2j + 4.
+//     (j + 1) % 2 (it read the one there itself in phase 2j - 1) and the
+//     upper x half of slice j + 2 into stage j % 2 (group 0 read the one
+//     there in phase 2j). All of group 1 reads the lower half in phase
+//     2j + 3, so group 1 waits for it at the end of phase 2j + 2 (measured:
+//     about 85 clocks of its 1100-clock MFMA phase); it waits for the upper
+//     half at the end of phase 2j + 3, before group 0 reads it in phase
+//     2j + 4.
 // Each wave waits for its own reads before the barrier that closes its read
 // phase, so a stage part is free when the next barrier has passed; waits for
 // loads use the exact in-order count of loads issued after them (or wait for
@@ -419,19 +443,47 @@ __device__ __forceinline__ void gemm_tile(const Gemm& g, const TileRef& tr, uint
             wait_loads();
         phase_barrier();
     }
+    const FragOffset fo(lane);
     for (int j = 0; j < slices; ++j) {
         const uint32_t cur = uniform((j & 1) * kStageBytes), nxt = uniform(((j + 1) & 1) * kStageBytes);
+        const bool next = j + 1 < slices, more = j + 2 < slices;
+        const uint8_t* stage = smem + cur;
         SliceFrags f;
-        read_slice(f, smem + cur, grp, s, lane);
-        const bool more = j + 2 < slices;
         if (g0) {
-            if (j + 1 < slices)
-                load_w(src, stages + nxt, (j + 1) * kBK, s);
+            // x fragments, two w loads of slice j + 1 after each K step's;
+            // then this wave's own w rows of slice j (8 loads were issued
+            // after them), and the w fragments
+#pragma unroll
+            for (int kk = 0; kk < kKSteps; ++kk) {
+                read_a(f, stage, grp, kk, fo);
+                if (next) {
+                    load_w_one(src, stages + nxt, (j + 1) * kBK, s, 2 * kk);
+                    load_w_one(src, stages + nxt, (j + 1) * kBK, s, 2 * kk + 1);
+                }
+            }
+            if (next)
+                asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+            else
+                wait_loads();
+#pragma unroll
+            for (int kk = 0; kk < kKSteps; ++kk)
+                read_b(f, stage, s, kk, fo);
         } else {
-            if (j + 1 < slices)
-                load_x(src, stages + nxt, (j + 1) * kBK, s, 1);
-            if (more)
-                load_x(src, stages + cur, (j + 2) * kBK, s, 0);
+            // each K step's fragments, then two loads: the lower x half of
+            // slice j + 1 after steps 0 and 1, the upper x half of slice
+            // j + 2 after steps 2 and 3
+#pragma unroll
+            for (int kk = 0; kk < kKSteps; ++kk) {
+                read_a(f, stage, grp, kk, fo);
+                read_b(f, stage, s, kk, fo);
+                if (kk < 2 && next) {
+                    load_x_one(src, stages + nxt, (j + 1) * kBK, s, 1, 2 * kk);
+                    load_x_one(src, stages + nxt, (j + 1) * kBK, s, 1, 2 * kk + 1);
+                } else if (kk >= 2 && more) {
+                    load_x_one(src, stages + cur, (j + 2) * kBK, s, 0, 2 * kk - 4);
+                    load_x_one(src, stages + cur, (j + 2) * kBK, s, 0, 2 * kk - 3);
+                }
+            }
         }
         wait_lds_reads();
         if (!g0) {
@@ -443,12 +495,12 @@ __device__ __forceinline__ void gemm_tile(const Gemm& g, const TileRef& tr, uint
         }
         phase_barrier();
         mma_slice(acc, f);
-        if (g0)
-            wait_loads();                                  // w of slice j + 1
-        else if (more)
-            asm volatile("s_waitcnt vmcnt(4)" ::: "memory");     // lower x half of slice j + 1
-        else
-            wait_loads();
+        if (!g0) {
+            if (more)
+                asm volatile("s_waitcnt vmcnt(4)" ::: "memory");     // lower x half of slice j + 1
+            else
+                wait_loads();
+        }
         phase_barrier();
     }
     if (g0)
