@@ -565,6 +565,24 @@ __device__ __forceinline__ float swiglu_f32(float g, float u)
     return (float)__builtin_ldexp((double)g * (double)u * (double)ss, -kk);
 }
 
+// swiglu_f32 for |g| < 44: there -p / 64 < 1, so k = 0, every shift is by
+// zero and p + 0 = p (a zero p included: exp2(+0) = exp2(-0)); this is the
+// same arithmetic with those steps left out, so the results are identical.
+__device__ __forceinline__ float swiglu_f32_small(float g, float u)
+{
+    const float kL2eHi = 0x1.715476p+0f;
+    const float kL2eLo = 0x1.4ae0bep-26f;
+    const float kLn2 = 0x1.62e430p-1f;
+    const float a = __builtin_fabsf(g);
+    const float p = -a * kL2eHi;
+    const float perr = __builtin_fmaf(-a, kL2eHi, -p);
+    const float t = __builtin_fmaf(-a, kL2eLo, perr);
+    const float es = __builtin_amdgcn_exp2f(p) * __builtin_fmaf(t, kLn2, 1.0f);
+    const float r = __builtin_amdgcn_rcpf(1.0f + es);
+    const float ss = g < 0.0f ? es * r : r;
+    return (float)((double)g * (double)u * (double)ss);
+}
+
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
 {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
@@ -601,10 +619,24 @@ __device__ __forceinline__ void fused_block(const Gemm& g, const TileRef& tr, in
         v[4 * q + 3] = f.w;
     }
     float y[16];
+    // the largest gate magnitude (a NaN gate is dropped by the max, and gives
+    // NaN on either path)
+    float gmax = 0.0f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        y[j] = swiglu_f32(v[j], v[8 + j]);
-        y[8 + j] = swiglu_f32(v[16 + j], v[24 + j]);
+    for (int j = 0; j < 8; ++j)
+        gmax = __builtin_fmaxf(gmax, __builtin_fmaxf(__builtin_fabsf(v[j]), __builtin_fabsf(v[16 + j])));
+    if (gmax < 44.0f) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            y[j] = swiglu_f32_small(v[j], v[8 + j]);
+            y[8 + j] = swiglu_f32_small(v[16 + j], v[24 + j]);
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            y[j] = swiglu_f32(v[j], v[8 + j]);
+            y[8 + j] = swiglu_f32(v[16 + j], v[24 + j]);
+        }
     }
     uint32_t sf;
     const uint2 q = nvfp4::quantize16<true, false>(y, nvfp4::block_amax(y), rs, sf);
