@@ -68,8 +68,10 @@ constexpr int kDmaRows = kWave * 16 / kRowBytes;          // staged rows one LDS
 constexpr int kPassRows = 64;                             // epilogue rows per pass
 constexpr int kCPitch = kBN + 4;                          // floats per LDS row of the C buffer
 constexpr int kCBytes = kPassRows * kCPitch * 4;          // 66,560 B
-constexpr int kLdsBytes = 2 * kStageBytes;
-static_assert(kCBytes <= kLdsBytes, "the C buffer overlays the operand stages");
+// The C buffer overlays stage 1 and the 1 KB after it, so that stage 0 can
+// take the next tile's first slice during the epilogue.
+constexpr int kLdsBytes = kStageBytes + kCBytes;
+static_assert(kCBytes >= kStageBytes, "the C buffer covers stage 1");
 constexpr int kMi355xCUs = 256;
 constexpr int kXcds = 8;
 constexpr int64_t kMaxPitch = int64_t(1) << 22;            // elements; 256 rows < 2^31 bytes
@@ -408,7 +410,17 @@ __device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)"
 // all at the end of the K loop). Every wave runs 2 + 2 K / 64 barriers
 // (s_barrier counts arrivals, not places in the code). Ends after the last
 // slice's MFMAs have issued, with every LDS read and load complete.
-__device__ __forceinline__ void gemm_tile(const Gemm& g, const TileRef& tr, uint8_t* smem,
+__device__ __forceinline__ void load_slice0(const TileSrc& src, uint32_t stages, int grp, int s)
+{
+    if (grp == 0) {
+        load_w(src, stages, 0, s);
+    } else {
+        load_x(src, stages, 0, s, 0);
+        load_x(src, stages, 0, s, 1);
+    }
+}
+
+__device__ __forceinline__ void gemm_tile(const Gemm& g, const TileSrc& src, uint8_t* smem,
                                           f32x16 (&acc)[kTM][kTN], int grp, int s, int lane)
 {
 #pragma unroll
@@ -418,31 +430,21 @@ __device__ __forceinline__ void gemm_tile(const Gemm& g, const TileRef& tr, uint
             acc[tm][tn] = f32x16{};
     const int slices = g.k / kBK;
     const bool g0 = grp == 0;
-    const TileSrc src = tile_src(g, tr, s);
     const uint32_t stages = lds_addr(smem);
-    // slice 0 (all of it) and the upper x half of slice 1
+    // slice 0 was issued by load_slice0 (group 0 its w, group 1 its two x
+    // halves, while the previous tile's epilogue ran); group 1 adds the
+    // upper x half of slice 1 and waits for slice 0's (4 loads after them)
     if (g0) {
-        load_w(src, stages, 0, s);
         wait_loads();
+    } else if (slices > 1) {
+        load_x(src, stages + kStageBytes, kBK, s, 0);
+        asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
     } else {
-        load_x(src, stages, 0, s, 0);
-        load_x(src, stages, 0, s, 1);
-        if (slices > 1) {
-            load_x(src, stages + kStageBytes, kBK, s, 0);
-            asm volatile("s_waitcnt vmcnt(8)" ::: "memory");     // upper x half of slice 0
-        } else {
-            asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-        }
+        wait_loads();
     }
-    phase_barrier();                                       // slice 0's upper half and w staged
-    if (!g0) {
-        // group 1 idles through phase 0: the lower x half of slice 0
-        if (slices > 1)
-            asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-        else
-            wait_loads();
-        phase_barrier();
-    }
+    phase_barrier();                                       // slice 0 is staged
+    if (!g0)
+        phase_barrier();                                   // group 1 idles through phase 0
     const FragOffset fo(lane);
     for (int j = 0; j < slices; ++j) {
         const uint32_t cur = uniform((j & 1) * kStageBytes), nxt = uniform(((j + 1) & 1) * kStageBytes);
@@ -711,15 +713,34 @@ __global__ __launch_bounds__(kThreads) void moe_gemm_kernel(Gemm g, Out o)
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = uniform(threadIdx.x / kWave);
     const int grp = wave >> 2, s = wave & 3;               // waves w and w + 4 share a SIMD
-    float* c = reinterpret_cast<float*>(smem);
+    float* c = reinterpret_cast<float*>(smem + kStageBytes);
+    const uint32_t stages = lds_addr(smem);
     int first = blockIdx.x;
     if (gridDim.x % kXcds == 0)
         first = (blockIdx.x % kXcds) * (gridDim.x / kXcds) + blockIdx.x / kXcds;
     f32x16 acc[kTM][kTN];
+    TileRef next_tr{};
+    TileSrc next_src{};
+    if (first < tiles) {
+        next_tr = tile_ref(g, off, pre, row_tiles, first);
+        next_src = tile_src(g, next_tr, s);
+        load_slice0(next_src, stages, grp, s);
+    }
     for (int tile = first; tile < tiles; tile += gridDim.x) {
-        const TileRef tr = tile_ref(g, off, pre, row_tiles, tile);
-        gemm_tile(g, tr, smem, acc, grp, s, lane);
-        const nvfp4::RowScale rs = nvfp4::row_scale(expert_scale(o, tr.e));
+        const TileRef tr = next_tr;
+        gemm_tile(g, next_src, smem, acc, grp, s, lane);
+        // the expert's scale, consumed here: a wait for it placed after the
+        // loads below would wait for them too
+        float gs = expert_scale(o, tr.e);
+        asm volatile("" : "+v"(gs));
+        const nvfp4::RowScale rs = nvfp4::row_scale(gs);
+        // the next tile's slice 0 into stage 0, free now that every wave has
+        // passed the K loop's last barrier; it lands during this epilogue
+        if (tile + (int)gridDim.x < tiles) {
+            next_tr = tile_ref(g, off, pre, row_tiles, tile + gridDim.x);
+            next_src = tile_src(g, next_tr, s);
+            load_slice0(next_src, stages, grp, s);
+        }
         // the thread index taken afresh per tile: the epilogue's addresses
         // are then computed here, not hoisted out of the tile loop, where
         // they would stay live through the K loop and crowd its registers
