@@ -420,7 +420,7 @@ __device__ __forceinline__ void load_slice0(const TileSrc& src, uint32_t stages,
     }
 }
 
-__device__ __forceinline__ void gemm_tile(const Gemm& g, const TileSrc& src, uint8_t* smem,
+__device__ __forceinline__ void gemm_tile(const Gemm& g, const TileRef& tr, uint8_t* smem,
                                           f32x16 (&acc)[kTM][kTN], int grp, int s, int lane)
 {
 #pragma unroll
@@ -430,6 +430,7 @@ __device__ __forceinline__ void gemm_tile(const Gemm& g, const TileSrc& src, uin
             acc[tm][tn] = f32x16{};
     const int slices = g.k / kBK;
     const bool g0 = grp == 0;
+    const TileSrc src = tile_src(g, tr, s);
     const uint32_t stages = lds_addr(smem);
     // slice 0 was issued by load_slice0 (group 0 its w, group 1 its two x
     // halves, while the previous tile's epilogue ran); group 1 adds the
@@ -720,15 +721,13 @@ __global__ __launch_bounds__(kThreads) void moe_gemm_kernel(Gemm g, Out o)
         first = (blockIdx.x % kXcds) * (gridDim.x / kXcds) + blockIdx.x / kXcds;
     f32x16 acc[kTM][kTN];
     TileRef next_tr{};
-    TileSrc next_src{};
     if (first < tiles) {
         next_tr = tile_ref(g, off, pre, row_tiles, first);
-        next_src = tile_src(g, next_tr, s);
-        load_slice0(next_src, stages, grp, s);
+        load_slice0(tile_src(g, next_tr, s), stages, grp, s);
     }
     for (int tile = first; tile < tiles; tile += gridDim.x) {
         const TileRef tr = next_tr;
-        gemm_tile(g, next_src, smem, acc, grp, s, lane);
+        gemm_tile(g, tr, smem, acc, grp, s, lane);
         // the expert's scale, consumed here: a wait for it placed after the
         // loads below would wait for them too
         float gs = expert_scale(o, tr.e);
@@ -738,8 +737,7 @@ __global__ __launch_bounds__(kThreads) void moe_gemm_kernel(Gemm g, Out o)
         // passed the K loop's last barrier; it lands during this epilogue
         if (tile + (int)gridDim.x < tiles) {
             next_tr = tile_ref(g, off, pre, row_tiles, tile + gridDim.x);
-            next_src = tile_src(g, next_tr, s);
-            load_slice0(next_src, stages, grp, s);
+            load_slice0(tile_src(g, next_tr, s), stages, grp, s);
         }
         // the thread index taken afresh per tile: the epilogue's addresses
         // are then computed here, not hoisted out of the tile loop, where

@@ -156,18 +156,38 @@ def gemm_isa(tmp_path_factory):
     return out.read_text()
 
 
+def _mfma_loop(body):
+    """The lines of the loop that holds the MFMAs (the K loop): from its
+    header label to the branch back to it. Within it the tile's buffer
+    descriptors are loop-invariant and stay in the same SGPRs."""
+    best = None
+    for i, l in enumerate(body):
+        m = re.match(r"(\.LBB\d+_\d+):", l)
+        if not m:
+            continue
+        back = [k for k in range(i + 1, len(body))
+                if re.match(r"s_(cbranch_\w+|branch) " + re.escape(m.group(1)) + r"$", body[k])]
+        if back and any(x.startswith("v_mfma") for x in body[i:back[-1]]):
+            span = (i, back[-1])
+            if best is None or span[1] - span[0] < best[1] - best[0]:
+                best = span
+    assert best is not None
+    return body[best[0]:best[1] + 1]
+
+
 def test_gemm_x_rows_are_range_checked(gemm_isa):
     ks = {n: b for n, b in _kernels(gemm_isa).items() if "moe_gemm_kernel" in n}
     assert len(ks) == 2, sorted(ks)
     for name, body in ks.items():
         voffsets = {}
-        for l in body:
+        for l in _mfma_loop(body):
             m = re.match(r"buffer_load_dwordx4 (?:v\[\d+:\d+\], )?(v\d+), (s\[\d+:\d+\]), \S+ offen", l)
             if m:
                 voffsets.setdefault(m.group(2), set()).add(m.group(1))
-        # the x resource (in whichever SGPRs it sits) is loaded through 8
-        # distinct VGPR offsets, one per row a lane loads; w through at most 2
-        # (its row step is in the SGPR offset: every w row is inside its window)
+        # in the K loop the x resource (in whichever SGPRs it sits) is loaded
+        # through 8 distinct VGPR offsets, one per row a lane loads; w through
+        # at most 2 (its row step is in the SGPR offset: every w row is inside
+        # its window)
         counts = sorted(len(v) for v in voffsets.values())
         assert 8 in counts and set(counts) <= {1, 2, 8}, (name, counts)
 
