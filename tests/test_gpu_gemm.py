@@ -71,14 +71,16 @@ def gs_rows_of(g, gs, rows=None):
     return r if rows is None else r[rows]
 
 
-# hidden / 64 K slices: 1, 2, 3, 4, 5, 8, 16 and 64. The K loop has a first
-# slice, a middle loop (slices 1 .. n - 2, each loading the next) and a last
-# slice, with the last K step's MFMAs of each slice issued after the next
-# barrier: one slice runs the first alone, two the first and the last, three
-# or more all three parts.
+# hidden / 64 K slices: 1, 2, 3, 4, 5, 8, 16 and 64. The K loop loads slices
+# one and two ahead with waits counted for the steady state; one slice loads
+# nothing in the loop, two load only the first slice's successor, three or
+# more run the steady state and its last two slices. The last two cases have
+# more than 256 tiles, so some workgroups take a second tile, whose first
+# slice is loaded during the first tile's epilogue (with one and two slices).
 @pytest.mark.parametrize("tokens,hidden,inter,experts,seed", [
     (300, 256, 128, 5, 1), (1000, 512, 384, 9, 2), (257, 64, 128, 1, 3), (513, 1024, 256, 3, 4),
-    (256, 4096, 128, 2, 5), (130, 128, 128, 2, 6), (260, 192, 256, 2, 7), (511, 320, 128, 4, 8)])
+    (256, 4096, 128, 2, 5), (130, 128, 128, 2, 6), (260, 192, 256, 2, 7), (511, 320, 128, 4, 8),
+    (40000, 64, 256, 3, 9), (40000, 128, 256, 5, 10)])
 def test_gemm_exact_operands(M, tokens, hidden, inter, experts, seed):
     g = W.moe_gemm(seed, tokens, hidden, inter, experts, exact=True)
     acc = oracle.moe_l1_gemm(g.x, g.w1, g.offsets)
