@@ -23,8 +23,8 @@
 // 256 x 256 output tiles; group G of 4 waves owns rows 128 G .. +128 and
 // wave s of it columns 64 s .. +64, as 4 x 2 MFMA tiles of 32 x 32 (128
 // accumulator registers per lane). The K loop stages 256 x 64 slices of x
-// and w in LDS (double-buffered, 16-byte chunks XOR-swizzled against bank
-// conflicts). The slices arrive by buffer loads straight into LDS
+// and w in LDS (double-buffered, the lower half of x triple-buffered;
+// 16-byte chunks XOR-swizzled against bank conflicts). The slices arrive by buffer loads straight into LDS
 // (buffer_load_dwordx4 ... lds, 16 bytes per lane on gfx950), so no
 // register holds them on the way. The loop is a ping-pong: the two waves of
 // each SIMD take turns issuing a slice's 32 MFMAs and reading the next
@@ -69,9 +69,19 @@ constexpr int kPassRows = 64;                             // epilogue rows per p
 constexpr int kCPitch = kBN + 4;                          // floats per LDS row of the C buffer
 constexpr int kCBytes = kPassRows * kCPitch * 4;          // 66,560 B
 // The C buffer overlays stage 1 and the 1 KB after it, so that stage 0 can
-// take the next tile's first slice during the epilogue.
-constexpr int kLdsBytes = kStageBytes + kCBytes;
+// take the next tile's first slice during the epilogue. The lower half of
+// the x slice (rows 128-255, group 1's) cycles through three slots: the
+// lower-half regions of the two stages and one more after the C buffer.
+constexpr int kHalfBytes = kRegionBytes / 2;              // 16 KB: 128 staged x rows
+constexpr int kSlot2 = kStageBytes + kCBytes;
+constexpr int kLdsBytes = kSlot2 + kHalfBytes;
 static_assert(kCBytes >= kStageBytes, "the C buffer covers stage 1");
+
+// LDS offset of lower-x-half slot k (0, 1, 2).
+__device__ __forceinline__ uint32_t xbot_slot(int k)
+{
+    return k == 2 ? (uint32_t)kSlot2 : (uint32_t)(k * kStageBytes + kHalfBytes);
+}
 constexpr int kMi355xCUs = 256;
 constexpr int kXcds = 8;
 constexpr int64_t kMaxPitch = int64_t(1) << 22;            // elements; 256 rows < 2^31 bytes
@@ -276,11 +286,14 @@ __device__ __forceinline__ void load_w_one(const TileSrc& src, uint32_t base, in
 }
 
 // Load i (0..3) of group 1 wave s's share of one half of the x slice at K
-// offset k0: staged x rows 128 half + 32 s + 8 i .. +8.
+// offset k0: x rows 128 half + 32 s + 8 i .. +8 of the tile, staged at rows
+// 32 s + 8 i .. +8 from LDS address `base` (the start of the half's 128
+// rows: the stage for the upper half, a slot for the lower; the swizzle
+// depends on the row modulo 16 only).
 __device__ __forceinline__ void load_x_one(const TileSrc& src, uint32_t base, int k0, int s,
                                            int half, int i)
 {
-    const int row = 128 * half + 32 * s + 8 * i;
+    const int row = 32 * s + 8 * i;
     load_lds16(src.x, base + row * kRowBytes, src.vx[4 * half + i], uniform(2 * k0));
 }
 
@@ -316,13 +329,14 @@ struct FragOffset {
     __device__ __forceinline__ int at(int kk) const { return row + (((2 * kk) ^ c0) << 4); }
 };
 
-__device__ __forceinline__ void read_a(SliceFrags& f, const uint8_t* stage, int grp, int kk,
+// A fragments of K step kk from the wave's 128 staged x rows at `xrows`.
+__device__ __forceinline__ void read_a(SliceFrags& f, const uint8_t* xrows, int kk,
                                        const FragOffset& fo)
 {
 #pragma unroll
     for (int t = 0; t < kTM; ++t)
         f.a[kk][t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
-                                                    stage + (kWaveM * grp + 32 * t) * kRowBytes + fo.at(kk)));
+                                                    xrows + 32 * t * kRowBytes + fo.at(kk)));
 }
 
 __device__ __forceinline__ void read_b(SliceFrags& f, const uint8_t* stage, int s, int kk,
@@ -380,7 +394,8 @@ __device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)"
 // (group 1 idles through phase 0, group 0 through the last phase), so each
 // SIMD's matrix core runs one wave's MFMAs while the other wave's LDS reads
 // are in flight, and a barrier costs a few cycles instead of the drift
-// between four waves that all compute. Slice j sits in stage j % 2.
+// between four waves that all compute. Slice j sits in stage j % 2, its
+// lower x half in slot j % 3 of a ring of three.
 //
 // The LDS-DMA loads are issued in the read phases, two after each K step's
 // fragment reads: a load can stall the issuing wave for tens of cycles
@@ -396,14 +411,14 @@ __device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)"
 //     (64 s .. +64), so it waits for them only in phase 2j + 2, after its x
 //     fragment reads and before its w ones; group 1's wave s reads them in
 //     phase 2j + 3, past the barrier. No MFMA phase of group 0 waits.
-//   * phase 2j + 1: group 1 loads the lower x half of slice j + 1 into stage
-//     (j + 1) % 2 (it read the one there itself in phase 2j - 1) and the
-//     upper x half of slice j + 2 into stage j % 2 (group 0 read the one
-//     there in phase 2j). All of group 1 reads the lower half in phase
-//     2j + 3, so group 1 waits for it at the end of phase 2j + 2 (measured:
-//     about 85 clocks of its 1100-clock MFMA phase); it waits for the upper
-//     half at the end of phase 2j + 3, before group 0 reads it in phase
-//     2j + 4.
+//   * phase 2j + 1: group 1 loads both x halves of slice j + 2: the upper
+//     half into stage j % 2 (group 0 read the one there in phase 2j), the
+//     lower half into slot (j + 2) % 3 of a three-slot ring (it read the
+//     one there itself in phase 2j - 1). It waits for slice j + 1's halves
+//     at the end of the same read phase, before the barrier, so no MFMA
+//     phase waits for loads. (With the lower half double-buffered like the
+//     rest, its window was one phase shorter and group 1 waited for it at
+//     the end of its MFMA phases, about 85 clocks each.)
 // Each wave waits for its own reads before the barrier that closes its read
 // phase, so a stage part is free when the next barrier has passed; waits for
 // loads use the exact in-order count of loads issued after them (or wait for
@@ -416,7 +431,7 @@ __device__ __forceinline__ void load_slice0(const TileSrc& src, uint32_t stages,
         load_w(src, stages, 0, s);
     } else {
         load_x(src, stages, 0, s, 0);
-        load_x(src, stages, 0, s, 1);
+        load_x(src, stages + xbot_slot(0), 0, s, 1);
     }
 }
 
@@ -433,13 +448,14 @@ __device__ __forceinline__ void gemm_tile(const Gemm& g, const TileRef& tr, uint
     const TileSrc src = tile_src(g, tr, s);
     const uint32_t stages = lds_addr(smem);
     // slice 0 was issued by load_slice0 (group 0 its w, group 1 its two x
-    // halves, while the previous tile's epilogue ran); group 1 adds the
-    // upper x half of slice 1 and waits for slice 0's (4 loads after them)
+    // halves, while the previous tile's epilogue ran); group 1 adds both x
+    // halves of slice 1 and waits for slice 0's (8 loads after them)
     if (g0) {
         wait_loads();
     } else if (slices > 1) {
         load_x(src, stages + kStageBytes, kBK, s, 0);
-        asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+        load_x(src, stages + xbot_slot(1), kBK, s, 1);
+        asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
     } else {
         wait_loads();
     }
@@ -447,10 +463,12 @@ __device__ __forceinline__ void gemm_tile(const Gemm& g, const TileRef& tr, uint
     if (!g0)
         phase_barrier();                                   // group 1 idles through phase 0
     const FragOffset fo(lane);
+    int slot = 0;                                          // j % 3: lower x half of slice j
     for (int j = 0; j < slices; ++j) {
         const uint32_t cur = uniform((j & 1) * kStageBytes), nxt = uniform(((j + 1) & 1) * kStageBytes);
         const bool next = j + 1 < slices, more = j + 2 < slices;
         const uint8_t* stage = smem + cur;
+        const int slot2 = slot == 0 ? 2 : slot - 1;        // (j + 2) % 3
         SliceFrags f;
         if (g0) {
             // x fragments, two w loads of slice j + 1 after each K step's;
@@ -458,7 +476,7 @@ __device__ __forceinline__ void gemm_tile(const Gemm& g, const TileRef& tr, uint
             // after them), and the w fragments
 #pragma unroll
             for (int kk = 0; kk < kKSteps; ++kk) {
-                read_a(f, stage, grp, kk, fo);
+                read_a(f, stage, kk, fo);
                 if (next) {
                     load_w_one(src, stages + nxt, (j + 1) * kBK, s, 2 * kk);
                     load_w_one(src, stages + nxt, (j + 1) * kBK, s, 2 * kk + 1);
@@ -472,25 +490,28 @@ __device__ __forceinline__ void gemm_tile(const Gemm& g, const TileRef& tr, uint
             for (int kk = 0; kk < kKSteps; ++kk)
                 read_b(f, stage, s, kk, fo);
         } else {
-            // each K step's fragments, then two loads: the lower x half of
-            // slice j + 1 after steps 0 and 1, the upper x half of slice
-            // j + 2 after steps 2 and 3
+            // each K step's fragments, then two loads of slice j + 2: its
+            // lower x half into slot (j + 2) % 3 after steps 0 and 1, its
+            // upper half into stage j % 2 after steps 2 and 3
+            const uint8_t* xrows = smem + xbot_slot(slot);
 #pragma unroll
             for (int kk = 0; kk < kKSteps; ++kk) {
-                read_a(f, stage, grp, kk, fo);
+                read_a(f, xrows, kk, fo);
                 read_b(f, stage, s, kk, fo);
-                if (kk < 2 && next) {
-                    load_x_one(src, stages + nxt, (j + 1) * kBK, s, 1, 2 * kk);
-                    load_x_one(src, stages + nxt, (j + 1) * kBK, s, 1, 2 * kk + 1);
-                } else if (kk >= 2 && more) {
-                    load_x_one(src, stages + cur, (j + 2) * kBK, s, 0, 2 * kk - 4);
-                    load_x_one(src, stages + cur, (j + 2) * kBK, s, 0, 2 * kk - 3);
+                if (more) {
+                    if (kk < 2) {
+                        load_x_one(src, stages + xbot_slot(slot2), (j + 2) * kBK, s, 1, 2 * kk);
+                        load_x_one(src, stages + xbot_slot(slot2), (j + 2) * kBK, s, 1, 2 * kk + 1);
+                    } else {
+                        load_x_one(src, stages + cur, (j + 2) * kBK, s, 0, 2 * kk - 4);
+                        load_x_one(src, stages + cur, (j + 2) * kBK, s, 0, 2 * kk - 3);
+                    }
                 }
             }
         }
         wait_lds_reads();
         if (!g0) {
-            // the upper x half of slice j + 1 (8 loads were issued after it)
+            // both x halves of slice j + 1 (8 loads were issued after them)
             if (more)
                 asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
             else
@@ -498,13 +519,8 @@ __device__ __forceinline__ void gemm_tile(const Gemm& g, const TileRef& tr, uint
         }
         phase_barrier();
         mma_slice(acc, f);
-        if (!g0) {
-            if (more)
-                asm volatile("s_waitcnt vmcnt(4)" ::: "memory");     // lower x half of slice j + 1
-            else
-                wait_loads();
-        }
         phase_barrier();
+        slot = slot == 2 ? 0 : slot + 1;
     }
     if (g0)
         phase_barrier();                                   // group 0 idles through the last phase
