@@ -39,8 +39,9 @@
 // every XCD), and the loads are spread over the waves that are not issuing
 // MFMAs. 256 x 256 is the largest tile the registers of 8 waves hold with
 // their fragments (4 SIMDs x 2 waves x 32 KB of accumulators). The MFMA
-// streams take about 84% of the K loop's clocks; the clock itself is held
-// down by the board's power limit while the matrix cores are this busy.
+// streams take about 90% of the K loop's clocks (about 2200-2250 clocks per
+// slice against the 2048 of its MFMAs); the clock itself is held down by
+// the board's power limit while the matrix cores are this busy.
 //
 // Tiles are enumerated per expert (ceil(rows_e / 256) row tiles each, from a
 // prefix sum the workgroup builds once in LDS) and handed to a persistent,
