@@ -24,9 +24,9 @@
 // wave s of it columns 64 s .. +64, as 4 x 2 MFMA tiles of 32 x 32 (128
 // accumulator registers per lane). The K loop stages 256 x 64 slices of x
 // and w in LDS (double-buffered, the lower half of x triple-buffered;
-// 16-byte chunks XOR-swizzled against bank conflicts). The slices arrive by buffer loads straight into LDS
-// (buffer_load_dwordx4 ... lds, 16 bytes per lane on gfx950), so no
-// register holds them on the way. The loop is a ping-pong: the two waves of
+// 16-byte chunks XOR-swizzled against bank conflicts). The slices arrive by
+// buffer loads straight into LDS (buffer_load_dwordx4 ... lds, 16 bytes per
+// lane on gfx950), so no register holds them on the way. The loop is a ping-pong: the two waves of
 // each SIMD take turns issuing a slice's 32 MFMAs and reading the next
 // slice's fragments (and issuing loads), so one wave feeds the SIMD's
 // matrix core while the other waits on LDS and memory.
@@ -46,7 +46,8 @@
 // Tiles are enumerated per expert (ceil(rows_e / 256) row tiles each, from a
 // prefix sum the workgroup builds once in LDS) and handed to a persistent,
 // XCD-aware grid. The epilogue runs in four 64-row passes through an LDS
-// buffer that overlays the stages.
+// buffer that overlays stage 1, while stage 0 takes the next tile's first
+// slice.
 #include "../../include/moe_nvfp4.h"
 #include "nvfp4_device.hpp"
 
