@@ -681,6 +681,8 @@ def main():
     achieved = ALG_BYTES / (kern_ms / 1e3) / 1e9
     print("[bench] fused prefill: %.4f ms/step wall, %.4f ms/launch events, %.1f GB/s"
           % (ms_per_step, kern_ms, value), file=sys.stderr, flush=True)
+    # the timed launches' output, before any other measurement reuses the buffers
+    output_sha = {"packed": W.sha256(packed.cpu().numpy()), "scales": W.sha256(scales.cpu().numpy())}
 
     secondary = None
     if not args.no_secondary:
@@ -726,6 +728,7 @@ def main():
                      "kernel": "quantize_tiles_kernel<FusedBlock, true>",
                      "kernel_ms": round(kern_ms, 5),
                      "kernel_ms_p10_p50_p90": [round(pct(per, q), 5) for q in (0.1, 0.5, 0.9)]},
+        "output_sha256": output_sha,
         "cpu_baseline": cpu,
         "gpu_state": gpu_state,
         "secondary": secondary,
