@@ -219,7 +219,9 @@ nvfp4_status_t swiglu_bf16(const uint16_t *gate_up, int64_t rows, int64_t inter,
  *   packed[tokens][inter/2], scales[tokens][inter/16] and, if swiglu_out is
  *   not NULL, y [tokens][inter] FP32.
  * expert_offsets: as above (NULL: one expert, w1[0], owns every row);
- * num_experts <= 512. Shapes: hidden % 64 == 0, inter % 128 == 0, ld_x and
+ * num_experts <= 512. Offsets that break the rules give unspecified bytes
+ * but no access outside x, w1 and the outputs: the kernel clamps them to
+ * [0, tokens] and raises each to the largest one before it. Shapes: hidden % 64 == 0, inter % 128 == 0, ld_x and
  * ld_w >= hidden, multiples of 8 and below 2^22 (NVFP4_ERROR_UNSUPPORTED_SHAPE
  * otherwise: a 256-row operand window is addressed with 32-bit offsets); x
  * and w1 16-byte aligned. One kernel.

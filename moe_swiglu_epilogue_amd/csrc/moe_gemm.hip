@@ -126,10 +126,16 @@ struct TileRef {
     int n0;         // first output column
 };
 
-// Tile prefix in LDS: off[e] (clamped to [0, tokens]) and pre[e] = row tiles
-// of experts 0..e-1 (thread t counts experts 2t and 2t + 1; Hillis-Steele
-// scan over the threads). Returns the total number of row tiles.
-static_assert(2 * kThreads >= kMaxExperts, "two experts per thread in the tile prefix");
+// Tile prefix in LDS: off[e] and pre[e] = row tiles of experts 0..e-1
+// (thread t counts experts 2t and 2t + 1; Hillis-Steele scan over the
+// threads). Returns the total number of row tiles. off[e] is the offset
+// clamped to [0, tokens] and raised to the largest offset before it (a
+// running maximum, also by Hillis-Steele). Valid offsets are non-decreasing,
+// so neither step changes them. Offsets that break the rules then still give
+// disjoint row ranges inside [0, tokens): every access stays inside x, w1 and
+// the outputs, and the row tiles number at most ceil(tokens / 256) + E, the
+// bound the host checks against INT32_MAX.
+static_assert(2 * kThreads >= kMaxExperts + 1, "two offsets per thread in the tile prefix");
 __device__ int build_tile_prefix(const Gemm& g, int* off, int* pre, int* part)
 {
     const int t = threadIdx.x;
@@ -139,6 +145,17 @@ __device__ int build_tile_prefix(const Gemm& g, int* off, int* pre, int* part)
         off[i] = min(max(o, 0), g.tokens);
     }
     __syncthreads();
+    for (int d = 1; d <= E; d <<= 1) {
+        const int i0 = t, i1 = t + kThreads;
+        const int a0 = i0 <= E && i0 >= d ? off[i0 - d] : 0;
+        const int a1 = i1 <= E && i1 >= d ? off[i1 - d] : 0;
+        __syncthreads();
+        if (i0 <= E)
+            off[i0] = max(off[i0], a0);
+        if (i1 <= E)
+            off[i1] = max(off[i1], a1);
+        __syncthreads();
+    }
     const int e0 = 2 * t, e1 = 2 * t + 1;
     const int c0 = e0 < E ? (max(off[e0 + 1] - off[e0], 0) + kBM - 1) / kBM : 0;
     const int c1 = e1 < E ? (max(off[e1 + 1] - off[e1], 0) + kBM - 1) / kBM : 0;

@@ -117,6 +117,47 @@ def test_gemm_single_expert_no_offsets(M):
     P.assert_fused_ok(P.fused_report(r["p"], r["s"], r["y"], rp, rs, ry, rbsf, rv), "one expert")
 
 
+@pytest.mark.parametrize("tokens,offsets", [
+    (600, [0, 500, 100, 900, 300]),     # decreasing steps and an end past the rows
+    (300, [0, 300, 0, 300, 0]),         # every other expert claims all rows again
+    (300, [-50, 100, 200]),             # negative start; rows 200.. belong to no expert
+])
+def test_gemm_offsets_out_of_rule_stay_in_bounds(M, tokens, offsets):
+    """expert_offsets that break the rules (device data, not checked) give
+    unspecified bytes for the rows they cover but no access outside the
+    buffers. The kernel clamps the offsets to [0, tokens] and takes their
+    running maximum, so that the row ranges are disjoint; this pins that
+    handling: covered rows equal the oracle's GEMM under those ranges, and
+    the poisoned rows behind every output stay untouched."""
+    E = len(offsets) - 1
+    g = W.moe_gemm(31, tokens, 128, 128, E, exact=True)
+    eff = np.maximum.accumulate(np.clip(np.asarray(offsets, np.int64), 0, tokens))
+    covered = np.arange(eff[0], eff[-1])
+    x, w = dev_bf16(g.x), dev_bf16(g.w1)
+    off = dev(np.asarray(offsets, np.int32))
+    n, inter, guard = 256, 128, 64
+    out = torch.full((tokens + guard, n), -7.0, dtype=torch.bfloat16, device="cuda")
+    pk = torch.full((tokens + guard, inter // 2), 0x5A, dtype=torch.uint8, device="cuda")
+    sc = torch.full((tokens + guard, inter // 16), 0x5A, dtype=torch.uint8, device="cuda")
+    yv = torch.full((tokens + guard, inter), -7.0, dtype=torch.float32, device="cuda")
+    M.moe_l1_gemm_bf16(x, w, off, out=out[:tokens])
+    M.moe_l1_gemm_swiglu_nvfp4(x, w, off, None, packed=pk[:tokens], scales=sc[:tokens],
+                               swiglu_out=yv[:tokens])
+    res = {k: host(t) for k, t in dict(out=out.view(torch.int16), pk=pk, sc=sc, y=yv).items()}
+    say("gemm offsets out of rule", offsets, "-> ranges", eff.tolist())
+    assert (res["out"][tokens:] == np.int16(np.float32(-7.0).view(np.int32) >> 16)).all()
+    assert (res["pk"][tokens:] == 0x5A).all() and (res["sc"][tokens:] == 0x5A).all()
+    assert (res["y"][tokens:] == np.float32(-7.0)).all()
+    acc32 = oracle.moe_l1_gemm(g.x, g.w1, eff, rows=covered).astype(np.float32)
+    P.assert_bytes_equal("bf16 GEMM, covered rows", res["out"][covered].view(np.uint16),
+                         oracle.f32_to_bf16(acc32))
+    ry = oracle.swiglu_f32(acc32)
+    rp, rs, rbsf, rv = oracle.quantize_f32(ry, None, diag=True)
+    rep = P.fused_report(res["pk"][covered], res["sc"][covered], res["y"][covered], rp, rs, ry,
+                         rbsf, rv)
+    P.assert_fused_ok(rep, "fused GEMM, covered rows")
+
+
 def check_random(g, r, rows, gs=None):
     """Bound checks of a random-operand run on the given token rows."""
     acc = oracle.moe_l1_gemm(g.x, g.w1, g.offsets, rows=rows)
