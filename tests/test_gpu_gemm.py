@@ -117,6 +117,36 @@ def test_gemm_single_expert_no_offsets(M):
     P.assert_fused_ok(P.fused_report(r["p"], r["s"], r["y"], rp, rs, ry, rbsf, rv), "one expert")
 
 
+def test_gemm_pitched_operands(M):
+    """x, w1 and the BF16 output as views into wider buffers (ld_x, ld_w and
+    ld_out above the used columns). The padding of x and w1 holds BF16 NaN,
+    so a read past `hidden` would poison the accumulators; the output's
+    padding is poisoned and must stay untouched."""
+    tokens, hidden, inter, E = 700, 256, 128, 3
+    n = 2 * inter
+    g = W.moe_gemm(41, tokens, hidden, inter, E, exact=True)
+    nan = np.uint16(0x7FC0)
+    xb = np.full((tokens, hidden + 72), nan, np.uint16)
+    xb[:, :hidden] = g.x
+    wb = np.full((E, n, hidden + 136), nan, np.uint16)
+    wb[:, :, :hidden] = g.w1
+    x = dev_bf16(xb)[:, :hidden]
+    w = dev_bf16(wb)[:, :, :hidden]
+    off = dev(g.offsets)
+    out_big = torch.full((tokens, n + 40), -7.0, dtype=torch.bfloat16, device="cuda")
+    M.moe_l1_gemm_bf16(x, w, off, out=out_big[:, :n])
+    p, s, y = M.moe_l1_gemm_swiglu_nvfp4(x, w, off, None, swiglu_out=True)
+    ob = host(out_big.view(torch.int16)).view(np.uint16)
+    say("gemm pitched: ld_x %d ld_w %d ld_out %d" % (x.stride(0), w.stride(1), out_big.stride(0)))
+    assert (ob[:, n:] == np.uint16(0xC0E0)).all(), "output padding was written"
+    acc32 = oracle.moe_l1_gemm(g.x, g.w1, g.offsets).astype(np.float32)
+    P.assert_bytes_equal("bf16 GEMM, pitched", ob[:, :n], oracle.f32_to_bf16(acc32))
+    ry = oracle.swiglu_f32(acc32)
+    rp, rs, rbsf, rv = oracle.quantize_f32(ry, None, diag=True)
+    P.assert_fused_ok(P.fused_report(host(p), host(s), host(y), rp, rs, ry, rbsf, rv),
+                      "fused GEMM, pitched operands")
+
+
 @pytest.mark.parametrize("tokens,offsets", [
     (600, [0, 500, 100, 900, 300]),     # decreasing steps and an end past the rows
     (300, [0, 300, 0, 300, 0]),         # every other expert claims all rows again
