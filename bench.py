@@ -25,6 +25,9 @@ flow and hipBLASLt.
 
 Every timed region is preceded by --settle-ms of untimed back-to-back
 launches (the clocks need ~30 ms of load to settle) and the warmup steps.
+The last timed output of every workload but the GEMM is hashed and compared
+with the digest of the oracle's output for the same input
+(tests/golden/bench_output_sha256.json): `outputs_match_oracle`.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--settle-ms MS]
                   [--no-cpu-baseline] [--no-secondary] [--only ITEMS]
@@ -45,6 +48,9 @@ ROWS, INTER = 65536, 3072
 BYTES_PER_ELEM = 4.5625             # 4 B read (gate+up BF16) + 0.5 B codes + 1/16 B scale
 ALG_BYTES = int(ROWS * INTER * BYTES_PER_ELEM)      # 918,552,576
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "fused_quantize_kernel_prefill_pmc.json")
+# SHA-256 of the oracle's outputs for the timed workloads, written by
+# tests/golden/make_bench_hashes.py (which calls only oracle/)
+EXPECTED_HASHES = os.path.join(ROOT, "tests", "golden", "bench_output_sha256.json")
 # grid sizes (256-thread workgroups) tried for the calibration kernels; the
 # best of them is the ceiling (measured: the read kernel peaks with a
 # persistent grid of 6 workgroups per CU, the copy with one 4 KB tile per wave)
@@ -56,6 +62,46 @@ CALIB_MIX_LDS = (0, 40960, 53248)
 SECONDARY = ("nvfp4_quantize", "nvfp4_dequantize", "global_scale", "two_pass", "calib_read",
              "calib_copy", "calib_mix", "ragged", "decode", "small", "kv", "gemm")
 PEAK_BF16_TFLOPS = 2500.0           # MI355X dense BF16 matrix peak
+
+
+class OutputCheck:
+    """Compares the SHA-256 of each workload's timed output with the digest of
+    the oracle's output for the same input (stored in EXPECTED_HASHES). The
+    benchmark runs no oracle code outside its CPU-baseline leg, so the other
+    workloads are checked through these digests. A key without a stored digest
+    is reported as unchecked."""
+
+    def __init__(self):
+        try:
+            with open(EXPECTED_HASHES) as f:
+                self.want = json.load(f)
+        except (OSError, ValueError):
+            self.want = {}
+        self.results = {}
+
+    @staticmethod
+    def digest(t) -> str:
+        import torch
+        if t.dtype == torch.bfloat16:
+            t = t.view(torch.int16)
+        return hashlib.sha256(t.contiguous().cpu().numpy().tobytes()).hexdigest()
+
+    def check(self, key, *tensors):
+        """True when every tensor's bytes hash to the stored digest for key."""
+        want = self.want.get(key)
+        if want is None:
+            self.results[key] = None
+            return None
+        ok = all(self.digest(t) == want for t in tensors)
+        self.results[key] = ok
+        return ok
+
+    def report(self):
+        done = {k: v for k, v in self.results.items() if v is not None}
+        return {"checked": len(done), "matched": sum(1 for v in done.values() if v),
+                "mismatched": sorted(k for k, v in done.items() if not v),
+                "unchecked": sorted(k for k, v in self.results.items() if v is None),
+                "expected_from": os.path.relpath(EXPECTED_HASHES, ROOT)}
 
 
 def load_calib():
@@ -342,8 +388,9 @@ def cpu_baseline(x, gpu_packed=None, gpu_scales=None, gpu_value=None):
 kern_ms_headline = []
 
 
-def secondary_figures(M, W, x, packed, scales, args, dev):
-    """Other kernels and the other workload shapes (not the headline)."""
+def secondary_figures(M, W, x, packed, scales, args, dev, oc):
+    """Other kernels and the other workload shapes (not the headline). Each
+    workload's last timed output goes through oc (OutputCheck)."""
     import numpy as np
     import torch
     sec = {}
@@ -356,6 +403,8 @@ def secondary_figures(M, W, x, packed, scales, args, dev):
         sec["nvfp4_quantize"] = measure(
             "nvfp4_quantize prefill-shaped", lambda: M.nvfp4_quantize(xq, packed=pq, scales=sq),
             ROWS * INTER * 2.5625, ROWS * INTER, st, ms, {"shape": [ROWS, INTER]})
+        oc.check("nvfp4_quantize.packed", pq)
+        oc.check("nvfp4_quantize.scales", sq)
         del xq, pq, sq
     if "nvfp4_dequantize" in want:
         out = torch.empty((ROWS, INTER), dtype=torch.float32, device=dev)
@@ -363,6 +412,7 @@ def secondary_figures(M, W, x, packed, scales, args, dev):
             "nvfp4_dequantize prefill-shaped",
             lambda: M.nvfp4_dequantize(packed, scales, out=out),
             ROWS * INTER * 4.5625, ROWS * INTER, st, ms, {"shape": [ROWS, INTER]})
+        oc.check("nvfp4_dequantize.out", out)
         del out
     if "global_scale" in want:
         gsb = torch.empty(1, dtype=torch.float32, device=dev)
@@ -370,6 +420,7 @@ def secondary_figures(M, W, x, packed, scales, args, dev):
             "swiglu_nvfp4_global_scale prefill", lambda: M.swiglu_nvfp4_global_scale(x, gs=gsb),
             ROWS * INTER * 4.0, ROWS * INTER, st, ms,
             {"shape": [ROWS, 2 * INTER], "note": "per-tensor amax pre-pass; 3 launches"})
+        oc.check("global_scale.gs", gsb)
     if "two_pass" in want:
         # the ablation that prices the fusion: SwiGLU to compact BF16 (4 B read,
         # 2 B written per element), then the standalone quantize of it
@@ -379,6 +430,7 @@ def secondary_figures(M, W, x, packed, scales, args, dev):
         sec["swiglu_bf16"] = measure(
             "swiglu_bf16 prefill", lambda: M.swiglu_bf16(x, out=yb), ROWS * INTER * 6.0,
             ROWS * INTER, st, ms, {"shape": [ROWS, 2 * INTER]})
+        oc.check("swiglu_bf16.out", yb)
 
         def two_pass():
             M.swiglu_bf16(x, out=yb)
@@ -388,6 +440,8 @@ def secondary_figures(M, W, x, packed, scales, args, dev):
                      {"note": "GB_s over the two passes' own 8.5625 B per element"})
         tp["fused_speedup"] = round(tp["ms"] / kern_ms_headline[0], 3) if kern_ms_headline else None
         sec["two_pass"] = tp
+        oc.check("two_pass.packed", pq)
+        oc.check("two_pass.scales", sq)
         del yb, pq, sq
     # in-repo calibration kernels over the same 805 MB input: HBM ceilings
     nbytes = x.numel() * 2
@@ -445,15 +499,19 @@ def secondary_figures(M, W, x, packed, scales, args, dev):
         ragged["global_scale"] = measure(
             "ragged swiglu_nvfp4_global_scale",
             lambda: M.swiglu_nvfp4_global_scale(xr, offr, gs=gsr), rr * ri * 4.0, rr * ri, st, ms)
+        oc.check("ragged.gs", gsr)
         ragged["quantize"] = measure(
             "ragged swiglu_nvfp4_quantize",
             lambda: M.swiglu_nvfp4_quantize(xr, gsr, offr, packed=pr, scales=sr),
             rr * ri * BYTES_PER_ELEM, rr * ri, st, ms)
+        oc.check("ragged.packed", pr)
+        oc.check("ragged.scales", sr)
         del xr
         outr = torch.empty((rr, ri), dtype=torch.float32, device=dev)
         ragged["dequantize"] = measure(
             "ragged nvfp4_dequantize", lambda: M.nvfp4_dequantize(pr, sr, gsr, offr, out=outr),
             rr * ri * 4.5625, rr * ri, st, ms)
+        oc.check("ragged.dequantize", outr)
         sec["ragged_256_experts"] = ragged
         del outr, pr, sr, gsr, offr
 
@@ -480,6 +538,9 @@ def secondary_figures(M, W, x, packed, scales, args, dev):
             max(st, 80), ms, {"shape": [dr, 2 * di], "note": "8 rotating input/output sets",
                               "input_sha256": decode_sha})
         dec["graph_ms"] = round(graph_ms(rotating, launches=80, replays=10), 5)
+        # the 8 sets hold copies of one input, so every set's output must match
+        oc.check("decode.packed", *[o[1] for o in sets])
+        oc.check("decode.scales", *[o[2] for o in sets])
         # the HBM ceilings at this size, over the same 8 rotating inputs: the
         # read kernel and the traffic-mix kernel (the fused kernel's 4 KB read
         # and 576 B written per wave tile, without compute)
@@ -535,6 +596,8 @@ def secondary_figures(M, W, x, packed, scales, args, dev):
             "standalone 128x256 nvfp4_quantize", lambda: M.nvfp4_quantize(xs, packed=ps, scales=ss),
             w.rows * w.out_cols * 2.5625, w.rows * w.out_cols, [w.rows, w.out_cols],
             W.sha256(w.x))
+        oc.check("small_standalone.packed", ps)
+        oc.check("small_standalone.scales", ss)
         w = W.fused_small()
         xf = torch.from_numpy(w.x.view(np.int16)).to(dev).view(torch.bfloat16)
         pf = torch.empty((w.rows, w.out_cols // 2), dtype=torch.uint8, device=dev)
@@ -544,6 +607,8 @@ def secondary_figures(M, W, x, packed, scales, args, dev):
             lambda: M.swiglu_nvfp4_quantize(xf, packed=pf, scales=sf),
             w.rows * w.out_cols * BYTES_PER_ELEM, w.rows * w.out_cols, [w.rows, 2 * w.out_cols],
             W.sha256(w.x))
+        oc.check("small_fused.packed", pf)
+        oc.check("small_fused.scales", sf)
         del xs, ps, ss, xf, pf, sf
     if "kv" in want:
         # paged KV-cache write and read: 65536 tokens x 8 heads x 128 into a
@@ -564,10 +629,13 @@ def secondary_figures(M, W, x, packed, scales, args, dev):
         kv["write"] = measure("paged KV write nvfp4_quantize_paged",
                               lambda: M.nvfp4_quantize_paged(xk, sk, pk, sck),
                               n * cols * 2 + valid * cols * 0.5625, n * cols, st, ms)
+        oc.check("kv_write.packed_cache", pk)
+        oc.check("kv_write.scales_cache", sck)
         outk = torch.empty((n, cols), dtype=torch.float32, device=dev)
         kv["read"] = measure("paged KV read nvfp4_dequantize_paged",
                              lambda: M.nvfp4_dequantize_paged(pk, sck, sk, out=outk),
                              valid * cols * 0.5625 + n * cols * 4, n * cols, st, ms)
+        oc.check("kv_read.out", outk)
         sec["kv_cache_paged"] = kv
         del xk, sk, pk, sck, outk
     if "gemm" in want:
@@ -683,10 +751,13 @@ def main():
           % (ms_per_step, kern_ms, value), file=sys.stderr, flush=True)
     # the timed launches' output, before any other measurement reuses the buffers
     output_sha = {"packed": W.sha256(packed.cpu().numpy()), "scales": W.sha256(scales.cpu().numpy())}
+    oc = OutputCheck()
+    oc.check("prefill.packed", packed)
+    oc.check("prefill.scales", scales)
 
     secondary = None
     if not args.no_secondary:
-        secondary = secondary_figures(M, W, x, packed, scales, args, dev)
+        secondary = secondary_figures(M, W, x, packed, scales, args, dev, oc)
         if "calib_read_ceiling" in secondary:
             r = secondary["calib_read_ceiling"]["GB_s"]
             secondary["fused_frac_of_read_ceiling"] = round(achieved / r, 4)
@@ -729,6 +800,7 @@ def main():
                      "kernel_ms": round(kern_ms, 5),
                      "kernel_ms_p10_p50_p90": [round(pct(per, q), 5) for q in (0.1, 0.5, 0.9)]},
         "output_sha256": output_sha,
+        "outputs_match_oracle": oc.report(),
         "cpu_baseline": cpu,
         "gpu_state": gpu_state,
         "secondary": secondary,
